@@ -1,0 +1,284 @@
+"""Plain, slow CPU oracle for LeanK-style channel-pruned decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import or call this module.  The product
+(the HIP library and its Python binding) never does, and this module imports
+nothing from the product: the two share no code.
+
+Sources (cited by page title and section):
+
+* LeanK page -- "大型语言模型KV缓存优化与LeanK剪枝技术解析" (framerc.cn):
+  - section 1: KV-cache size is 2 x L x h x d x N elements;
+  - section 2.2, stage 1: the learned scale alpha has shape L x h x d and is
+    applied only to the middle of the context (not the sink tokens, not the
+    sliding local window);
+  - section 2.2, stage 2: the hardware-friendly mask -- one global
+    percentile threshold over all of alpha, then per head the kept count is
+    floored to the alignment and the top-k channels of that head are kept;
+  - section 3.1, item 2: sink + local-window keys are stored full width,
+    the middle of the context is stored channel-pruned;
+  - section 3.1 (kernel sketch): only the kept channels are loaded;
+  - section 3.2: a head whose channels are all pruned can drop its V cache.
+* KV-pruning white paper -- "智能剪枝深度解析：大型语言模型KV缓存优化技术白皮书"
+  (blog.yyx235.top): section 3.3.1 (attention sinks + sliding window),
+  section 5.2.3 (grouped-query attention: a group of query heads shares one
+  K/V head).
+* FastGen page (mhpn.cn, FastGen / ICLR 2024): section 2.2 (worked KV-cache
+  size example), section 5.3 (attention weights are Softmax(QK^T / sqrt(d))).
+
+Readings taken where the pages are silent or garbled (each one is listed in
+the design notes of the repository):
+
+* prune_pct is the prune ratio of the prose; the threshold is the
+  prune_pct-th percentile of alpha and channels with alpha >= threshold
+  survive the global step.  The linear-interpolation percentile is replaced
+  by the exact order statistic at rank ceil((N-1)*p/100), which selects the
+  same channels (the interpolated value always lies strictly above the
+  lower neighbour unless the two neighbours are equal);
+* top-k ties are broken towards the lower channel index; kept channel ids
+  are reported in ascending order;
+* a query head j reads KV head j // G (contiguous GQA groups);
+* a fully-pruned head excludes its middle tokens from the softmax (no
+  weight, no V), it does not score them as zero;
+* the softmax scale is 1/sqrt(head_dim) with the full head_dim;
+* regions for a context of T tokens: sink [0, min(S, T)), local window
+  [max(S, T - W), T), middle [S, T - W) (empty when T <= S + W);
+* cache layout of the full-width region: sink token p < S in slot p, a
+  window token p >= S in ring slot S + (p - S) mod W.
+
+Every floating-point step runs in float64 on bf16 inputs widened exactly.
+"""
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "prune_rank",
+    "build_mask",
+    "regions",
+    "ring_slot",
+    "pack_reference",
+    "decode",
+    "kv_cache_bytes",
+    "decode_traffic_bytes",
+]
+
+
+def bf16_bits_to_f64(bits):
+    """Widen bf16 bit patterns (uint16) to float64 exactly.
+
+    A bf16 value is the upper half of an IEEE float32; widening to float32
+    and then float64 is exact.
+    """
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def prune_rank(n, prune_pct):
+    """Rank (0-based, ascending) of the global threshold among n values.
+
+    LeanK page, section 2.2 stage 2: the threshold is a percentile of the
+    flattened alpha.  With linear interpolation at position (n-1)*p/100, the
+    set {alpha >= value} equals {alpha >= x[ceil((n-1)*p/100)]} for the
+    ascending order statistics x, so the rank is that ceiling, taken in
+    integer arithmetic.
+    """
+    return -((-(n - 1) * prune_pct) // 100)
+
+
+def build_mask(alpha, prune_pct, align):
+    """Stage-2 mask of the LeanK page, section 2.2.
+
+    alpha: float32 array [L, H, d] (H = KV heads).
+    Returns (mask uint8 [L, H, d], kept_count int32 [L, H],
+             kept_idx int16 [L, H, d] -- ascending kept channels, -1 padded).
+
+    Steps, in the page's order:
+    1. one threshold over all of alpha: the prune_pct-th percentile;
+    2. per (layer, head): count the channels with alpha >= threshold;
+    3. floor that count to a multiple of `align`;
+    4. keep that many channels with the largest alpha of the head
+       (ties towards the lower channel index).
+    """
+    alpha = np.asarray(alpha)
+    if alpha.dtype != np.float32 or alpha.ndim != 3:
+        raise ValueError("alpha must be a float32 array [L, H, d]")
+    if np.any(np.isnan(alpha)):
+        raise ValueError("alpha holds NaN")
+    n_layers, n_heads, d = alpha.shape
+    if not 0 <= prune_pct <= 100:
+        raise ValueError("prune_pct must lie in [0, 100]")
+    if align < 1 or d % align != 0:
+        raise ValueError("align must be >= 1 and divide head_dim")
+    n = alpha.size
+    if n == 0:
+        raise ValueError("alpha is empty")
+
+    values = alpha.astype(np.float64)
+    ordered = np.sort(values.ravel())
+    threshold = ordered[prune_rank(n, prune_pct)]
+
+    mask = np.zeros((n_layers, n_heads, d), dtype=np.uint8)
+    kept_count = np.zeros((n_layers, n_heads), dtype=np.int32)
+    kept_idx = np.full((n_layers, n_heads, d), -1, dtype=np.int16)
+    for layer in range(n_layers):
+        for head in range(n_heads):
+            a = values[layer, head]
+            n_keep = int(np.count_nonzero(a >= threshold))
+            n_keep = (n_keep // align) * align
+            by_importance = sorted(range(d), key=lambda c: (-a[c], c))
+            kept = sorted(by_importance[:n_keep])
+            mask[layer, head, kept] = 1
+            kept_count[layer, head] = n_keep
+            kept_idx[layer, head, :n_keep] = kept
+    return mask, kept_count, kept_idx
+
+
+def regions(ctx_len, n_sink, window):
+    """Split positions [0, ctx_len) into (sink, middle, local) ranges.
+
+    LeanK page, section 2.2 stage 1 and section 3.1 item 2; white paper
+    section 3.3.1.  Returns three Python ranges.
+    """
+    sink = range(0, min(n_sink, ctx_len))
+    local_begin = max(n_sink, ctx_len - window)
+    middle = range(n_sink, local_begin)
+    local = range(local_begin, ctx_len)
+    return sink, middle, local
+
+
+def ring_slot(pos, n_sink, window):
+    """Slot of a full-width token: sink tokens in place, window tokens in a ring."""
+    if pos < n_sink:
+        return pos
+    return n_sink + (pos - n_sink) % window
+
+
+def pack_reference(k_bits, v_bits, kept_count, kept_idx, n_sink, window):
+    """Expected cache contents after packing a whole context (one layer).
+
+    LeanK page, section 3.1 item 2 (K_cache for sink + local window, K_prun
+    for the middle) and section 3.2 (no middle V for fully-pruned heads).
+
+    k_bits, v_bits: uint16 [B, H, T, d] bf16 bit patterns of the context.
+    kept_count: int [H]; kept_idx: int [H, d] (ascending, -1 padded).
+    Returns a dict:
+      ring_k, ring_v: uint16 [B, H, S + W, d] (unfilled slots are zero),
+      slot_pos: int64 [S + W] position held by each slot (-1 = empty),
+      k_prun: list over heads of uint16 [B, T_mid, c_h],
+      v_mid: list over heads of uint16 [B, T_mid, d] or None (dead head).
+    """
+    k_bits = np.asarray(k_bits, dtype=np.uint16)
+    v_bits = np.asarray(v_bits, dtype=np.uint16)
+    batch, n_heads, ctx_len, d = k_bits.shape
+    sink, middle, local = regions(ctx_len, n_sink, window)
+    n_slots = n_sink + window
+    ring_k = np.zeros((batch, n_heads, n_slots, d), dtype=np.uint16)
+    ring_v = np.zeros_like(ring_k)
+    slot_pos = np.full(n_slots, -1, dtype=np.int64)
+    for pos in list(sink) + list(local):
+        slot = ring_slot(pos, n_sink, window)
+        ring_k[:, :, slot, :] = k_bits[:, :, pos, :]
+        ring_v[:, :, slot, :] = v_bits[:, :, pos, :]
+        slot_pos[slot] = pos
+    mid = np.asarray(list(middle), dtype=np.int64)
+    k_prun, v_mid = [], []
+    for head in range(n_heads):
+        c = int(kept_count[head])
+        chans = np.asarray(kept_idx[head][:c], dtype=np.int64)
+        rows = k_bits[:, head][:, mid]  # [B, T_mid, d]
+        k_prun.append(rows[:, :, chans].copy())
+        v_mid.append(v_bits[:, head][:, mid].copy() if c > 0 else None)
+    return {"ring_k": ring_k, "ring_v": ring_v, "slot_pos": slot_pos,
+            "k_prun": k_prun, "v_mid": v_mid}
+
+
+def decode(q_bits, k_bits, v_bits, mask, n_sink, window, scale=None, pairs=None):
+    """Single-token decode attention over a channel-pruned cache (one layer).
+
+    q_bits: uint16 [B, Hq, d]; k_bits, v_bits: uint16 [B, H, T, d] -- the
+    full, unpruned context of T tokens; mask: uint8 [H, d] (beta of the
+    LeanK page, section 2.2 stage 2).  Query head j reads KV head j // G.
+
+    For query head j with KV head h (definition, float64):
+      * sink and local-window tokens score q . k over all channels;
+      * middle tokens of a head with kept channels score q . (beta_h * k);
+      * middle tokens of a fully-pruned head are left out entirely;
+      * out = sum_t softmax(scale * s)_t v_t over the included tokens,
+        scale = 1/sqrt(d) by default (FastGen page, section 5.3).
+
+    Returns float64 [B, Hq, d], or [len(pairs), d] for a list of (b, j).
+    """
+    q_bits = np.asarray(q_bits, dtype=np.uint16)
+    k_bits = np.asarray(k_bits, dtype=np.uint16)
+    v_bits = np.asarray(v_bits, dtype=np.uint16)
+    batch, n_q_heads, d = q_bits.shape
+    _, n_heads, ctx_len, _ = k_bits.shape
+    if ctx_len < 1:
+        raise ValueError("empty context")
+    group = n_q_heads // n_heads
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    sink, middle, local = regions(ctx_len, n_sink, window)
+    full_rows = np.asarray(list(sink) + list(local), dtype=np.int64)
+    mid_rows = np.asarray(list(middle), dtype=np.int64)
+
+    if pairs is None:
+        pairs = [(b, j) for b in range(batch) for j in range(n_q_heads)]
+        out = np.zeros((batch, n_q_heads, d), dtype=np.float64)
+        put = lambda b, j, val: out.__setitem__((b, j), val)
+    else:
+        out = np.zeros((len(pairs), d), dtype=np.float64)
+        index = {pair: n for n, pair in enumerate(pairs)}
+        put = lambda b, j, val: out.__setitem__(index[(b, j)], val)
+
+    by_kv = {}
+    for b, j in pairs:
+        by_kv.setdefault((b, j // group), []).append(j)
+    for (b, h), heads in sorted(by_kv.items()):
+        beta = np.asarray(mask[h], dtype=np.float64)
+        live = bool(np.any(beta != 0))
+        keys_full = bf16_bits_to_f64(k_bits[b, h, full_rows])
+        vals_full = bf16_bits_to_f64(v_bits[b, h, full_rows])
+        if live and mid_rows.size:
+            keys_mid = bf16_bits_to_f64(k_bits[b, h, mid_rows]) * beta
+            vals_mid = bf16_bits_to_f64(v_bits[b, h, mid_rows])
+            keys = np.concatenate([keys_full, keys_mid])
+            vals = np.concatenate([vals_full, vals_mid])
+        else:
+            keys, vals = keys_full, vals_full
+        for j in heads:
+            qv = bf16_bits_to_f64(q_bits[b, j])
+            s = (keys @ qv) * scale
+            w = np.exp(s - s.max())
+            put(b, j, (w @ vals) / w.sum())
+    return out
+
+
+def kv_cache_bytes(n_layers, n_heads, head_dim, n_tokens, batch=1, bytes_per_elem=2):
+    """Dense KV-cache size: 2 (K and V) x L x h x d x N per sequence.
+
+    LeanK page, section 1.
+    """
+    return 2 * n_layers * n_heads * head_dim * n_tokens * batch * bytes_per_elem
+
+
+def decode_traffic_bytes(batch, n_q_heads, n_kv_heads, head_dim, ctx_len,
+                         n_sink, window, kept_count):
+    """Bytes one pruned decode step must move for one layer.
+
+    Reads q (bf16), the full-width sink+window keys and values of every head,
+    the kept middle channels of K and the middle V of live heads (bf16), and
+    writes the fp32 output.  Nothing else is counted.
+    """
+    sink, middle, local = regions(ctx_len, n_sink, window)
+    n_full = len(sink) + len(local)
+    n_mid = len(middle)
+    kept = [int(c) for c in kept_count]
+    live = sum(1 for c in kept if c > 0)
+    total = batch * n_q_heads * head_dim * 2                      # q
+    total += 2 * batch * n_kv_heads * n_full * head_dim * 2        # K, V full width
+    total += batch * n_mid * sum(kept) * 2                         # kept K channels
+    total += batch * live * n_mid * head_dim * 2                   # middle V, live heads
+    total += batch * n_q_heads * head_dim * 4                      # out
+    return total
