@@ -1,0 +1,320 @@
+"""Benchmark: one decode step of channel-pruned attention on one MI355X.
+
+Workload (Llama-3.1-8B attention shape, one layer): 32 query / 8 KV heads,
+head_dim 128, batch 64, context 4096 (64 sink tokens, 512-token window),
+70% prune with align 32 on a seeded synthetic alpha, bf16 N(0,1) q/K/V with
+LogNormal(0, 0.5) K channel scales.
+
+A step is what a generation loop does per layer: append the new token's K/V
+(leank_pack_k, which also moves the token leaving the window into the
+pruned middle) and run decode attention over the whole cache
+(leank_decode_attn).  Each step appends one token, so the context grows by
+one per step on each cache copy; copies rotate so that consecutive steps
+read different HBM data (the copies together exceed the 256 MB Infinity
+Cache many times over).
+
+Reported on one JSON line: microseconds per step (value), the decode
+kernel's roofline figures from HIP events on the launch stream, the same
+kernel at 0% pruning, the Qwen2.5-7B-shaped cache, and the CPU oracle's time
+for the same step (a baseline, not a target).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = ("pruned decode-attn µs/step & achieved HBM GB/s (% of 8 TB/s), "
+          "Llama-3.1-8B shape")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=6, help="rotating cache copies")
+    ap.add_argument("--skip-extras", action="store_true",
+                    help="only the main workload (no 0%% pruning, Qwen or CPU baseline)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def setup_caches(cfg, mask_counts, kept_idx_dev, k, v, copies, max_ctx):
+    """`copies` caches holding the first ctx-1 tokens of k, v."""
+    import decode_attention_channel_amd as dac
+
+    caches = []
+    for _ in range(copies):
+        cache = dac.LayerCache(mask_counts, kept_idx_dev, cfg.batch, cfg.n_q_heads,
+                               cfg.n_kv_heads, cfg.n_sink, cfg.window, max_ctx)
+        dac.leank_pack_k(cache, k[:, :, : cfg.ctx - 1].contiguous(),
+                         v[:, :, : cfg.ctx - 1].contiguous())
+        cache.workspace()
+        caches.append(cache)
+    return caches
+
+
+def run_steps(cfg, caches, q, new_k, new_v, steps, warmup):
+    """Warm-up, then `steps` timed (append + decode) steps.  Returns timings."""
+    import torch
+
+    import decode_attention_channel_amd as dac
+
+    stream = torch.cuda.current_stream()
+    n = len(caches)
+    outs = [torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device) for _ in range(n)]
+
+    def step(idx, events=None):
+        cache = caches[idx % n]
+        kk = new_k[idx % new_k.shape[0]]
+        vv = new_v[idx % new_v.shape[0]]
+        if events is not None:
+            events[0].record(stream)
+        dac.leank_pack_k(cache, kk, vv)
+        if events is not None:
+            events[1].record(stream)
+        dac.leank_decode_attn(cache, q, out=outs[idx % n])
+        if events is not None:
+            events[2].record(stream)
+        return cache.length
+
+    for idx in range(warmup):
+        step(idx)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ctxs = []
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for s in range(steps):
+        ctxs.append(step(warmup + s, ev[s]))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_begin.elapsed_time(t_end)
+    append_us = [ev[s][0].elapsed_time(ev[s][1]) * 1e3 for s in range(steps)]
+    decode_us = [ev[s][1].elapsed_time(ev[s][2]) * 1e3 for s in range(steps)]
+    bytes_per = [dac.leank_decode_bytes(caches[(warmup + s) % n], ctxs[s]) for s in range(steps)]
+    return {
+        "total_ms": total_ms,
+        "wall_s": wall,
+        "append_us": append_us,
+        "decode_us": decode_us,
+        "ctx": ctxs,
+        "decode_bytes": bytes_per,
+    }
+
+
+def summarize(t):
+    import numpy as np
+
+    d = np.asarray(t["decode_us"])
+    byt = float(np.mean(t["decode_bytes"]))
+    dec_mean = float(d.mean())
+    gbps = byt / (dec_mean * 1e-6) / 1e9
+    return {
+        "us_per_step": t["total_ms"] * 1e3 / len(d),
+        "decode_us_mean": dec_mean,
+        "decode_us_p10": float(np.percentile(d, 10)),
+        "decode_us_p50": float(np.percentile(d, 50)),
+        "decode_us_p90": float(np.percentile(d, 90)),
+        "append_us_mean": float(np.mean(t["append_us"])),
+        "decode_bytes_mean": byt,
+        "achieved_GBps": gbps,
+        "frac_of_peak": gbps / HBM_PEAK_GBPS,
+        "ctx_min": int(min(t["ctx"])),
+        "ctx_max": int(max(t["ctx"])),
+    }
+
+
+def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20):
+    """Prepare one workload and time it.  prune_override=0 keeps every channel."""
+    import numpy as np
+    import torch
+
+    import decode_attention_channel_amd as dac
+    from synthetic import alpha_for, make_kv, make_q, make_step_kv
+
+    dev = torch.device("cuda:0")
+    alpha = torch.from_numpy(alpha_for(cfg)).to(dev)
+    prune = cfg.prune_pct if prune_override is None else prune_override
+    mask, kept_count, kept_idx = dac.leank_build_mask(alpha, prune, cfg.align)
+    counts = kept_count[0].cpu().tolist()
+    k, v = make_kv(cfg, 0, device=dev)
+    q = make_q(cfg, 0, device=dev)
+    n_new = 8
+    new = [make_step_kv(cfg, 0, s, device=dev) for s in range(n_new)]
+    new_k = torch.stack([a for a, _ in new])
+    new_v = torch.stack([b for _, b in new])
+    max_ctx = cfg.ctx + (steps + warmup) // copies + 2
+    caches = setup_caches(cfg, counts, kept_idx[0].contiguous(), k, v, copies, max_ctx)
+    torch.cuda.synchronize()
+    timings = run_steps(cfg, caches, q, new_k, new_v, steps, warmup)
+    res = summarize(timings)
+    res["kept_count"] = counts
+    res["dead_heads"] = int(sum(1 for c in counts if c == 0))
+    res["realized_prune_pct"] = 100.0 * (1 - sum(counts) / (len(counts) * cfg.head_dim))
+    res["cache_bytes_per_copy"] = int(caches[0].nbytes())
+    del caches, k, v
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, target_seconds):
+    """The CPU oracle on the same workload's full decode step, on host cores."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from synthetic import alpha_for, bf16_bits, make_kv, make_q
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    dev = torch.device("cuda:0")
+    alpha = alpha_for(cfg)
+    om, _, _ = oracle.build_mask(alpha, cfg.prune_pct, cfg.align)
+    k, v = make_kv(cfg, 0, device=dev)
+    q = make_q(cfg, 0, device=dev)
+    kh, vh, qh = bf16_bits(k), bf16_bits(v), bf16_bits(q)
+    del k, v
+    # sample: whole batch rows (all 32 query heads each) until the time target
+    per_row = []
+    t_all = time.perf_counter()
+    b = 0
+    while time.perf_counter() - t_all < target_seconds and b < cfg.batch:
+        t0 = time.perf_counter()
+        oracle.decode(qh[b:b + 1], kh[b:b + 1], vh[b:b + 1], om[0], cfg.n_sink, cfg.window)
+        per_row.append(time.perf_counter() - t0)
+        b += 1
+    us_per_step = float(np.mean(per_row)) * cfg.batch * 1e6
+    return {
+        "value": us_per_step,
+        "unit": "us/step",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(per_row)} of {cfg.batch} batch rows of the {cfg.name} step "
+                   f"(all {cfg.n_q_heads} query heads, ctx {cfg.ctx}), float64 numpy, "
+                   f"scaled to the full batch; {sum(per_row):.1f} s of CPU time"),
+    }
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling memory counters."""
+    import torch
+
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read": n, "bytes_written": n, "launches": 5}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; every figure is one GPU's.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from synthetic import get_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import decode_attention_channel_amd as dac
+
+    dac.lib()  # fail loudly if the HIP library is missing
+    cfg = get_config("llama_b64_4k")
+    torch.cuda.synchronize()
+    main_res = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup)
+    extras = {}
+    if not args.skip_extras:
+        dense = workload(cfg, prune_override=0, copies=args.copies, steps=args.steps,
+                         warmup=args.warmup)
+        qwen_cfg = get_config("qwen_b16_32k")
+        qwen = workload(qwen_cfg, copies=args.copies, steps=args.steps, warmup=args.warmup)
+        qwen_dense = workload(qwen_cfg, prune_override=0, copies=max(2, args.copies // 2),
+                              steps=args.steps, warmup=args.warmup)
+        extras = {
+            "dense_0pct": dense,
+            "speedup_vs_0pct_decode": dense["decode_us_mean"] / main_res["decode_us_mean"],
+            "speedup_vs_0pct_step": dense["us_per_step"] / main_res["us_per_step"],
+            "qwen_b16_32k": qwen,
+            "qwen_b16_32k_dense_0pct": qwen_dense,
+            "qwen_speedup_vs_0pct_decode": qwen_dense["decode_us_mean"] / qwen["decode_us_mean"],
+        }
+    if args.copy_calibration:
+        extras["copy_calibration"] = copy_calibration()
+    cpu = None
+    if not args.skip_extras:
+        cpu = cpu_baseline(cfg, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": main_res["us_per_step"],
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["us_per_step"] / 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "shape": "Llama-3.1-8B attention, one layer",
+            "batch": cfg.batch,
+            "n_q_heads": cfg.n_q_heads,
+            "n_kv_heads": cfg.n_kv_heads,
+            "head_dim": cfg.head_dim,
+            "ctx": cfg.ctx,
+            "ctx_range_timed": [main_res["ctx_min"], main_res["ctx_max"]],
+            "n_sink": cfg.n_sink,
+            "window": cfg.window,
+            "prune_pct": cfg.prune_pct,
+            "align": cfg.align,
+            "step": "leank_pack_k (1 token) + leank_decode_attn",
+            "cache_copies": args.copies,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel<4>",
+            "achieved": main_res["achieved_GBps"],
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": main_res["frac_of_peak"],
+            "traffic": None,
+            "bytes_per_launch": main_res["decode_bytes_mean"],
+            "launch_us": main_res["decode_us_mean"],
+        },
+        "cpu_baseline": cpu,
+        "pruned": main_res,
+    }
+    line.update(extras)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,226 @@
+"""Channel-pruned (LeanK-style) single-token decode attention for MI355X (gfx950).
+
+Thin Python layer over the C ABI of ``include/leank.h`` (libleank.so): the
+functions carry the C names, take torch tensors on the GPU and pass their
+pointers plus the current HIP stream.  torch provides device memory and
+streams only; every step runs in the library's HIP kernels.
+
+    mask, kept_count, kept_idx = leank_build_mask(alpha, prune_pct, align)
+    cache = LayerCache(kept_count[layer].cpu(), kept_idx[layer], batch,
+                       n_q_heads, n_kv_heads, n_sink, window, max_ctx)
+    leank_pack_k(cache, k_prefill, v_prefill)        # appends, tracks length
+    leank_pack_k(cache, k_step, v_step)              # one decode step's token
+    out = leank_decode_attn(cache, q)                # float32 [B, Hq, 128]
+"""
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import (  # noqa: F401
+    CHANNEL_QUANTUM,
+    HEAD_DIM,
+    MAX_GROUP,
+    MAX_KV_HEADS,
+    LayerCacheDesc,
+    LeankError,
+    check,
+    lib,
+    ptr,
+    status_string,
+    stream_handle,
+)
+
+__all__ = [
+    "LayerCache",
+    "LayerCacheDesc",
+    "LeankError",
+    "leank_build_mask",
+    "leank_plan_layer",
+    "leank_pack_k",
+    "leank_workspace_bytes",
+    "leank_workspace_init",
+    "leank_decode_attn",
+    "leank_decode_bytes",
+    "status_string",
+]
+
+
+def _normalize_device(device):
+    device = torch.device(device)
+    if device.type == "cuda" and device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    return device
+
+
+def _require(t, dtype, name, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype} tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def leank_build_mask(alpha, prune_pct, align, stream=None):
+    """Channel mask from alpha float32 [L, H_kv, d] on the GPU (synchronous).
+
+    Returns (mask uint8 [L,H,d], kept_count int32 [L,H], kept_idx int16 [L,H,d]),
+    all on alpha's device.
+    """
+    _require(alpha, torch.float32, "alpha", ndim=3)
+    n_layers, n_heads, d = alpha.shape
+    mask = torch.empty((n_layers, n_heads, d), dtype=torch.uint8, device=alpha.device)
+    kept_count = torch.empty((n_layers, n_heads), dtype=torch.int32, device=alpha.device)
+    kept_idx = torch.empty((n_layers, n_heads, d), dtype=torch.int16, device=alpha.device)
+    status = lib().leank_build_mask(ptr(alpha), n_layers, n_heads, d, int(prune_pct), int(align),
+                                    ptr(mask), ptr(kept_count), ptr(kept_idx),
+                                    stream_handle(stream))
+    check(status, "leank_build_mask")
+    return mask, kept_count, kept_idx
+
+
+def leank_plan_layer(kept_count, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window, max_ctx):
+    """Host plan of one layer's cache (head grouping, offsets, byte sizes)."""
+    counts = [int(c) for c in kept_count]
+    if len(counts) != n_kv_heads:
+        raise ValueError("kept_count must hold one count per KV head")
+    arr = (ctypes.c_int32 * max(1, len(counts)))(*counts)
+    desc = LayerCacheDesc()
+    status = lib().leank_plan_layer(arr, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window,
+                                    int(max_ctx), ctypes.byref(desc))
+    check(status, "leank_plan_layer")
+    return desc
+
+
+class LayerCache:
+    """One layer's channel-pruned KV cache, with buffers allocated by torch.
+
+    ``length`` is the number of tokens appended so far (the library itself
+    keeps no state).
+    """
+
+    def __init__(self, kept_count, kept_idx, batch, n_q_heads, n_kv_heads, n_sink, window,
+                 max_ctx, head_dim=HEAD_DIM, device=None):
+        device = _normalize_device(device if device is not None else kept_idx.device)
+        self.desc = leank_plan_layer(kept_count, batch, n_q_heads, n_kv_heads, head_dim,
+                                     n_sink, window, max_ctx)
+        _require(kept_idx, torch.int16, "kept_idx", ndim=2, device=device)
+        if tuple(kept_idx.shape) != (n_kv_heads, head_dim):
+            raise ValueError("kept_idx must be [n_kv_heads, head_dim]")
+        self.kept_idx = kept_idx
+        self.device = device
+
+        def buf(nbytes):
+            return torch.empty(max(1, nbytes // 2), dtype=torch.bfloat16, device=device)
+
+        self.k_sl = buf(self.desc.k_sl_bytes)
+        self.v_sl = buf(self.desc.v_sl_bytes)
+        self.k_prun = buf(self.desc.k_prun_bytes)
+        self.v_mid = buf(self.desc.v_mid_bytes)
+        self.desc.kept_idx = kept_idx.data_ptr()
+        self.desc.k_sl = self.k_sl.data_ptr()
+        self.desc.v_sl = self.v_sl.data_ptr()
+        self.desc.k_prun = self.k_prun.data_ptr()
+        self.desc.v_mid = self.v_mid.data_ptr()
+        self.length = 0
+        self._workspace = None
+
+    # shape shortcuts
+    @property
+    def batch(self):
+        return self.desc.batch
+
+    @property
+    def n_q_heads(self):
+        return self.desc.n_q_heads
+
+    @property
+    def n_kv_heads(self):
+        return self.desc.n_kv_heads
+
+    @property
+    def max_ctx(self):
+        return self.desc.max_ctx
+
+    @property
+    def kept_count(self):
+        return [self.desc.kept_count[h] for h in range(self.desc.n_kv_heads)]
+
+    def workspace(self):
+        """A zero-filled workspace sized for max_ctx (allocated once)."""
+        if self._workspace is None:
+            nbytes = leank_workspace_bytes(self, self.max_ctx)
+            self._workspace = torch.zeros(max(16, nbytes), dtype=torch.uint8, device=self.device)
+        return self._workspace
+
+    def nbytes(self):
+        d = self.desc
+        return d.k_sl_bytes + d.v_sl_bytes + d.k_prun_bytes + d.v_mid_bytes
+
+
+def _desc(cache):
+    return ctypes.byref(cache.desc if isinstance(cache, LayerCache) else cache)
+
+
+def leank_pack_k(cache, k_new, v_new, pos0=None, stream=None):
+    """Append K, V bf16 [B, H_kv, n, 128] at position pos0 (default: cache.length)."""
+    if pos0 is None:
+        pos0 = cache.length
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _require(t, torch.bfloat16, name, ndim=4, device=cache.device)
+        if tuple(t.shape[:2]) != (cache.batch, cache.n_kv_heads) or t.shape[3] != HEAD_DIM:
+            raise ValueError(f"{name} must be [batch, n_kv_heads, n, {HEAD_DIM}]")
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new differ in shape")
+    n_new = k_new.shape[2]
+    status = lib().leank_pack_k(_desc(cache), ptr(k_new), ptr(v_new), int(pos0), int(n_new),
+                                stream_handle(stream))
+    check(status, "leank_pack_k")
+    cache.length = int(pos0) + int(n_new)
+
+
+def leank_workspace_bytes(cache, ctx_len):
+    out = ctypes.c_size_t(0)
+    check(lib().leank_workspace_bytes(_desc(cache), int(ctx_len), ctypes.byref(out)),
+          "leank_workspace_bytes")
+    return int(out.value)
+
+
+def leank_workspace_init(workspace, stream=None):
+    check(lib().leank_workspace_init(ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     stream_handle(stream)), "leank_workspace_init")
+
+
+def leank_decode_bytes(cache, ctx_len):
+    out = ctypes.c_int64(0)
+    check(lib().leank_decode_bytes(_desc(cache), int(ctx_len), ctypes.byref(out)),
+          "leank_decode_bytes")
+    return int(out.value)
+
+
+def leank_decode_attn(cache, q, ctx_len=None, scale=None, out=None, workspace=None, stream=None):
+    """Decode attention for q bf16 [B, Hq, 128]; returns float32 [B, Hq, 128]."""
+    if ctx_len is None:
+        ctx_len = cache.length
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    _require(q, torch.bfloat16, "q", ndim=3, device=cache.device)
+    if tuple(q.shape) != (cache.batch, cache.n_q_heads, HEAD_DIM):
+        raise ValueError("q must be [batch, n_q_heads, 128]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    else:
+        _require(out, torch.float32, "out", ndim=3, device=cache.device)
+        if out.shape != q.shape:
+            raise ValueError("out must match q's shape")
+    if workspace is None:
+        workspace = cache.workspace()
+    status = lib().leank_decode_attn(_desc(cache), ptr(q), int(ctx_len), float(scale), ptr(out),
+                                     ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     stream_handle(stream))
+    check(status, "leank_decode_attn")
+    return out

@@ -1,0 +1,87 @@
+// Internal helpers shared by the library's translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
+#include "leank.h"
+
+namespace leank {
+
+// ---------------------------------------------------------------- host side
+
+#define LEANK_HIP_TRY(expr)                          \
+  do {                                               \
+    if ((expr) != hipSuccess) return LEANK_EHIP;     \
+  } while (0)
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Decomposition of one decode call into work items.  Every (batch row,
+// KV head) pair owns n_sl_items items over its full-width rows followed by
+// n_mid[h] items over its middle rows; the pairs of one batch row are laid
+// out head by head, and batch rows follow each other.
+struct WorkPlan {
+  int32_t group;          // query heads per KV head
+  int32_t t_sl;           // valid full-width rows: min(ctx, n_sink + window)
+  int32_t t_mid;          // middle rows: max(0, ctx - n_sink - window)
+  int32_t n_sl_items;
+  int32_t sl_rows;        // rows per full-width item
+  int32_t n_mid[LEANK_MAX_KV_HEADS];
+  int32_t mid_rows[LEANK_MAX_KV_HEADS];
+  int32_t head_base[LEANK_MAX_KV_HEADS + 1];  // first item of head h within a batch row
+  int32_t items_per_b;
+  int64_t n_items;
+  int32_t partial_stride;  // floats per item record
+  size_t partial_bytes;
+  size_t counter_offset;   // bytes
+  size_t workspace_bytes;
+};
+
+int validate_cache(const leank_layer_cache* c, bool need_buffers);
+int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, WorkPlan* plan);
+
+// ---------------------------------------------------------------- device side
+
+template <int... Is, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, fully unrolled,
+// so that i can feed builtins that need an immediate operand.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, static_cast<F&&>(f));
+}
+
+// DPP controls of the GCN/CDNA encoding (all act inside a 16-lane row).
+enum : int {
+  kDppQuadXor1 = 0xB1,      // quad_perm [1,0,3,2]: lane ^ 1
+  kDppQuadXor2 = 0x4E,      // quad_perm [2,3,0,1]: lane ^ 2
+  kDppRowMirror = 0x140,    // lane i <- lane 15 - i
+  kDppHalfMirror = 0x141,   // lane i <- lane 7 - i within each half row
+  kDppRowNewBcast = 0x150,  // + n: every lane <- lane n of its row
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.x*b.x + a.y*b.y + c for two packed bf16 pairs, float32 accumulation.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+}  // namespace leank

@@ -1,0 +1,186 @@
+// leank_pack_k: route appended tokens into the channel-pruned cache
+// (LeanK page, section 3.1 item 2; section 3.2 for heads without middle V).
+//
+// One wavefront handles one (batch row, KV head, token) unit and moves one
+// 256-byte K row and one V row: lane l carries 32-bit word l (channels 2l,
+// 2l+1).  The kept-channel gather into K_prun reads the source word of each
+// kept channel from the lane that holds it (ds_bpermute).
+
+#include "common.h"
+
+namespace leank {
+namespace {
+
+enum PackMode : int32_t {
+  kFused = 0,    // n_new <= window: each unit migrates the token its ring row holds, then writes
+  kMigrate = 1,  // move window tokens that leave the window to the middle
+  kPlace = 2,    // route new tokens to sink rows, the middle or ring rows
+};
+
+struct PackHead {
+  int64_t k_off;  // elements
+  int64_t v_off;  // elements
+  int32_t kept;
+  int32_t pad;
+};
+
+struct PackParams {
+  const uint32_t* k_new;
+  const uint32_t* v_new;
+  uint32_t* k_sl;
+  uint32_t* v_sl;
+  uint32_t* k_prun;
+  uint32_t* v_mid;
+  const int16_t* kept_idx;
+  int64_t t_old;       // tokens in the cache before the append
+  int64_t t_new;       // tokens after it
+  int64_t n_new;
+  int64_t mid_cap;
+  int64_t unit_lo;     // kMigrate: position of unit 0
+  int64_t units_per_pair;
+  int64_t n_units;
+  int32_t n_kv;
+  int32_t n_sink;
+  int32_t window;
+  int32_t slots;
+  int32_t mode;
+  int32_t pad;
+  PackHead heads[LEANK_MAX_KV_HEADS];
+};
+
+constexpr int kWordsPerRow = LEANK_HEAD_DIM / 2;  // 64 words of two bf16
+constexpr int kUnitsPerBlock = 4;
+
+// Writes one token's K (kept channels) and V (live heads) to middle row r.
+__device__ __forceinline__ void write_middle(const PackParams& p, int b, int h, int64_t r,
+                                             uint32_t kw, uint32_t vw, int lane) {
+  const PackHead hd = p.heads[h];
+  if (hd.kept <= 0) return;  // fully pruned head: no middle K, no middle V
+  const int j0 = 2 * lane;
+  // channel ids are masked into [0, 128) so that bad ids cannot leave the row
+  const int c0 = j0 < hd.kept ? (p.kept_idx[h * LEANK_HEAD_DIM + j0] & (LEANK_HEAD_DIM - 1)) : 0;
+  const int c1 = j0 < hd.kept ? (p.kept_idx[h * LEANK_HEAD_DIM + j0 + 1] & (LEANK_HEAD_DIM - 1)) : 0;
+  const uint32_t w0 = static_cast<uint32_t>(__shfl(static_cast<int>(kw), c0 >> 1));
+  const uint32_t w1 = static_cast<uint32_t>(__shfl(static_cast<int>(kw), c1 >> 1));
+  const uint32_t lo = (c0 & 1) ? (w0 >> 16) : (w0 & 0xffffu);
+  const uint32_t hi = (c1 & 1) ? (w1 >> 16) : (w1 & 0xffffu);
+  const int64_t row = static_cast<int64_t>(b) * p.mid_cap + r;
+  if (j0 < hd.kept) p.k_prun[(hd.k_off + row * hd.kept) / 2 + lane] = lo | (hi << 16);
+  p.v_mid[(hd.v_off + row * LEANK_HEAD_DIM) / 2 + lane] = vw;
+}
+
+__global__ __launch_bounds__(64 * kUnitsPerBlock) void pack_kernel(const PackParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kUnitsPerBlock + (threadIdx.x >> 6);
+  if (unit >= p.n_units) return;  // whole wavefront leaves together
+  const int64_t pair = unit / p.units_per_pair;
+  const int64_t i = unit - pair * p.units_per_pair;
+  const int b = static_cast<int>(pair / p.n_kv);
+  const int h = static_cast<int>(pair - static_cast<int64_t>(b) * p.n_kv);
+  uint32_t* ring_k = p.k_sl + (pair * p.slots) * kWordsPerRow;
+  uint32_t* ring_v = p.v_sl + (pair * p.slots) * kWordsPerRow;
+
+  if (p.mode == kMigrate) {
+    const int64_t q = p.unit_lo + i;
+    const int64_t slot = p.n_sink + (q - p.n_sink) % p.window;
+    const uint32_t kw = ring_k[slot * kWordsPerRow + lane];
+    const uint32_t vw = ring_v[slot * kWordsPerRow + lane];
+    write_middle(p, b, h, q - p.n_sink, kw, vw, lane);
+    return;
+  }
+
+  const int64_t pos = p.t_old + i;
+  const int64_t src = (pair * p.n_new + i) * kWordsPerRow + lane;
+  const uint32_t kw = p.k_new[src];
+  const uint32_t vw = p.v_new[src];
+  if (pos < p.n_sink) {
+    ring_k[pos * kWordsPerRow + lane] = kw;
+    ring_v[pos * kWordsPerRow + lane] = vw;
+    return;
+  }
+  if (p.mode == kPlace && pos < p.t_new - p.window) {
+    write_middle(p, b, h, pos - p.n_sink, kw, vw, lane);  // already outside the window
+    return;
+  }
+  const int64_t slot = p.n_sink + (pos - p.n_sink) % p.window;
+  if (p.mode == kFused) {
+    const int64_t leaving = pos - p.window;  // token held by this ring row until now
+    if (leaving >= p.n_sink) {
+      const uint32_t old_k = ring_k[slot * kWordsPerRow + lane];
+      const uint32_t old_v = ring_v[slot * kWordsPerRow + lane];
+      write_middle(p, b, h, leaving - p.n_sink, old_k, old_v, lane);
+    }
+  }
+  ring_k[slot * kWordsPerRow + lane] = kw;
+  ring_v[slot * kWordsPerRow + lane] = vw;
+}
+
+int launch(PackParams& p, int64_t units_per_pair, int64_t pairs, hipStream_t s) {
+  p.units_per_pair = units_per_pair;
+  p.n_units = units_per_pair * pairs;
+  const int64_t blocks = (p.n_units + kUnitsPerBlock - 1) / kUnitsPerBlock;
+  if (blocks > INT32_MAX) return LEANK_EUNSUPPORTED;
+  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(64 * kUnitsPerBlock),
+                     0, s, p);
+  LEANK_HIP_TRY(hipGetLastError());
+  return LEANK_OK;
+}
+
+}  // namespace
+}  // namespace leank
+
+using namespace leank;
+
+extern "C" int leank_pack_k(const leank_layer_cache* c, const void* k_new, const void* v_new,
+                            int64_t pos0, int64_t n_new, void* stream) {
+  int st = validate_cache(c, true);
+  if (st != LEANK_OK) return st;
+  if (pos0 < 0 || n_new < 0) return LEANK_EINVAL;
+  if (n_new == 0) return LEANK_OK;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return LEANK_EINVAL;
+  if (pos0 + n_new > c->max_ctx) return LEANK_ECAPACITY;
+
+  PackParams p;
+  memset(&p, 0, sizeof(p));
+  p.k_new = static_cast<const uint32_t*>(k_new);
+  p.v_new = static_cast<const uint32_t*>(v_new);
+  p.k_sl = static_cast<uint32_t*>(c->k_sl);
+  p.v_sl = static_cast<uint32_t*>(c->v_sl);
+  p.k_prun = static_cast<uint32_t*>(c->k_prun);
+  p.v_mid = static_cast<uint32_t*>(c->v_mid);
+  p.kept_idx = c->kept_idx;
+  p.t_old = pos0;
+  p.t_new = pos0 + n_new;
+  p.n_new = n_new;
+  p.mid_cap = c->mid_capacity;
+  p.n_kv = c->n_kv_heads;
+  p.n_sink = c->n_sink;
+  p.window = c->window;
+  p.slots = c->n_sink + c->window;
+  for (int h = 0; h < c->n_kv_heads; ++h) {
+    p.heads[h].k_off = c->k_prun_off[h];
+    p.heads[h].v_off = c->v_mid_off[h];
+    p.heads[h].kept = c->kept_count[h];
+  }
+  const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (c->window > 0 && n_new <= c->window) {
+    p.mode = kFused;
+    return launch(p, n_new, pairs, s);
+  }
+  if (c->window > 0) {
+    // window tokens pushed out by this append move to the middle first
+    const int64_t lo = std::max<int64_t>(c->n_sink, pos0 - c->window);
+    const int64_t hi = std::min<int64_t>(pos0, pos0 + n_new - c->window);
+    if (hi > lo) {
+      p.mode = kMigrate;
+      p.unit_lo = lo;
+      st = launch(p, hi - lo, pairs, s);
+      if (st != LEANK_OK) return st;
+    }
+  }
+  p.mode = kPlace;
+  p.unit_lo = 0;
+  return launch(p, n_new, pairs, s);
+}

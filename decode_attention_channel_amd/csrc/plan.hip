@@ -1,0 +1,214 @@
+// Host-side entry points: status strings, layer plan (head grouping and
+// cache layout, LeanK page section 3.1 items 1-2), work decomposition of a
+// decode call, workspace sizing and algorithmic byte accounting.
+
+#include <string.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace leank {
+
+namespace {
+
+constexpr int64_t kRowQuantum = 64;        // item row counts are multiples of this
+constexpr int64_t kItemBytesWide = 160 << 10;  // target bytes per item, many (b, h) pairs
+constexpr int64_t kItemBytesNarrow = 64 << 10; // target bytes per item, few pairs
+constexpr int64_t kFewPairs = 64;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Rows per item for a stream whose rows take row_bytes: about `target`
+// bytes per item, a multiple of kRowQuantum, at least kRowQuantum.
+int64_t row_target(int64_t row_bytes, int64_t target) {
+  int64_t rows = (target / row_bytes) / kRowQuantum * kRowQuantum;
+  return std::max(rows, kRowQuantum);
+}
+
+// Splits `rows` rows into items of at most `target_rows` rows each (a
+// multiple of kRowQuantum).  `bound` receives an item count that never
+// decreases as `rows` grows (used for workspace sizing).
+void split_rows(int64_t rows, int64_t target_rows, int32_t* n_items, int32_t* rows_per_item,
+                int64_t* bound) {
+  if (rows <= 0) {
+    *n_items = 0;
+    *rows_per_item = 0;
+    *bound = 0;
+    return;
+  }
+  int64_t n = ceil_div(rows, target_rows);
+  int64_t per = ceil_div(ceil_div(rows, n), kRowQuantum) * kRowQuantum;
+  *bound = n;
+  *n_items = static_cast<int32_t>(ceil_div(rows, per));
+  *rows_per_item = static_cast<int32_t>(per);
+}
+
+}  // namespace
+
+int validate_cache(const leank_layer_cache* c, bool need_buffers) {
+  if (!c) return LEANK_EINVAL;
+  if (c->head_dim != LEANK_HEAD_DIM) return LEANK_EUNSUPPORTED;
+  if (c->n_kv_heads < 1 || c->n_kv_heads > LEANK_MAX_KV_HEADS) return LEANK_EINVAL;
+  if (c->n_q_heads < c->n_kv_heads || c->n_q_heads % c->n_kv_heads) return LEANK_EINVAL;
+  if (c->n_q_heads / c->n_kv_heads > LEANK_MAX_GROUP) return LEANK_EUNSUPPORTED;
+  if (c->batch < 1 || c->n_sink < 0 || c->window < 0) return LEANK_EINVAL;
+  if (static_cast<int64_t>(c->n_sink) + c->window < 1) return LEANK_EINVAL;
+  if (c->max_ctx < 1 || c->max_ctx > INT32_MAX) return LEANK_EINVAL;
+  if (c->mid_capacity != std::max<int64_t>(0, c->max_ctx - c->n_sink - c->window)) return LEANK_EINVAL;
+  int live = 0;
+  for (int h = 0; h < c->n_kv_heads; ++h) {
+    int k = c->kept_count[h];
+    if (k < 0 || k > LEANK_HEAD_DIM) return LEANK_EINVAL;
+    if (k % LEANK_CHANNEL_QUANTUM) return LEANK_EUNSUPPORTED;
+    if (k > 0) {
+      ++live;
+      if (c->k_prun_off[h] < 0 || c->v_mid_off[h] < 0) return LEANK_EINVAL;
+      if (c->k_prun_off[h] % LEANK_CHANNEL_QUANTUM || c->v_mid_off[h] % LEANK_HEAD_DIM) return LEANK_EINVAL;
+    }
+  }
+  if (live != c->n_live) return LEANK_EINVAL;
+  if (need_buffers) {
+    if (!c->k_sl || !c->v_sl || !c->kept_idx) return LEANK_EINVAL;
+    if (!aligned16(c->k_sl) || !aligned16(c->v_sl)) return LEANK_EINVAL;
+    if (c->k_prun_bytes && (!c->k_prun || !aligned16(c->k_prun))) return LEANK_EINVAL;
+    if (c->v_mid_bytes && (!c->v_mid || !aligned16(c->v_mid))) return LEANK_EINVAL;
+  }
+  return LEANK_OK;
+}
+
+int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, WorkPlan* w) {
+  memset(w, 0, sizeof(*w));
+  const int64_t slots = static_cast<int64_t>(c->n_sink) + c->window;
+  w->group = c->n_q_heads / c->n_kv_heads;
+  w->t_sl = static_cast<int32_t>(std::min<int64_t>(ctx_len, slots));
+  w->t_mid = static_cast<int32_t>(std::max<int64_t>(0, ctx_len - slots));
+  const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
+  const int64_t target = pairs >= kFewPairs ? kItemBytesWide : kItemBytesNarrow;
+
+  int64_t bound_per_b = 0, b;
+  split_rows(w->t_sl, row_target(2 * LEANK_HEAD_DIM * 2, target), &w->n_sl_items, &w->sl_rows, &b);
+  bound_per_b += b * c->n_kv_heads;
+  int32_t base = 0;
+  for (int h = 0; h < c->n_kv_heads; ++h) {
+    w->head_base[h] = base;
+    const int kept = c->kept_count[h];
+    if (kept > 0) {
+      split_rows(w->t_mid, row_target(2 * kept + 2 * LEANK_HEAD_DIM, target), &w->n_mid[h],
+                 &w->mid_rows[h], &b);
+      bound_per_b += b;
+    }
+    base += w->n_sl_items + w->n_mid[h];
+  }
+  w->head_base[c->n_kv_heads] = base;
+  w->items_per_b = base;
+  w->n_items = static_cast<int64_t>(base) * c->batch;
+
+  w->partial_stride = w->group * LEANK_HEAD_DIM + ((2 * w->group + 3) / 4) * 4;
+  const int64_t bound_items = bound_per_b * c->batch;
+  w->partial_bytes = static_cast<size_t>(bound_items) * w->partial_stride * sizeof(float);
+  w->counter_offset = (w->partial_bytes + 255) / 256 * 256;
+  w->workspace_bytes = (w->counter_offset + pairs * sizeof(uint32_t) + 255) / 256 * 256;
+  return LEANK_OK;
+}
+
+}  // namespace leank
+
+using namespace leank;
+
+extern "C" const char* leank_status_string(int status) {
+  switch (status) {
+    case LEANK_OK: return "LEANK_OK";
+    case LEANK_EINVAL: return "LEANK_EINVAL: invalid argument";
+    case LEANK_EUNSUPPORTED: return "LEANK_EUNSUPPORTED: shape outside what the kernels implement";
+    case LEANK_ECAPACITY: return "LEANK_ECAPACITY: position beyond the cache capacity";
+    case LEANK_EWORKSPACE: return "LEANK_EWORKSPACE: workspace missing or too small";
+    case LEANK_EHIP: return "LEANK_EHIP: HIP runtime or launch failure";
+    default: return "unknown leank status";
+  }
+}
+
+extern "C" int leank_abi_version(void) { return LEANK_ABI_VERSION; }
+
+extern "C" size_t leank_layer_cache_size(void) { return sizeof(leank_layer_cache); }
+
+extern "C" int leank_plan_layer(const int32_t* kept_count_host, int32_t batch, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t head_dim, int32_t n_sink,
+                                int32_t window, int64_t max_ctx, leank_layer_cache* out) {
+  if (!kept_count_host || !out) return LEANK_EINVAL;
+  leank_layer_cache c;
+  memset(&c, 0, sizeof(c));
+  c.batch = batch;
+  c.n_q_heads = n_q_heads;
+  c.n_kv_heads = n_kv_heads;
+  c.head_dim = head_dim;
+  c.n_sink = n_sink;
+  c.window = window;
+  c.max_ctx = max_ctx;
+  if (n_kv_heads < 1 || n_kv_heads > LEANK_MAX_KV_HEADS) return LEANK_EINVAL;
+  c.mid_capacity = std::max<int64_t>(0, max_ctx - static_cast<int64_t>(n_sink) - window);
+
+  int order[LEANK_MAX_KV_HEADS];
+  for (int h = 0; h < n_kv_heads; ++h) {
+    c.kept_count[h] = kept_count_host[h];
+    order[h] = h;
+    c.k_prun_off[h] = -1;
+    c.v_mid_off[h] = -1;
+  }
+  // Head grouping: live heads by kept count (descending, then id), dead heads last.
+  std::stable_sort(order, order + n_kv_heads, [&](int a, int b) {
+    return c.kept_count[a] > c.kept_count[b];
+  });
+  int64_t k_off = 0, v_off = 0;
+  for (int n = 0; n < n_kv_heads; ++n) {
+    const int h = order[n];
+    c.group_order[n] = h;
+    const int kept = c.kept_count[h];
+    if (kept <= 0) continue;
+    ++c.n_live;
+    c.k_prun_off[h] = k_off;
+    c.v_mid_off[h] = v_off;
+    k_off += static_cast<int64_t>(batch) * c.mid_capacity * kept;
+    v_off += static_cast<int64_t>(batch) * c.mid_capacity * LEANK_HEAD_DIM;
+  }
+  const int64_t slots = static_cast<int64_t>(n_sink) + window;
+  c.k_sl_bytes = static_cast<uint64_t>(batch) * n_kv_heads * slots * LEANK_HEAD_DIM * 2;
+  c.v_sl_bytes = c.k_sl_bytes;
+  c.k_prun_bytes = static_cast<uint64_t>(k_off) * 2;
+  c.v_mid_bytes = static_cast<uint64_t>(v_off) * 2;
+  int st = validate_cache(&c, false);
+  if (st != LEANK_OK) return st;
+  *out = c;
+  return LEANK_OK;
+}
+
+extern "C" int leank_workspace_bytes(const leank_layer_cache* cache, int64_t ctx_len,
+                                     size_t* bytes_out) {
+  int st = validate_cache(cache, false);
+  if (st != LEANK_OK) return st;
+  if (!bytes_out || ctx_len < 1) return LEANK_EINVAL;
+  if (ctx_len > cache->max_ctx) return LEANK_ECAPACITY;
+  WorkPlan w;
+  make_work_plan(cache, ctx_len, &w);
+  *bytes_out = w.workspace_bytes;
+  return LEANK_OK;
+}
+
+extern "C" int leank_decode_bytes(const leank_layer_cache* c, int64_t ctx_len, int64_t* bytes_out) {
+  int st = validate_cache(c, false);
+  if (st != LEANK_OK) return st;
+  if (!bytes_out || ctx_len < 1) return LEANK_EINVAL;
+  if (ctx_len > c->max_ctx) return LEANK_ECAPACITY;
+  const int64_t slots = static_cast<int64_t>(c->n_sink) + c->window;
+  const int64_t t_sl = std::min<int64_t>(ctx_len, slots);
+  const int64_t t_mid = std::max<int64_t>(0, ctx_len - slots);
+  const int64_t bq = static_cast<int64_t>(c->batch) * c->n_q_heads * LEANK_HEAD_DIM;
+  int64_t kept_sum = 0;
+  for (int h = 0; h < c->n_kv_heads; ++h) kept_sum += c->kept_count[h];
+  int64_t bytes = bq * 2 + bq * 4;
+  bytes += 2 * static_cast<int64_t>(c->batch) * c->n_kv_heads * t_sl * LEANK_HEAD_DIM * 2;
+  bytes += static_cast<int64_t>(c->batch) * t_mid * kept_sum * 2;
+  bytes += static_cast<int64_t>(c->batch) * c->n_live * t_mid * LEANK_HEAD_DIM * 2;
+  *bytes_out = bytes;
+  return LEANK_OK;
+}

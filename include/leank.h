@@ -1,0 +1,233 @@
+/*
+ * leank.h -- C ABI of the MI355X (gfx950) library for single-token decode
+ * attention over a statically channel-pruned KV cache (LeanK style).
+ *
+ * The method is described on the page "大型语言模型KV缓存优化与LeanK剪枝技术解析"
+ * (framerc.cn), called "the LeanK page" below:
+ *   - section 2.2, stage 2: a binary channel mask from a learned importance
+ *     alpha -- one global percentile threshold, a per-head count floored to
+ *     a hardware alignment, then the top channels of each head;
+ *   - section 3.1 items 1-3: heads grouped by kept-channel count, a
+ *     full-width cache for the sink and local-window tokens, a compacted
+ *     cache (K_prun) for the middle of the context, and one fused
+ *     attention pass that loads only the kept channels;
+ *   - section 3.2: a head with every channel pruned needs no middle V.
+ * Grouped-query attention (a group of query heads shares one KV head) is as
+ * in section 5.2.3 of "智能剪枝深度解析：大型语言模型KV缓存优化技术白皮书"; the
+ * softmax scale convention Softmax(QK^T / sqrt(d)) is section 5.3 of the
+ * FastGen page (mhpn.cn).
+ *
+ * Conventions for every entry point:
+ *   - All buffers are caller-owned.  The library allocates no device memory
+ *     and keeps no state between calls; every function is re-entrant.
+ *   - "device" pointers address HIP device memory of the current device;
+ *     "host" pointers address ordinary host memory.
+ *   - bf16 tensors are passed as raw 16-bit patterns (void*).
+ *   - Argument checks run on the host before any launch and return a
+ *     negative leank_status; nothing is written then.  A failed launch or
+ *     HIP call returns LEANK_EHIP.  No C++ exception crosses this boundary.
+ *   - Asynchronous entry points enqueue work on `stream` (a hipStream_t
+ *     passed as void*, NULL = the null stream) and return immediately.
+ */
+#ifndef LEANK_H
+#define LEANK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LEANK_ABI_VERSION 1
+#define LEANK_HEAD_DIM 128      /* the only head_dim the kernels implement   */
+#define LEANK_MAX_KV_HEADS 64   /* per-layer KV heads a cache plan can hold  */
+#define LEANK_MAX_GROUP 8       /* query heads per KV head the kernels take  */
+#define LEANK_CHANNEL_QUANTUM 8 /* kept counts must be multiples of this     */
+
+typedef enum {
+  LEANK_OK = 0,
+  LEANK_EINVAL = -1,        /* null pointer, size out of range, misaligned buffer, NaN in alpha */
+  LEANK_EUNSUPPORTED = -2,  /* valid request outside what the kernels implement */
+  LEANK_ECAPACITY = -3,     /* a position or context length beyond max_ctx */
+  LEANK_EWORKSPACE = -4,    /* workspace missing or smaller than leank_workspace_bytes() */
+  LEANK_EHIP = -5           /* a HIP runtime call or kernel launch failed */
+} leank_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* leank_status_string(int status);
+
+/* LEANK_ABI_VERSION of the built library. */
+int leank_abi_version(void);
+
+/* sizeof(leank_layer_cache) of the built library (lets bindings check their mirror). */
+size_t leank_layer_cache_size(void);
+
+/*
+ * leank_build_mask -- the stage-2 mask of the LeanK page, section 2.2.
+ *
+ * alpha       device, float32 [n_layers][n_kv_heads][head_dim], finite or
+ *             +-inf (NaN -> LEANK_EINVAL).  -0.0 and +0.0 compare equal.
+ * prune_pct   prune ratio in percent, 0..100.  The global threshold is the
+ *             order statistic of all n = n_layers*n_kv_heads*head_dim
+ *             values at ascending rank ceil((n-1)*prune_pct/100), which is
+ *             the set a linear-interpolation percentile selects; channels
+ *             with alpha >= threshold pass the global step.
+ * align       >= 1 and divides head_dim.  Each head's passing count is
+ *             floored to a multiple of align; that many channels with the
+ *             largest alpha of the head are kept, ties towards the lower
+ *             channel index.
+ * mask_out        device, uint8 [L][H][d]: 1 = kept.
+ * kept_count_out  device, int32 [L][H]: kept channels per head.
+ * kept_idx_out    device, int16 [L][H][d]: kept channel ids in ascending
+ *                 order, then -1 padding.
+ *
+ * Runs two kernels on `stream` and waits for them (the threshold is read
+ * back to the host between them through kept_count_out[0]); returns only
+ * after the outputs are complete.  Host-side cost is one 4-byte copy.
+ */
+int leank_build_mask(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
+                     int32_t head_dim, int32_t prune_pct, int32_t align,
+                     uint8_t* mask_out, int32_t* kept_count_out,
+                     int16_t* kept_idx_out, void* stream);
+
+/*
+ * One layer's channel-pruned KV cache: shape, head grouping and buffer
+ * layout.  leank_plan_layer fills every field above `kept_idx`; the caller
+ * allocates the four cache buffers with at least the *_bytes reported and
+ * sets the pointers.  Layout (bf16 elements, row-major):
+ *
+ *   k_sl, v_sl  [batch][n_kv_heads][n_sink + window][128]
+ *               full-width sink + local-window rows (LeanK page, section
+ *               3.1 item 2).  Token p < n_sink lives in row p; a window
+ *               token p >= n_sink in ring row n_sink + (p - n_sink) % window.
+ *   k_prun      per live head h, at element offset k_prun_off[h]:
+ *               [batch][mid_capacity][kept_count[h]] -- middle-of-context
+ *               keys reduced to the kept channels, in ascending channel
+ *               order; middle token p is row p - n_sink.
+ *   v_mid       per live head h, at element offset v_mid_off[h]:
+ *               [batch][mid_capacity][128] -- middle values.  Fully pruned
+ *               heads have no segment (LeanK page, section 3.2).
+ *
+ * Live heads are grouped by kept count (descending, then head id): their
+ * segments follow `group_order`, so heads of one width form one contiguous
+ * region (LeanK page, section 3.1 item 1).
+ */
+typedef struct leank_layer_cache {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t n_sink;
+  int32_t window;
+  int64_t max_ctx;        /* tokens the cache can hold */
+  int64_t mid_capacity;   /* max(0, max_ctx - n_sink - window) */
+  int32_t n_live;         /* heads with kept_count > 0 */
+  int32_t reserved0;
+  int32_t kept_count[LEANK_MAX_KV_HEADS];
+  int32_t group_order[LEANK_MAX_KV_HEADS];  /* live heads by (count desc, id asc), then dead */
+  int64_t k_prun_off[LEANK_MAX_KV_HEADS];   /* elements; -1 for dead heads */
+  int64_t v_mid_off[LEANK_MAX_KV_HEADS];    /* elements; -1 for dead heads */
+  uint64_t k_sl_bytes;
+  uint64_t v_sl_bytes;
+  uint64_t k_prun_bytes;
+  uint64_t v_mid_bytes;
+  /* set by the caller: */
+  const int16_t* kept_idx; /* device int16 [n_kv_heads][128], as leank_build_mask writes it */
+  void* k_sl;              /* device, 16-byte aligned */
+  void* v_sl;
+  void* k_prun;
+  void* v_mid;
+} leank_layer_cache;
+
+/*
+ * leank_plan_layer -- host, pure.  kept_count_host: host int32
+ * [n_kv_heads] (one layer's row of kept_count_out).  Requirements:
+ * head_dim == 128; 1 <= n_kv_heads <= LEANK_MAX_KV_HEADS; n_q_heads a
+ * multiple of n_kv_heads with n_q_heads / n_kv_heads <= LEANK_MAX_GROUP;
+ * every kept count in [0, 128] and a multiple of LEANK_CHANNEL_QUANTUM
+ * (LEANK_EUNSUPPORTED otherwise); batch >= 1; n_sink, window >= 0 with
+ * n_sink + window >= 1 (so every head always has a full-width token);
+ * max_ctx >= 1.  Clears the caller-set pointer fields.
+ */
+int leank_plan_layer(const int32_t* kept_count_host, int32_t batch,
+                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                     int32_t n_sink, int32_t window, int64_t max_ctx,
+                     leank_layer_cache* cache_out);
+
+/*
+ * leank_pack_k -- append n_new tokens at positions [pos0, pos0 + n_new)
+ * (LeanK page, section 3.1 item 2).  pos0 must equal the number of tokens
+ * already in the cache (append-only; the library does not track it).
+ *
+ * k_new, v_new  device bf16 [batch][n_kv_heads][n_new][128].
+ *
+ * Sink tokens go to their rows of k_sl/v_sl.  Window tokens go to their
+ * ring rows; a token that the append pushes out of the window is first
+ * moved to the middle: its kept K channels gathered into k_prun and its V
+ * row copied into v_mid (dropped for fully pruned heads).  New tokens that
+ * are already out of the window when the append ends go straight to the
+ * middle.  Bit copies only.  Errors: LEANK_ECAPACITY if pos0 + n_new >
+ * max_ctx.  n_new == 0 is a no-op.  One kernel when n_new <= window, two
+ * otherwise; asynchronous on `stream`.
+ */
+int leank_pack_k(const leank_layer_cache* cache, const void* k_new,
+                 const void* v_new, int64_t pos0, int64_t n_new, void* stream);
+
+/*
+ * leank_workspace_bytes -- host.  Bytes of device workspace
+ * leank_decode_attn needs for a context of ctx_len tokens (non-decreasing
+ * in ctx_len, so the size for max_ctx serves every call).
+ */
+int leank_workspace_bytes(const leank_layer_cache* cache, int64_t ctx_len,
+                          size_t* bytes_out);
+
+/*
+ * leank_workspace_init -- zero a workspace before its first use.  A
+ * workspace allocated zero-filled (e.g. torch.zeros) needs no init.  Every
+ * leank_decode_attn call that completes leaves the workspace ready for the
+ * next.  Asynchronous on `stream` (a fill kernel, no memset node).
+ */
+int leank_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * leank_decode_attn -- one decode step of attention for every (batch row,
+ * query head) of one layer (LeanK page, section 3.1 item 3 and section
+ * 3.2).
+ *
+ * q         device bf16 [batch][n_q_heads][128]; query head j reads KV
+ *           head j / (n_q_heads / n_kv_heads).
+ * ctx_len   tokens in the cache (1..max_ctx), newest included.
+ * scale     softmax scale, normally 1/sqrt(128).
+ * out       device float32 [batch][n_q_heads][128].
+ *
+ * For query head j of KV head h, over the cached tokens t:
+ *   score(t) = scale * q_j . K[t]            sink and window tokens,
+ *   score(t) = scale * sum_i q_j[idx_h[i]] K_prun[t][i]
+ *                                            middle tokens of a live head,
+ *   middle tokens of a fully pruned head take no part;
+ *   out_j = sum_t softmax(score)_t V[t].
+ * bf16 inputs, float32 accumulation.  The context is split into work items
+ * whose partial (max, sum, weighted V) results are merged by the last item
+ * of each (batch row, KV head) in a fixed order, so the output does not
+ * depend on scheduling.  One kernel launch, asynchronous on `stream`.
+ * Calls that share a workspace must not overlap in time.
+ */
+int leank_decode_attn(const leank_layer_cache* cache, const void* q,
+                      int64_t ctx_len, float scale, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * leank_decode_bytes -- host.  Algorithmic HBM bytes of one
+ * leank_decode_attn call: q (bf16) + full-width K and V of every head +
+ * kept K channels and V of live heads over the middle + out (float32).
+ * The split-K workspace traffic is not counted.
+ */
+int leank_decode_bytes(const leank_layer_cache* cache, int64_t ctx_len,
+                       int64_t* bytes_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LEANK_H */

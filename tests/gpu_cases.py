@@ -1,0 +1,118 @@
+"""Helpers for the GPU parity tests: build caches through the C ABI, read
+their buffers back, and compare with the CPU oracle."""
+
+import numpy as np
+import torch
+
+import decode_attention_channel_amd as dac
+import oracle
+from synthetic import bf16_bits
+
+# max |gpu - oracle| <= ATOL + RTOL * |oracle|, elementwise (bf16 inputs,
+# float32 accumulation against a float64 oracle)
+ATOL = 2e-3
+RTOL = 1e-2
+
+
+def assert_close(gpu, ref, what=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    err = np.abs(gpu - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    worst = np.argmax(err - bound)
+    assert np.all(err <= bound), (
+        f"{what}: max err {err.ravel()[worst]:.3e} > bound {bound.ravel()[worst]:.3e} "
+        f"at {np.unravel_index(worst, err.shape)}")
+
+
+def kept_from_mask(mask):
+    """kept_count [H] and kept_idx [H, 128] (ascending, -1 padded) of a 0/1 mask [H, 128]."""
+    mask = np.asarray(mask)
+    n_heads, d = mask.shape
+    kept_count = mask.sum(axis=1).astype(np.int32)
+    kept_idx = np.full((n_heads, d), -1, dtype=np.int16)
+    for h in range(n_heads):
+        kept_idx[h, :kept_count[h]] = np.flatnonzero(mask[h])
+    return kept_count, kept_idx
+
+
+def mask_with_counts(rng, counts, d=128):
+    mask = np.zeros((len(counts), d), dtype=np.uint8)
+    for h, c in enumerate(counts):
+        if c:
+            mask[h, np.sort(rng.choice(d, size=c, replace=False))] = 1
+    return mask
+
+
+def make_cache(mask, batch, n_q, n_sink, window, max_ctx, device="cuda"):
+    kept_count, kept_idx = kept_from_mask(mask)
+    kept_dev = torch.from_numpy(kept_idx).to(device)
+    return dac.LayerCache(kept_count.tolist(), kept_dev, batch, n_q, mask.shape[0], n_sink,
+                          window, max_ctx, device=device)
+
+
+def random_bf16(shape, gen, scale=1.0, device="cuda"):
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return (x * scale).to(torch.bfloat16)
+
+
+def read_cache(cache):
+    """Host uint16 views of the cache buffers, split per head as the plan lays them out."""
+    d = cache.desc
+    batch, n_kv = d.batch, d.n_kv_heads
+    slots = d.n_sink + d.window
+    mid_cap = d.mid_capacity
+    k_sl = bf16_bits(cache.k_sl)[: batch * n_kv * slots * 128].reshape(batch, n_kv, slots, 128)
+    v_sl = bf16_bits(cache.v_sl)[: batch * n_kv * slots * 128].reshape(batch, n_kv, slots, 128)
+    k_prun_all = bf16_bits(cache.k_prun)
+    v_mid_all = bf16_bits(cache.v_mid)
+    k_prun, v_mid = [], []
+    for h in range(n_kv):
+        c = d.kept_count[h]
+        if c == 0:
+            k_prun.append(None)
+            v_mid.append(None)
+            continue
+        ko, vo = d.k_prun_off[h], d.v_mid_off[h]
+        k_prun.append(k_prun_all[ko: ko + batch * mid_cap * c].reshape(batch, mid_cap, c))
+        v_mid.append(v_mid_all[vo: vo + batch * mid_cap * 128].reshape(batch, mid_cap, 128))
+    return {"k_sl": k_sl, "v_sl": v_sl, "k_prun": k_prun, "v_mid": v_mid}
+
+
+def assert_cache_matches(cache, k_bits, v_bits, mask, pairs=None):
+    """Bit-exact comparison of the cache with the oracle's packing of the
+    full context k_bits/v_bits [B, H, T, d] (optionally for some (b, h) only:
+    then k_bits/v_bits hold just those rows, in the order of `pairs`)."""
+    d = cache.desc
+    kept_count, kept_idx = kept_from_mask(mask)
+    got = read_cache(cache)
+    if pairs is None:
+        pairs = [(b, h) for b in range(d.batch) for h in range(d.n_kv_heads)]
+        rows = {(b, h): (b, h) for b, h in pairs}
+    else:
+        rows = {pair: (n, 0) for n, pair in enumerate(pairs)}
+    for (b, h) in pairs:
+        rb, rh = rows[(b, h)]
+        one_k = k_bits[rb:rb + 1, rh:rh + 1]
+        one_v = v_bits[rb:rb + 1, rh:rh + 1]
+        ref = oracle.pack_reference(one_k, one_v, kept_count[h:h + 1], kept_idx[h:h + 1],
+                                    d.n_sink, d.window)
+        for slot, pos in enumerate(ref["slot_pos"]):
+            if pos < 0:
+                continue
+            assert np.array_equal(got["k_sl"][b, h, slot], ref["ring_k"][0, 0, slot]), (b, h, slot, pos)
+            assert np.array_equal(got["v_sl"][b, h, slot], ref["ring_v"][0, 0, slot]), (b, h, slot, pos)
+        n_mid = ref["k_prun"][0].shape[1]
+        if kept_count[h] == 0:
+            assert got["k_prun"][h] is None and ref["v_mid"][0] is None
+            continue
+        assert np.array_equal(got["k_prun"][h][b, :n_mid], ref["k_prun"][0][0]), (b, h)
+        assert np.array_equal(got["v_mid"][h][b, :n_mid], ref["v_mid"][0][0]), (b, h)
+
+
+def oracle_outputs(q, k, v, mask, n_sink, window, pairs=None):
+    """Oracle decode for torch bf16 tensors (host copies of the same bits)."""
+    return oracle.decode(bf16_bits(q), bf16_bits(k), bf16_bits(v), mask, n_sink, window,
+                         pairs=pairs)

@@ -1,0 +1,162 @@
+"""Host-side checks of the C ABI: loading, exported symbols, plan logic, byte
+accounting and argument errors that return before any kernel launch.
+
+No call here launches a kernel: every failing call is rejected by the
+host-side validation, and the success paths exercised are pure host code.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_attention_channel_amd as dac
+import oracle
+from decode_attention_channel_amd import _lib
+from synthetic import CONFIGS, alpha_for
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "leank.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(leank_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = _lib.lib()
+    names = declared_functions()
+    assert "leank_build_mask" in names and "leank_pack_k" in names and "leank_decode_attn" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.leank_abi_version() == 1
+    assert lib.leank_layer_cache_size() == ctypes.sizeof(_lib.LayerCacheDesc)
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert dac.status_string(code).startswith("LEANK_")
+    assert "unknown" in dac.status_string(42)
+
+
+def test_plan_groups_heads_by_kept_count():
+    kept = [32, 0, 64, 32, 128, 0, 96, 32]
+    batch, max_ctx, n_sink, window = 3, 1000, 4, 60
+    d = dac.leank_plan_layer(kept, batch, 16, 8, 128, n_sink, window, max_ctx)
+    mid_cap = max_ctx - n_sink - window
+    assert d.mid_capacity == mid_cap and d.n_live == 6
+    order = [d.group_order[n] for n in range(8)]
+    assert order == [4, 6, 2, 0, 3, 7, 1, 5]
+    k_off = v_off = 0
+    for h in order:
+        if kept[h] == 0:
+            assert d.k_prun_off[h] == -1 and d.v_mid_off[h] == -1
+            continue
+        assert d.k_prun_off[h] == k_off and d.v_mid_off[h] == v_off
+        k_off += batch * mid_cap * kept[h]
+        v_off += batch * mid_cap * 128
+    assert d.k_prun_bytes == 2 * k_off and d.v_mid_bytes == 2 * v_off
+    assert d.k_sl_bytes == d.v_sl_bytes == batch * 8 * (n_sink + window) * 128 * 2
+    assert [d.kept_count[h] for h in range(8)] == kept
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(head_dim=64), _lib.EUNSUPPORTED),
+    (dict(kept=[12, 32]), _lib.EUNSUPPORTED),
+    (dict(kept=[136, 32]), _lib.EINVAL),
+    (dict(n_q=18), _lib.EUNSUPPORTED),      # 9 query heads per KV head
+    (dict(n_q=3), _lib.EINVAL),             # not a multiple of n_kv
+    (dict(n_sink=0, window=0), _lib.EINVAL),
+    (dict(batch=0), _lib.EINVAL),
+    (dict(max_ctx=0), _lib.EINVAL),
+    (dict(n_sink=-1), _lib.EINVAL),
+])
+def test_plan_rejects(args, status):
+    kw = dict(kept=[32, 64], batch=2, n_q=4, head_dim=128, n_sink=4, window=8, max_ctx=100)
+    kw.update(args)
+    with pytest.raises(dac.LeankError) as err:
+        dac.leank_plan_layer(kw["kept"], kw["batch"], kw["n_q"], 2, kw["head_dim"],
+                             kw["n_sink"], kw["window"], kw["max_ctx"])
+    assert err.value.status == status
+
+
+def test_plan_rejects_too_many_heads():
+    with pytest.raises(dac.LeankError):
+        dac.leank_plan_layer([32] * 65, 1, 65, 65, 128, 4, 8, 100)
+
+
+@pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
+def test_decode_bytes_match_oracle_accounting(cfg):
+    _, kept_count, _ = oracle.build_mask(alpha_for(cfg), cfg.prune_pct, cfg.align)
+    for layer in range(min(cfg.n_layers, 3)):
+        kept = kept_count[layer].tolist()
+        desc = dac.leank_plan_layer(kept, cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, 128,
+                                    cfg.n_sink, cfg.window, cfg.max_ctx)
+        for ctx in sorted({1, cfg.n_sink, cfg.n_sink + cfg.window, cfg.n_sink + cfg.window + 1,
+                           cfg.ctx, cfg.max_ctx}):
+            if ctx < 1:
+                continue
+            got = dac.leank_decode_bytes(desc, ctx)
+            assert got == oracle.decode_traffic_bytes(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads,
+                                                       128, ctx, cfg.n_sink, cfg.window, kept)
+
+
+def test_workspace_grows_with_context():
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        n_kv = int(rng.integers(1, 9))
+        group = int(rng.integers(1, 9))
+        kept = [int(x) for x in rng.integers(0, 17, size=n_kv) * 8]
+        batch = int(rng.integers(1, 70))
+        n_sink, window = int(rng.integers(0, 70)), int(rng.integers(1, 700))
+        max_ctx = int(rng.integers(1, 20000))
+        desc = dac.leank_plan_layer(kept, batch, n_kv * group, n_kv, 128, n_sink, window, max_ctx)
+        prev = 0
+        for ctx in sorted(set(rng.integers(1, max_ctx + 1, size=40).tolist()) | {max_ctx}):
+            ws = dac.leank_workspace_bytes(desc, ctx)
+            assert ws >= prev and ws % 256 == 0
+            prev = ws
+
+
+def _fake_buffers(desc):
+    # 16-byte aligned, never dereferenced: each call below fails validation first
+    desc.kept_idx = desc.k_sl = desc.v_sl = desc.k_prun = desc.v_mid = 0x1000
+    return desc
+
+
+def test_calls_rejected_before_launch():
+    L = _lib.lib()
+    desc = dac.leank_plan_layer([32, 0], 2, 4, 2, 128, 4, 8, 100)
+    ref = ctypes.byref(desc)
+    # buffers not set
+    assert L.leank_decode_attn(ref, 0x1000, 10, 0.1, 0x1000, 0x1000, 1 << 20, None) == _lib.EINVAL
+    assert L.leank_pack_k(ref, 0x1000, 0x1000, 0, 1, None) == _lib.EINVAL
+    _fake_buffers(desc)
+    ws = dac.leank_workspace_bytes(desc, 100)
+    assert L.leank_decode_attn(ref, 0x1000, 0, 0.1, 0x1000, 0x1000, ws, None) == _lib.EINVAL
+    assert L.leank_decode_attn(ref, 0x1000, 101, 0.1, 0x1000, 0x1000, ws, None) == _lib.ECAPACITY
+    assert L.leank_decode_attn(ref, 0x1000, 100, 0.1, 0x1000, 0x1000, ws - 1, None) == _lib.EWORKSPACE
+    assert L.leank_decode_attn(ref, 0x1000, 100, 0.1, 0x1000, None, ws, None) == _lib.EWORKSPACE
+    assert L.leank_decode_attn(ref, 0x1001, 100, 0.1, 0x1000, 0x1000, ws, None) == _lib.EINVAL
+    assert L.leank_decode_attn(ref, 0x1000, 100, float("nan"), 0x1000, 0x1000, ws, None) == _lib.EINVAL
+    assert L.leank_decode_attn(ref, 0x1000, 100, -1.0, 0x1000, 0x1000, ws, None) == _lib.EINVAL
+    assert L.leank_pack_k(ref, 0x1000, 0x1000, 99, 2, None) == _lib.ECAPACITY
+    assert L.leank_pack_k(ref, 0x1000, 0x1000, -1, 1, None) == _lib.EINVAL
+    assert L.leank_pack_k(ref, 0x1000, 0x1008, 0, 1, None) == _lib.EINVAL
+    assert L.leank_pack_k(ref, 0x1000, 0x1000, 5, 0, None) == _lib.OK   # empty append: no launch
+    assert L.leank_decode_attn(None, 0x1000, 1, 0.1, 0x1000, 0x1000, ws, None) == _lib.EINVAL
+
+
+def test_build_mask_rejected_before_launch():
+    L = _lib.lib()
+    p = ctypes.c_void_p(0x1000)
+    assert L.leank_build_mask(None, 1, 2, 128, 50, 32, p, p, p, None) == _lib.EINVAL
+    assert L.leank_build_mask(p, 1, 2, 128, 101, 32, p, p, p, None) == _lib.EINVAL
+    assert L.leank_build_mask(p, 1, 2, 128, -1, 32, p, p, p, None) == _lib.EINVAL
+    assert L.leank_build_mask(p, 1, 2, 128, 50, 48, p, p, p, None) == _lib.EINVAL
+    assert L.leank_build_mask(p, 1, 2, 128, 50, 0, p, p, p, None) == _lib.EINVAL
+    assert L.leank_build_mask(p, 0, 2, 128, 50, 32, p, p, p, None) == _lib.EINVAL
