@@ -39,7 +39,6 @@ struct WorkPlan {
   int64_t n_items;
   int32_t partial_stride;  // floats per item record
   size_t partial_bytes;
-  size_t counter_offset;   // bytes
   size_t workspace_bytes;
 };
 

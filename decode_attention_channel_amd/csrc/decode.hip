@@ -24,9 +24,10 @@
 //
 // Merge.  The 4 rows of a wavefront share the running max, so their sums
 // and V accumulators add directly (permlane16/32 swaps).  The 4 wavefronts
-// merge through LDS into one (max, sum, acc[G][128]) record per item.  The
-// last item of a (b, h) pair to finish -- counted with a device-scope
-// atomic -- merges the pair's records in item order and writes the output.
+// merge through LDS into one (max, sum, acc[G][128]) record per item.  A
+// second kernel merges each (b, h) pair's records in item order and writes
+// the output, so the result does not depend on scheduling and no workgroup
+// waits on another.
 
 #include <math.h>
 
@@ -57,7 +58,6 @@ struct DecodeParams {
   const int16_t* kept_idx;
   float* out;
   float* partials;
-  uint32_t* counters;
   int64_t mid_cap;
   int32_t n_kv;
   int32_t n_q;
@@ -270,11 +270,10 @@ __device__ __forceinline__ void load_q_gather(const uint16_t* qh, const int16_t*
 }
 
 template <int G>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeParams p) {
   __shared__ float s_acc[kWaves][G][LEANK_HEAD_DIM];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
-  __shared__ int s_last;
 
   const int item = blockIdx.x;
   const int b = item / p.items_per_b;
@@ -392,37 +391,35 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
       rec[G * LEANK_HEAD_DIM + G + g] = l;
     }
   }
+}
 
-  // the last item of the (b, h) pair merges the pair's records
-  __threadfence();
-  __syncthreads();
-  const int64_t pair = static_cast<int64_t>(b) * p.n_kv + h;
-  const int n_pair_items = p.n_sl_items + hd.n_mid;
-  if (threadIdx.x == 0) {
-    const uint32_t done = atomicAdd(p.counters + pair, 1u);
-    s_last = done + 1 == static_cast<uint32_t>(n_pair_items);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float* first = p.partials + static_cast<int64_t>(b * p.items_per_b + hd.base) * p.partial_stride;
+// Merges the records of one (batch row, KV head) pair in item order and
+// writes the G query heads' outputs.  One workgroup per pair.
+template <int G>
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodeParams p) {
+  const int64_t pair = blockIdx.x;
+  const int b = static_cast<int>(pair / p.n_kv);
+  const int h = static_cast<int>(pair - static_cast<int64_t>(b) * p.n_kv);
+  const DecodeHead hd = p.heads[h];
+  const int n_items = p.n_sl_items + hd.n_mid;
+  const float* first =
+      p.partials + (static_cast<int64_t>(b) * p.items_per_b + hd.base) * p.partial_stride;
   float* out = p.out + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM;
   for (int t = threadIdx.x; t < G * LEANK_HEAD_DIM; t += kThreads) {
     const int g = t / LEANK_HEAD_DIM;
     float m = -INFINITY;
-    for (int n = 0; n < n_pair_items; ++n)
-      m = fmaxf(m, __builtin_nontemporal_load(first + n * p.partial_stride + G * LEANK_HEAD_DIM + g));
+    for (int n = 0; n < n_items; ++n)
+      m = fmaxf(m, first[n * p.partial_stride + G * LEANK_HEAD_DIM + g]);
     const float m_use = m == -INFINITY ? 0.0f : m;
     float a = 0.0f, l = 0.0f;
-    for (int n = 0; n < n_pair_items; ++n) {
+    for (int n = 0; n < n_items; ++n) {
       const float* rn = first + n * p.partial_stride;
-      const float f = fast_exp2(__builtin_nontemporal_load(rn + G * LEANK_HEAD_DIM + g) - m_use);
-      a = fmaf(__builtin_nontemporal_load(rn + t), f, a);
-      l = fmaf(__builtin_nontemporal_load(rn + G * LEANK_HEAD_DIM + G + g), f, l);
+      const float f = fast_exp2(rn[G * LEANK_HEAD_DIM + g] - m_use);
+      a = fmaf(rn[t], f, a);
+      l = fmaf(rn[G * LEANK_HEAD_DIM + G + g], f, l);
     }
     out[t] = a / l;
   }
-  if (threadIdx.x == 0) p.counters[pair] = 0u;  // ready for the next call
 }
 
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n_words) {
@@ -432,8 +429,12 @@ __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n_words) {
 }
 
 template <int G>
-int launch_decode(const DecodeParams& p, int64_t n_items, hipStream_t s) {
-  hipLaunchKernelGGL(decode_kernel<G>, dim3(static_cast<unsigned>(n_items)), dim3(kThreads), 0, s, p);
+int launch_decode(const DecodeParams& p, int64_t n_items, int64_t n_pairs, hipStream_t s) {
+  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(static_cast<unsigned>(n_items)), dim3(kThreads),
+                     0, s, p);
+  LEANK_HIP_TRY(hipGetLastError());
+  hipLaunchKernelGGL(decode_combine_kernel<G>, dim3(static_cast<unsigned>(n_pairs)),
+                     dim3(kThreads), 0, s, p);
   LEANK_HIP_TRY(hipGetLastError());
   return LEANK_OK;
 }
@@ -479,7 +480,6 @@ extern "C" int leank_decode_attn(const leank_layer_cache* c, const void* q, int6
   p.kept_idx = c->kept_idx;
   p.out = out;
   p.partials = static_cast<float*>(workspace);
-  p.counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + w.counter_offset);
   p.mid_cap = c->mid_capacity;
   p.n_kv = c->n_kv_heads;
   p.n_q = c->n_q_heads;
@@ -500,15 +500,16 @@ extern "C" int leank_decode_attn(const leank_layer_cache* c, const void* q, int6
     p.heads[h].base = w.head_base[h];
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n_pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
   switch (w.group) {
-    case 1: return launch_decode<1>(p, w.n_items, s);
-    case 2: return launch_decode<2>(p, w.n_items, s);
-    case 3: return launch_decode<3>(p, w.n_items, s);
-    case 4: return launch_decode<4>(p, w.n_items, s);
-    case 5: return launch_decode<5>(p, w.n_items, s);
-    case 6: return launch_decode<6>(p, w.n_items, s);
-    case 7: return launch_decode<7>(p, w.n_items, s);
-    case 8: return launch_decode<8>(p, w.n_items, s);
+    case 1: return launch_decode<1>(p, w.n_items, n_pairs, s);
+    case 2: return launch_decode<2>(p, w.n_items, n_pairs, s);
+    case 3: return launch_decode<3>(p, w.n_items, n_pairs, s);
+    case 4: return launch_decode<4>(p, w.n_items, n_pairs, s);
+    case 5: return launch_decode<5>(p, w.n_items, n_pairs, s);
+    case 6: return launch_decode<6>(p, w.n_items, n_pairs, s);
+    case 7: return launch_decode<7>(p, w.n_items, n_pairs, s);
+    case 8: return launch_decode<8>(p, w.n_items, n_pairs, s);
     default: return LEANK_EUNSUPPORTED;
   }
 }

@@ -107,8 +107,7 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, WorkPlan* w) {
   w->partial_stride = w->group * LEANK_HEAD_DIM + ((2 * w->group + 3) / 4) * 4;
   const int64_t bound_items = bound_per_b * c->batch;
   w->partial_bytes = static_cast<size_t>(bound_items) * w->partial_stride * sizeof(float);
-  w->counter_offset = (w->partial_bytes + 255) / 256 * 256;
-  w->workspace_bytes = (w->counter_offset + pairs * sizeof(uint32_t) + 255) / 256 * 256;
+  w->workspace_bytes = std::max<size_t>(256, (w->partial_bytes + 255) / 256 * 256);
   return LEANK_OK;
 }
 

@@ -183,10 +183,10 @@ int leank_workspace_bytes(const leank_layer_cache* cache, int64_t ctx_len,
                           size_t* bytes_out);
 
 /*
- * leank_workspace_init -- zero a workspace before its first use.  A
- * workspace allocated zero-filled (e.g. torch.zeros) needs no init.  Every
- * leank_decode_attn call that completes leaves the workspace ready for the
- * next.  Asynchronous on `stream` (a fill kernel, no memset node).
+ * leank_workspace_init -- zero-fill a workspace (optional: leank_decode_attn
+ * writes every workspace byte it later reads, so a fresh workspace needs
+ * no preparation).  Asynchronous on `stream` (a fill kernel, no memset
+ * node).  workspace_bytes must be a multiple of 4.
  */
 int leank_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
@@ -208,10 +208,11 @@ int leank_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *   middle tokens of a fully pruned head take no part;
  *   out_j = sum_t softmax(score)_t V[t].
  * bf16 inputs, float32 accumulation.  The context is split into work items
- * whose partial (max, sum, weighted V) results are merged by the last item
- * of each (batch row, KV head) in a fixed order, so the output does not
- * depend on scheduling.  One kernel launch, asynchronous on `stream`.
- * Calls that share a workspace must not overlap in time.
+ * whose partial (max, sum, weighted V) records go to the workspace; a second
+ * kernel merges each (batch row, KV head) pair's records in a fixed order,
+ * so the output does not depend on scheduling.  Two kernel launches,
+ * asynchronous on `stream`.  Calls that share a workspace must not overlap
+ * in time.
  */
 int leank_decode_attn(const leank_layer_cache* cache, const void* q,
                       int64_t ctx_len, float scale, float* out,
