@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libleank.so")
-SOURCES = ["plan.hip", "mask.hip", "pack.hip", "decode.hip"]
+SOURCES = ["plan.hip", "mask.hip", "pack.hip", "decode.hip"] + [f"decode_g{g}.hip" for g in range(1, 9)]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms (v_pk_fma_f32 and friends) are switched off for the
@@ -54,7 +54,7 @@ def build(verbose=False, extra_flags=()):
         objects.append(obj)
         jobs.append([hipcc, *COMMON_FLAGS, *DEVICE_FLAGS, *extra_flags, "-c",
                      os.path.join(CSRC, src), "-o", obj])
-    workers = min(len(jobs), max(1, (os.cpu_count() or 2) // 2))
+    workers = min(len(jobs), max(1, os.cpu_count() or 2))
     with concurrent.futures.ThreadPoolExecutor(workers) as pool:
         for fut in [pool.submit(_run, cmd, verbose) for cmd in jobs]:
             fut.result()

@@ -1,442 +1,27 @@
-// leank_decode_attn: single-token decode attention over the channel-pruned
-// cache (LeanK page, section 3.1 item 3 and section 3.2; GQA as in section
-// 5.2.3 of the KV-pruning white paper; scale as in FastGen page 5.3).
-//
-// Work items.  Each (batch row b, KV head h) pair is split into items over
-// its full-width rows (K_sl/V_sl, 128 channels) and, for a live head, over
-// its middle rows (K_prun with the head's kept channels, V_mid).  One
-// 256-thread workgroup runs one item; its 4 wavefronts take the item's row
-// tiles round-robin.  All G query heads of the group share every K and V
-// load.
-//
-// Lane layout inside a wavefront (4 rows of 16 lanes):
-//   V: lane (r, i) loads 16 bytes (channels 8i..8i+7) of token row 4j + r
-//      for V-load j, so a V-load moves 4 whole 256-byte rows.
-//   K: a K row of C = 8R channels is loaded by R lanes, 16 bytes each; a
-//      K-load moves 64/R rows (1 KB).  Lane (r, i) takes chunk i % R of row
-//      4 * (i / R) + r of the load, so the K row that V-load j needs sits in
-//      the same 16-lane row r as that V row.
-// Scores: bf16 dot2 products of the lane's 8 channels, summed over the R
-// lanes of the K row with DPP (quad_perm, half-mirror, mirror), scaled by
-// scale*log2(e).  Softmax runs in base 2 with one running max per
-// wavefront; the exp2 of each score is computed once in the K layout and
-// broadcast to the 16 lanes of its V row with DPP row_newbcast.
-//
-// Merge.  The 4 rows of a wavefront share the running max, so their sums
-// and V accumulators add directly (permlane16/32 swaps).  The 4 wavefronts
-// merge through LDS into one (max, sum, acc[G][128]) record per item.  A
-// second kernel merges each (b, h) pair's records in item order and writes
-// the output, so the result does not depend on scheduling and no workgroup
-// waits on another.
+// Host entry points of the decode path: leank_decode_attn (argument checks,
+// work plan, dispatch on the group size) and leank_workspace_init.  The
+// kernels live in decode_kernels.h, instantiated per group size in
+// decode_g1.hip .. decode_g8.hip.
 
-#include <math.h>
-
-#include "common.h"
+#include "decode_kernels.h"
 
 namespace leank {
+
+extern template int launch_decode<1>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+extern template int launch_decode<2>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+extern template int launch_decode<3>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+extern template int launch_decode<4>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+extern template int launch_decode<5>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+extern template int launch_decode<6>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+extern template int launch_decode<7>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+extern template int launch_decode<8>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-constexpr float kLog2e = 1.4426950408889634f;
-
-struct DecodeHead {
-  int64_t k_off;   // elements of K_prun, -1 for a dead head
-  int64_t v_off;   // elements of V_mid, -1 for a dead head
-  int32_t kept;
-  int32_t n_mid;     // middle items of this head per batch row
-  int32_t mid_rows;  // rows per middle item
-  int32_t base;      // first item of this head within a batch row
-};
-
-struct DecodeParams {
-  const uint16_t* q;
-  const uint16_t* k_sl;
-  const uint16_t* v_sl;
-  const uint16_t* k_prun;
-  const uint16_t* v_mid;
-  const int16_t* kept_idx;
-  float* out;
-  float* partials;
-  int64_t mid_cap;
-  int32_t n_kv;
-  int32_t n_q;
-  int32_t slots;
-  int32_t t_sl;
-  int32_t t_mid;
-  int32_t n_sl_items;
-  int32_t sl_rows;
-  int32_t items_per_b;
-  int32_t partial_stride;
-  float qk_scale;  // softmax scale * log2(e)
-  DecodeHead heads[LEANK_MAX_KV_HEADS];
-};
-
-template <int G>
-struct Running {
-  float m[G];       // running max (base-2 units), uniform over the wavefront
-  float l[G];       // running sum of exp2 weights over this lane's V rows
-  float acc[G][8];  // running weighted V for this lane's 8 channels
-};
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// x + x of the row at lane distance 16 / 32, as a VALU swap (no LDS).
-__device__ __forceinline__ float add_xor16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float add_xor32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float max_xor16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-template <int G, int R>
-struct TileShape {
-  static constexpr int kRowsPerKLoad = 64 / R;
-  static constexpr int kWant = G > 4 ? (R == 16 ? 16 : 32) : (R >= 8 ? 32 : 64);
-  static constexpr int kRows = kWant > kRowsPerKLoad ? kWant : kRowsPerKLoad;
-  static constexpr int kVLoads = kRows / 4;
-  static constexpr int kKLoads = kRows / kRowsPerKLoad;
-  static constexpr int kRowsPerGroup = 16 / R;  // K rows per 16-lane row per K-load
-};
-
-// One tile of kRows rows starting at row t0 of the stream (rows >= nvalid
-// are outside the item when kTail).  kb/vb point at row 0 of the K and V
-// streams; kstride is the K row length in elements (= 8R unless kGeneric,
-// where R = 16 and only lanes with k_active hold K data).
-template <int G, int R, bool kTail, bool kGeneric>
-__device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ kb,
-                                            const uint16_t* __restrict__ vb, int kstride, int t0,
-                                            int nvalid, bool k_active, const uint32_t (&qw)[G][4],
-                                            float qk_scale, Running<G>& st) {
-  using S = TileShape<G, R>;
-  const int lane = threadIdx.x & 63;
-  const int row16 = lane >> 4;
-  const int i = lane & 15;
-  const int grp = i / R;
-  const int chunk = i % R;
-
-  const uint16_t* kt = kb + static_cast<int64_t>(t0) * kstride;
-  const uint16_t* vt = vb + static_cast<int64_t>(t0) * LEANK_HEAD_DIM;
-  uint4 kv[S::kKLoads];
-  uint4 vv[S::kVLoads];
-  static_for<S::kKLoads>([&](auto KK) {
-    constexpr int kk = decltype(KK)::value;
-    const int row = kk * S::kRowsPerKLoad + 4 * grp + row16;
-    const bool ok = (!kTail || row < nvalid) && (!kGeneric || k_active);
-    kv[kk] = ok ? *reinterpret_cast<const uint4*>(kt + row * kstride + chunk * 8)
-                : make_uint4(0u, 0u, 0u, 0u);
-  });
-  static_for<S::kVLoads>([&](auto JJ) {
-    constexpr int jj = decltype(JJ)::value;
-    const int row = 4 * jj + row16;
-    const bool ok = !kTail || row < nvalid;
-    vv[jj] = ok ? *reinterpret_cast<const uint4*>(vt + row * LEANK_HEAD_DIM + i * 8)
-                : make_uint4(0u, 0u, 0u, 0u);
-  });
-
-  // scores (base-2 logits) of the K rows this lane's group holds
-  float s[S::kKLoads][G];
-  static_for<S::kKLoads>([&](auto KK) {
-    constexpr int kk = decltype(KK)::value;
-    const int row = kk * S::kRowsPerKLoad + 4 * grp + row16;
-    static_for<G>([&](auto GG) {
-      constexpr int g = decltype(GG)::value;
-      float a = dot2_bf16(qw[g][0], kv[kk].x, 0.0f);
-      a = dot2_bf16(qw[g][1], kv[kk].y, a);
-      a = dot2_bf16(qw[g][2], kv[kk].z, a);
-      a = dot2_bf16(qw[g][3], kv[kk].w, a);
-      if constexpr (R >= 2) a += dpp_f32<kDppQuadXor1>(a);
-      if constexpr (R >= 4) a += dpp_f32<kDppQuadXor2>(a);
-      if constexpr (R >= 8) a += dpp_f32<kDppHalfMirror>(a);
-      if constexpr (R >= 16) a += dpp_f32<kDppRowMirror>(a);
-      a *= qk_scale;
-      if (kTail && row >= nvalid) a = -INFINITY;
-      s[kk][g] = a;
-    });
-  });
-
-  // running max over the wavefront, rescale, exp2 in the K layout
-  static_for<G>([&](auto GG) {
-    constexpr int g = decltype(GG)::value;
-    float mx = s[0][g];
-    static_for<S::kKLoads>([&](auto KK) {
-      constexpr int kk = decltype(KK)::value;
-      if constexpr (kk > 0) mx = fmaxf(mx, s[kk][g]);
-    });
-    if constexpr (R < 2) mx = fmaxf(mx, dpp_f32<kDppQuadXor1>(mx));
-    if constexpr (R < 4) mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
-    if constexpr (R < 8) mx = fmaxf(mx, dpp_f32<kDppHalfMirror>(mx));
-    if constexpr (R < 16) mx = fmaxf(mx, dpp_f32<kDppRowMirror>(mx));
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
-    const float m_new = fmaxf(st.m[g], mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float corr = fast_exp2(st.m[g] - m_use);
-    st.m[g] = m_new;
-    st.l[g] *= corr;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) st.acc[g][c] *= corr;
-    static_for<S::kKLoads>([&](auto KK) {
-      constexpr int kk = decltype(KK)::value;
-      s[kk][g] = fast_exp2(s[kk][g] - m_use);
-    });
-  });
-
-  // weighted V: V-load jj holds row 4jj + row16, whose weight sits in K-load
-  // jj / kRowsPerGroup, lane group jj % kRowsPerGroup of the same 16-lane row
-  static_for<S::kVLoads>([&](auto JJ) {
-    constexpr int jj = decltype(JJ)::value;
-    constexpr int kk = jj / S::kRowsPerGroup;
-    constexpr int src_lane = R * (jj % S::kRowsPerGroup);
-    float v[8];
-    v[0] = bf16_lo(vv[jj].x);
-    v[1] = bf16_hi(vv[jj].x);
-    v[2] = bf16_lo(vv[jj].y);
-    v[3] = bf16_hi(vv[jj].y);
-    v[4] = bf16_lo(vv[jj].z);
-    v[5] = bf16_hi(vv[jj].z);
-    v[6] = bf16_lo(vv[jj].w);
-    v[7] = bf16_hi(vv[jj].w);
-    static_for<G>([&](auto GG) {
-      constexpr int g = decltype(GG)::value;
-      float p;
-      if constexpr (S::kRowsPerGroup == 1) {
-        p = s[kk][g];
-      } else {
-        p = dpp_f32<kDppRowNewBcast + src_lane>(s[kk][g]);
-      }
-      st.l[g] += p;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) st.acc[g][c] = fmaf(p, v[c], st.acc[g][c]);
-    });
-  });
-}
-
-template <int G, int R, bool kGeneric>
-__device__ __forceinline__ void attend_range(const uint16_t* kb, const uint16_t* vb, int kstride,
-                                             int r0, int r1, bool k_active,
-                                             const uint32_t (&qw)[G][4], float qk_scale,
-                                             Running<G>& st) {
-  constexpr int kRows = TileShape<G, R>::kRows;
-  const int wave = threadIdx.x >> 6;
-  for (int t0 = r0 + wave * kRows; t0 < r1; t0 += kWaves * kRows) {
-    const int nvalid = r1 - t0;
-    if (nvalid >= kRows) {
-      attend_tile<G, R, false, kGeneric>(kb, vb, kstride, t0, kRows, k_active, qw, qk_scale, st);
-    } else {
-      attend_tile<G, R, true, kGeneric>(kb, vb, kstride, t0, nvalid, k_active, qw, qk_scale, st);
-    }
-  }
-}
-
-// q channels of the lane's K chunk for the G query heads, packed bf16 pairs.
-template <int G>
-__device__ __forceinline__ void load_q_dense(const uint16_t* qh, int chunk, uint32_t (&qw)[G][4]) {
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4 w = *reinterpret_cast<const uint4*>(qh + g * LEANK_HEAD_DIM + chunk * 8);
-    qw[g][0] = w.x;
-    qw[g][1] = w.y;
-    qw[g][2] = w.z;
-    qw[g][3] = w.w;
-  }
-}
-
-template <int G>
-__device__ __forceinline__ void load_q_gather(const uint16_t* qh, const int16_t* idx, int chunk,
-                                              bool active, uint32_t (&qw)[G][4]) {
-  int ch[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) ch[k] = active ? (idx[chunk * 8 + k] & (LEANK_HEAD_DIM - 1)) : 0;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = active ? qh[g * LEANK_HEAD_DIM + ch[2 * k]] : 0u;
-      const uint32_t hi = active ? qh[g * LEANK_HEAD_DIM + ch[2 * k + 1]] : 0u;
-      qw[g][k] = lo | (hi << 16);
-    }
-  }
-}
-
-template <int G>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeParams p) {
-  __shared__ float s_acc[kWaves][G][LEANK_HEAD_DIM];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-
-  const int item = blockIdx.x;
-  const int b = item / p.items_per_b;
-  const int r = item - b * p.items_per_b;
-  int h = 0;
-  while (h + 1 < p.n_kv && r >= p.heads[h + 1].base) ++h;
-  const DecodeHead hd = p.heads[h];
-  const int local = r - hd.base;
-  const bool middle = local >= p.n_sl_items;
-
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15;
-  const uint16_t* qh = p.q + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM;
-
-  Running<G> st;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    st.m[g] = -INFINITY;
-    st.l[g] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) st.acc[g][c] = 0.0f;
-  }
-  uint32_t qw[G][4];
-
-  if (!middle) {
-    const int r0 = local * p.sl_rows;
-    const int r1 = min(p.t_sl, r0 + p.sl_rows);
-    const int64_t pair = static_cast<int64_t>(b) * p.n_kv + h;
-    const uint16_t* kb = p.k_sl + pair * p.slots * LEANK_HEAD_DIM;
-    const uint16_t* vb = p.v_sl + pair * p.slots * LEANK_HEAD_DIM;
-    load_q_dense<G>(qh, i, qw);
-    attend_range<G, 16, false>(kb, vb, LEANK_HEAD_DIM, r0, r1, true, qw, p.qk_scale, st);
-  } else {
-    const int chunk_id = local - p.n_sl_items;
-    const int r0 = chunk_id * hd.mid_rows;
-    const int r1 = min(p.t_mid, r0 + hd.mid_rows);
-    const int kept = hd.kept;
-    const int64_t brow = static_cast<int64_t>(b) * p.mid_cap;
-    const uint16_t* kb = p.k_prun + hd.k_off + brow * kept;
-    const uint16_t* vb = p.v_mid + hd.v_off + brow * LEANK_HEAD_DIM;
-    const int16_t* idx = p.kept_idx + h * LEANK_HEAD_DIM;
-    switch (kept) {
-      case 8:
-        load_q_gather<G>(qh, idx, i % 1, true, qw);
-        attend_range<G, 1, false>(kb, vb, 8, r0, r1, true, qw, p.qk_scale, st);
-        break;
-      case 16:
-        load_q_gather<G>(qh, idx, i % 2, true, qw);
-        attend_range<G, 2, false>(kb, vb, 16, r0, r1, true, qw, p.qk_scale, st);
-        break;
-      case 32:
-        load_q_gather<G>(qh, idx, i % 4, true, qw);
-        attend_range<G, 4, false>(kb, vb, 32, r0, r1, true, qw, p.qk_scale, st);
-        break;
-      case 64:
-        load_q_gather<G>(qh, idx, i % 8, true, qw);
-        attend_range<G, 8, false>(kb, vb, 64, r0, r1, true, qw, p.qk_scale, st);
-        break;
-      case 128:
-        load_q_gather<G>(qh, idx, i, true, qw);
-        attend_range<G, 16, false>(kb, vb, 128, r0, r1, true, qw, p.qk_scale, st);
-        break;
-      default: {
-        const bool active = i < kept / 8;
-        load_q_gather<G>(qh, idx, i, active, qw);
-        attend_range<G, 16, true>(kb, vb, kept, r0, r1, active, qw, p.qk_scale, st);
-        break;
-      }
-    }
-  }
-
-  // the 4 rows of the wavefront share st.m: add their sums and accumulators
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    st.l[g] = add_xor32(add_xor16(st.l[g]));
-#pragma unroll
-    for (int c = 0; c < 8; ++c) st.acc[g][c] = add_xor32(add_xor16(st.acc[g][c]));
-  }
-  const int wave = threadIdx.x >> 6;
-  if (lane < 16) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) s_acc[wave][g][lane * 8 + c] = st.acc[g][c];
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      s_m[wave][g] = st.m[g];
-      s_l[wave][g] = st.l[g];
-    }
-  }
-  __syncthreads();
-
-  // one record per item: (acc[G][128], m[G], l[G]) merged over the wavefronts
-  float* rec = p.partials + static_cast<int64_t>(item) * p.partial_stride;
-  for (int t = threadIdx.x; t < G * LEANK_HEAD_DIM; t += kThreads) {
-    const int g = t / LEANK_HEAD_DIM;
-    const int ch = t - g * LEANK_HEAD_DIM;
-    float m = s_m[0][g];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_m[w][g]);
-    const float m_use = m == -INFINITY ? 0.0f : m;
-    float a = 0.0f, l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(s_m[w][g] - m_use);
-      a = fmaf(s_acc[w][g][ch], f, a);
-      l = fmaf(s_l[w][g], f, l);
-    }
-    rec[t] = a;
-    if (ch == 0) {
-      rec[G * LEANK_HEAD_DIM + g] = m;
-      rec[G * LEANK_HEAD_DIM + G + g] = l;
-    }
-  }
-}
-
-// Merges the records of one (batch row, KV head) pair in item order and
-// writes the G query heads' outputs.  One workgroup per pair.
-template <int G>
-__global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodeParams p) {
-  const int64_t pair = blockIdx.x;
-  const int b = static_cast<int>(pair / p.n_kv);
-  const int h = static_cast<int>(pair - static_cast<int64_t>(b) * p.n_kv);
-  const DecodeHead hd = p.heads[h];
-  const int n_items = p.n_sl_items + hd.n_mid;
-  const float* first =
-      p.partials + (static_cast<int64_t>(b) * p.items_per_b + hd.base) * p.partial_stride;
-  float* out = p.out + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM;
-  for (int t = threadIdx.x; t < G * LEANK_HEAD_DIM; t += kThreads) {
-    const int g = t / LEANK_HEAD_DIM;
-    float m = -INFINITY;
-    for (int n = 0; n < n_items; ++n)
-      m = fmaxf(m, first[n * p.partial_stride + G * LEANK_HEAD_DIM + g]);
-    const float m_use = m == -INFINITY ? 0.0f : m;
-    float a = 0.0f, l = 0.0f;
-    for (int n = 0; n < n_items; ++n) {
-      const float* rn = first + n * p.partial_stride;
-      const float f = fast_exp2(rn[G * LEANK_HEAD_DIM + g] - m_use);
-      a = fmaf(rn[t], f, a);
-      l = fmaf(rn[G * LEANK_HEAD_DIM + G + g], f, l);
-    }
-    out[t] = a / l;
-  }
-}
 
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n_words) {
   for (int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; k < n_words;
        k += static_cast<int64_t>(gridDim.x) * blockDim.x)
     p[k] = 0u;
-}
-
-template <int G>
-int launch_decode(const DecodeParams& p, int64_t n_items, int64_t n_pairs, hipStream_t s) {
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(static_cast<unsigned>(n_items)), dim3(kThreads),
-                     0, s, p);
-  LEANK_HIP_TRY(hipGetLastError());
-  hipLaunchKernelGGL(decode_combine_kernel<G>, dim3(static_cast<unsigned>(n_pairs)),
-                     dim3(kThreads), 0, s, p);
-  LEANK_HIP_TRY(hipGetLastError());
-  return LEANK_OK;
 }
 
 }  // namespace
@@ -490,6 +75,10 @@ extern "C" int leank_decode_attn(const leank_layer_cache* c, const void* q, int6
   p.sl_rows = w.sl_rows;
   p.items_per_b = w.items_per_b;
   p.partial_stride = w.partial_stride;
+  // pairs with many items get their channels split over several combine workgroups
+  int32_t max_items = 0;
+  for (int h = 0; h < c->n_kv_heads; ++h) max_items = std::max(max_items, w.n_sl_items + w.n_mid[h]);
+  p.combine_slices = max_items > 256 ? 8 : max_items > 64 ? 4 : max_items > 16 ? 2 : 1;
   p.qk_scale = scale * kLog2e;
   for (int h = 0; h < c->n_kv_heads; ++h) {
     p.heads[h].k_off = c->k_prun_off[h];

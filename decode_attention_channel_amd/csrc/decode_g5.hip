@@ -1,0 +1,5 @@
+// Decode kernels instantiated for 5 query heads per KV head (one
+// translation unit per group size keeps builds parallel).
+#include "decode_kernels.h"
+
+template int leank::launch_decode<5>(const leank::DecodeParams&, int64_t, int64_t, hipStream_t);

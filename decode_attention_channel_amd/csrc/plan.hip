@@ -12,10 +12,23 @@ namespace leank {
 
 namespace {
 
-constexpr int64_t kRowQuantum = 64;        // item row counts are multiples of this
-constexpr int64_t kItemBytesWide = 160 << 10;  // target bytes per item, many (b, h) pairs
-constexpr int64_t kItemBytesNarrow = 64 << 10; // target bytes per item, few pairs
-constexpr int64_t kFewPairs = 64;
+// Work-item sizing (compile-time tuning knobs; defaults measured on MI355X).
+// Items are sized so that one decode call makes about kTargetCUs *
+// LEANK_ITEMS_PER_CU of them, within [LEANK_ITEM_KB_MIN, LEANK_ITEM_KB_MAX].
+#ifndef LEANK_ITEMS_PER_CU
+#define LEANK_ITEMS_PER_CU 8
+#endif
+#ifndef LEANK_ITEM_KB_MIN
+#define LEANK_ITEM_KB_MIN 64
+#endif
+#ifndef LEANK_ITEM_KB_MAX
+#define LEANK_ITEM_KB_MAX 1024
+#endif
+
+constexpr int64_t kTargetCUs = 256;  // compute units of an MI355X
+constexpr int64_t kRowQuantum = 64;  // item row counts are multiples of this
+constexpr int64_t kItemBytesMin = int64_t{LEANK_ITEM_KB_MIN} << 10;
+constexpr int64_t kItemBytesMax = int64_t{LEANK_ITEM_KB_MAX} << 10;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -83,23 +96,33 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, WorkPlan* w) {
   w->group = c->n_q_heads / c->n_kv_heads;
   w->t_sl = static_cast<int32_t>(std::min<int64_t>(ctx_len, slots));
   w->t_mid = static_cast<int32_t>(std::max<int64_t>(0, ctx_len - slots));
-  const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
-  const int64_t target = pairs >= kFewPairs ? kItemBytesWide : kItemBytesNarrow;
+  // bytes the call streams (K and V rows of both regions)
+  int64_t stream_bytes = static_cast<int64_t>(c->batch) * c->n_kv_heads * w->t_sl * 4 * LEANK_HEAD_DIM;
+  for (int h = 0; h < c->n_kv_heads; ++h)
+    if (c->kept_count[h] > 0)
+      stream_bytes += static_cast<int64_t>(c->batch) * w->t_mid * (2 * c->kept_count[h] + 2 * LEANK_HEAD_DIM);
+  const int64_t target = std::min(kItemBytesMax, std::max(kItemBytesMin,
+                                  stream_bytes / (kTargetCUs * LEANK_ITEMS_PER_CU)));
 
-  int64_t bound_per_b = 0, b;
-  split_rows(w->t_sl, row_target(2 * LEANK_HEAD_DIM * 2, target), &w->n_sl_items, &w->sl_rows, &b);
+  // item counts at the smallest item size bound the workspace for any ctx <= this one
+  int64_t bound_per_b = 0, b, unused_n, unused_rows;
+  int32_t n32, rows32;
+  split_rows(w->t_sl, row_target(4 * LEANK_HEAD_DIM, kItemBytesMin), &n32, &rows32, &b);
   bound_per_b += b * c->n_kv_heads;
+  split_rows(w->t_sl, row_target(4 * LEANK_HEAD_DIM, target), &w->n_sl_items, &w->sl_rows, &unused_n);
   int32_t base = 0;
   for (int h = 0; h < c->n_kv_heads; ++h) {
     w->head_base[h] = base;
     const int kept = c->kept_count[h];
     if (kept > 0) {
-      split_rows(w->t_mid, row_target(2 * kept + 2 * LEANK_HEAD_DIM, target), &w->n_mid[h],
-                 &w->mid_rows[h], &b);
+      const int64_t row_bytes = 2 * kept + 2 * LEANK_HEAD_DIM;
+      split_rows(w->t_mid, row_target(row_bytes, kItemBytesMin), &n32, &rows32, &b);
       bound_per_b += b;
+      split_rows(w->t_mid, row_target(row_bytes, target), &w->n_mid[h], &w->mid_rows[h], &unused_n);
     }
     base += w->n_sl_items + w->n_mid[h];
   }
+  (void)unused_rows;
   w->head_base[c->n_kv_heads] = base;
   w->items_per_b = base;
   w->n_items = static_cast<int64_t>(base) * c->batch;
