@@ -90,11 +90,16 @@ struct DecodeParams {
   DecodeHead heads[LEANK_MAX_KV_HEADS];
 };
 
+// The running max only moves when a tile's max exceeds it by more than this
+// (base-2 units), so weights stay <= 2^kRescaleSlack and most tiles skip
+// the rescale; the softmax is unchanged because the reference cancels.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int G>
 struct Running {
-  float m[G];       // running max (base-2 units), uniform over the wavefront
-  float l[G];       // running sum of exp2 weights over this lane's V rows
-  float acc[G][8];  // running weighted V for this lane's 8 channels
+  float m[G];       // reference max (base-2 units), uniform over the wavefront
+  float l[G];       // sum of exp2 weights of this lane's K rows (K layout)
+  float acc[G][8];  // weighted V for this lane's 8 channels (V layout)
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -194,7 +199,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ kb,
     });
   });
 
-  // running max over the wavefront, rescale, exp2 in the K layout
+  // running max over the wavefront, lazy rescale, exp2 in the K layout
   static_for<G>([&](auto GG) {
     constexpr int g = decltype(GG)::value;
     float mx = s[0][g];
@@ -206,18 +211,20 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ kb,
     if constexpr (R < 4) mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
     if constexpr (R < 8) mx = fmaxf(mx, dpp_f32<kDppHalfMirror>(mx));
     if constexpr (R < 16) mx = fmaxf(mx, dpp_f32<kDppRowMirror>(mx));
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
-    const float m_new = fmaxf(st.m[g], mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float corr = fast_exp2(st.m[g] - m_use);
-    st.m[g] = m_new;
-    st.l[g] *= corr;
+    mx = max_xor32(max_xor16(mx));
+    mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));
+    if (mx > st.m[g] + kRescaleSlack) {  // uniform over the wavefront
+      const float corr = st.m[g] == -INFINITY ? 0.0f : fast_exp2(st.m[g] - mx);
+      st.m[g] = mx;
+      st.l[g] *= corr;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) st.acc[g][c] *= corr;
+      for (int c = 0; c < 8; ++c) st.acc[g][c] *= corr;
+    }
+    const float m_use = st.m[g] == -INFINITY ? 0.0f : st.m[g];
     static_for<S::kKLoads>([&](auto KK) {
       constexpr int kk = decltype(KK)::value;
       s[kk][g] = fast_exp2(s[kk][g] - m_use);
+      st.l[g] += s[kk][g];
     });
   });
 
@@ -244,7 +251,6 @@ __device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ kb,
       } else {
         p = dpp_f32<kDppRowNewBcast + src_lane>(s[kk][g]);
       }
-      st.l[g] += p;
 #pragma unroll
       for (int c = 0; c < 8; ++c) st.acc[g][c] = fmaf(p, v[c], st.acc[g][c]);
     });
@@ -265,6 +271,15 @@ __device__ __forceinline__ void attend_range(const uint16_t* kb, const uint16_t*
     } else {
       attend_tile<G, R, true, kGeneric>(kb, vb, kstride, t0, nvalid, k_active, qw, qk_scale, st);
     }
+  }
+  // each lane group of R lanes summed the weights of its own K rows: add the
+  // groups of the 16-lane row so that l covers the row's V rows like acc
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if constexpr (R < 2) st.l[g] += dpp_f32<kDppQuadXor1>(st.l[g]);
+    if constexpr (R < 4) st.l[g] += dpp_f32<kDppQuadXor2>(st.l[g]);
+    if constexpr (R < 8) st.l[g] += dpp_f32<kDppHalfMirror>(st.l[g]);
+    if constexpr (R < 16) st.l[g] += dpp_f32<kDppRowMirror>(st.l[g]);
   }
 }
 

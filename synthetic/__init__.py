@@ -42,5 +42,7 @@ from .generate import (  # noqa: F401
     make_q,
     make_kv,
     make_step_kv,
+    make_steps_kv,
+    make_steps_q,
     seed_for,
 )

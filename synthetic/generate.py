@@ -3,7 +3,7 @@
 import numpy as np
 import torch
 
-KIND_Q, KIND_K, KIND_V, KIND_KSCALE = 1, 2, 3, 4
+KIND_Q, KIND_K, KIND_V, KIND_KSCALE, KIND_STEPS_K, KIND_STEPS_V, KIND_STEPS_Q = 1, 2, 3, 4, 5, 6, 7
 
 
 def seed_for(cfg_index, layer, kind, step=0):
@@ -79,6 +79,26 @@ def make_step_kv(cfg, layer, step, device="cpu", batch=None):
         k.mul_(scales[None, :, None, :])
     v = _normal(shape, seed_for(cfg.index, layer, KIND_V, step + 1), device)
     return k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def make_steps_kv(cfg, layer, n_steps, device="cpu", batch=None):
+    """K, V bf16 [n_steps, B, H_kv, 1, d] of the tokens appended by a generation loop."""
+    b = cfg.batch if batch is None else batch
+    shape = (n_steps, b, cfg.n_kv_heads, 1, cfg.head_dim)
+    k = _normal(shape, seed_for(cfg.index, layer, KIND_STEPS_K), device)
+    scales = _k_scales(cfg, layer, device)
+    if scales is not None:
+        k.mul_(scales[None, None, :, None, :])
+    v = _normal(shape, seed_for(cfg.index, layer, KIND_STEPS_V), device)
+    return k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+def make_steps_q(cfg, step, device="cpu", batch=None):
+    """q bf16 [L, B, Hq, d] for every layer at one generation step."""
+    b = cfg.batch if batch is None else batch
+    x = _normal((cfg.n_layers, b, cfg.n_q_heads, cfg.head_dim),
+                seed_for(cfg.index, 0, KIND_STEPS_Q, step), device)
+    return x.to(torch.bfloat16)
 
 
 def bf16_bits(t):

@@ -58,27 +58,25 @@ def random_bf16(shape, gen, scale=1.0, device="cuda"):
     return (x * scale).to(torch.bfloat16)
 
 
-def read_cache(cache):
-    """Host uint16 views of the cache buffers, split per head as the plan lays them out."""
+def read_pair(cache, b, h, n_mid=None):
+    """Host uint16 copies of one (batch row, KV head) pair's cache rows:
+    ring K/V [slots, 128], K_prun [n_mid, kept] and V_mid [n_mid, 128] (None
+    for a fully pruned head).  Slices on the GPU before copying."""
     d = cache.desc
-    batch, n_kv = d.batch, d.n_kv_heads
     slots = d.n_sink + d.window
     mid_cap = d.mid_capacity
-    k_sl = bf16_bits(cache.k_sl)[: batch * n_kv * slots * 128].reshape(batch, n_kv, slots, 128)
-    v_sl = bf16_bits(cache.v_sl)[: batch * n_kv * slots * 128].reshape(batch, n_kv, slots, 128)
-    k_prun_all = bf16_bits(cache.k_prun)
-    v_mid_all = bf16_bits(cache.v_mid)
-    k_prun, v_mid = [], []
-    for h in range(n_kv):
-        c = d.kept_count[h]
-        if c == 0:
-            k_prun.append(None)
-            v_mid.append(None)
-            continue
-        ko, vo = d.k_prun_off[h], d.v_mid_off[h]
-        k_prun.append(k_prun_all[ko: ko + batch * mid_cap * c].reshape(batch, mid_cap, c))
-        v_mid.append(v_mid_all[vo: vo + batch * mid_cap * 128].reshape(batch, mid_cap, 128))
-    return {"k_sl": k_sl, "v_sl": v_sl, "k_prun": k_prun, "v_mid": v_mid}
+    n_mid = mid_cap if n_mid is None else n_mid
+    base = ((b * d.n_kv_heads) + h) * slots * 128
+    ring_k = bf16_bits(cache.k_sl[base: base + slots * 128]).reshape(slots, 128)
+    ring_v = bf16_bits(cache.v_sl[base: base + slots * 128]).reshape(slots, 128)
+    c = d.kept_count[h]
+    if c == 0:
+        return ring_k, ring_v, None, None
+    ko = d.k_prun_off[h] + b * mid_cap * c
+    vo = d.v_mid_off[h] + b * mid_cap * 128
+    k_prun = bf16_bits(cache.k_prun[ko: ko + n_mid * c]).reshape(n_mid, c)
+    v_mid = bf16_bits(cache.v_mid[vo: vo + n_mid * 128]).reshape(n_mid, 128)
+    return ring_k, ring_v, k_prun, v_mid
 
 
 def assert_cache_matches(cache, k_bits, v_bits, mask, pairs=None):
@@ -87,7 +85,6 @@ def assert_cache_matches(cache, k_bits, v_bits, mask, pairs=None):
     then k_bits/v_bits hold just those rows, in the order of `pairs`)."""
     d = cache.desc
     kept_count, kept_idx = kept_from_mask(mask)
-    got = read_cache(cache)
     if pairs is None:
         pairs = [(b, h) for b in range(d.batch) for h in range(d.n_kv_heads)]
         rows = {(b, h): (b, h) for b, h in pairs}
@@ -99,17 +96,18 @@ def assert_cache_matches(cache, k_bits, v_bits, mask, pairs=None):
         one_v = v_bits[rb:rb + 1, rh:rh + 1]
         ref = oracle.pack_reference(one_k, one_v, kept_count[h:h + 1], kept_idx[h:h + 1],
                                     d.n_sink, d.window)
+        n_mid = ref["k_prun"][0].shape[1]
+        ring_k, ring_v, k_prun, v_mid = read_pair(cache, b, h, n_mid)
         for slot, pos in enumerate(ref["slot_pos"]):
             if pos < 0:
                 continue
-            assert np.array_equal(got["k_sl"][b, h, slot], ref["ring_k"][0, 0, slot]), (b, h, slot, pos)
-            assert np.array_equal(got["v_sl"][b, h, slot], ref["ring_v"][0, 0, slot]), (b, h, slot, pos)
-        n_mid = ref["k_prun"][0].shape[1]
+            assert np.array_equal(ring_k[slot], ref["ring_k"][0, 0, slot]), (b, h, slot, pos)
+            assert np.array_equal(ring_v[slot], ref["ring_v"][0, 0, slot]), (b, h, slot, pos)
         if kept_count[h] == 0:
-            assert got["k_prun"][h] is None and ref["v_mid"][0] is None
+            assert k_prun is None and ref["v_mid"][0] is None
             continue
-        assert np.array_equal(got["k_prun"][h][b, :n_mid], ref["k_prun"][0][0]), (b, h)
-        assert np.array_equal(got["v_mid"][h][b, :n_mid], ref["v_mid"][0][0]), (b, h)
+        assert np.array_equal(k_prun, ref["k_prun"][0][0]), (b, h)
+        assert np.array_equal(v_mid, ref["v_mid"][0][0]), (b, h)
 
 
 def oracle_outputs(q, k, v, mask, n_sink, window, pairs=None):
