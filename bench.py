@@ -174,7 +174,12 @@ def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20):
 
 
 def cpu_baseline(cfg, target_seconds):
-    """The CPU oracle on the same workload's full decode step, on host cores."""
+    """The CPU oracle on the same workload's decode step, on host cores.
+
+    Samples whole batch rows (all query heads of a row, full context),
+    cycling through the batch until about `target_seconds` of CPU time have
+    been spent, and scales the mean time per row to the full batch.
+    """
     import numpy as np
     import torch
 
@@ -194,38 +199,79 @@ def cpu_baseline(cfg, target_seconds):
     q = make_q(cfg, 0, device=dev)
     kh, vh, qh = bf16_bits(k), bf16_bits(v), bf16_bits(q)
     del k, v
-    # sample: whole batch rows (all 32 query heads each) until the time target
     per_row = []
     t_all = time.perf_counter()
-    b = 0
-    while time.perf_counter() - t_all < target_seconds and b < cfg.batch:
+    n = 0
+    while time.perf_counter() - t_all < target_seconds:
+        b = n % cfg.batch
         t0 = time.perf_counter()
         oracle.decode(qh[b:b + 1], kh[b:b + 1], vh[b:b + 1], om[0], cfg.n_sink, cfg.window)
         per_row.append(time.perf_counter() - t0)
-        b += 1
+        n += 1
     us_per_step = float(np.mean(per_row)) * cfg.batch * 1e6
     return {
         "value": us_per_step,
         "unit": "us/step",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{len(per_row)} of {cfg.batch} batch rows of the {cfg.name} step "
-                   f"(all {cfg.n_q_heads} query heads, ctx {cfg.ctx}), float64 numpy, "
-                   f"scaled to the full batch; {sum(per_row):.1f} s of CPU time"),
+        "sample": (f"{n} batch-row decodes of the {cfg.name} step ({n / cfg.batch:.1f} passes over "
+                   f"the {cfg.batch} rows; each row = all {cfg.n_q_heads} query heads over the "
+                   f"{cfg.ctx}-token cache), float64 numpy, mean per row x {cfg.batch}; "
+                   f"{sum(per_row):.1f} s of CPU time"),
     }
 
 
 def copy_calibration():
-    """A plain device copy of known size, for scaling memory counters."""
+    """A plain device copy of known size (256 MiB read + 256 MiB written), run
+    five times, so that memory counters of the same profile can be scaled."""
     import torch
 
     n = 256 << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
     dst = torch.empty_like(src)
+    torch.cuda.synchronize()
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
     return {"bytes_read": n, "bytes_written": n, "launches": 5}
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_llama_b64_4k_counters.md")
+KERNEL_SOURCES = ["decode_attention_channel_amd/csrc/decode_kernels.h",
+                  "decode_attention_channel_amd/csrc/decode_g4.hip",
+                  "decode_attention_channel_amd/csrc/decode.hip",
+                  "decode_attention_channel_amd/csrc/common.h",
+                  "decode_attention_channel_amd/csrc/plan.hip"]
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter summary, or None
+    if the summary is missing or was taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_decode_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -300,12 +346,12 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_kernel<4>",
+            "kernel": "leank_decode_attn = decode_split_kernel<4> + decode_combine_kernel<4>",
             "achieved": main_res["achieved_GBps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": main_res["frac_of_peak"],
-            "traffic": None,
+            "traffic": measured_traffic(),
             "bytes_per_launch": main_res["decode_bytes_mean"],
             "launch_us": main_res["decode_us_mean"],
         },
