@@ -22,6 +22,18 @@ namespace leank {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// V rows are stored in blocks of LEANK_V_BLOCK rows: a region of `rows` rows
+// takes v_rows(rows) rows of storage.
+__host__ __device__ inline int64_t v_rows(int64_t rows) {
+  return (rows + LEANK_V_BLOCK - 1) / LEANK_V_BLOCK * LEANK_V_BLOCK;
+}
+
+// Element offset of (row r, channel ch) inside a V region stored in blocks:
+// block r / 8 holds, channel by channel, the 8 rows of that block.
+__host__ __device__ inline int64_t v_elem(int64_t r, int ch) {
+  return ((r / LEANK_V_BLOCK) * LEANK_HEAD_DIM + ch) * LEANK_V_BLOCK + (r % LEANK_V_BLOCK);
+}
+
 // Decomposition of one decode call into work items.  Every (batch row,
 // KV head) pair owns n_sl_items items over its full-width rows followed by
 // n_mid[h] items over its middle rows; the pairs of one batch row are laid

@@ -66,6 +66,8 @@ extern "C" int leank_decode_attn(const leank_layer_cache* c, const void* q, int6
   p.out = out;
   p.partials = static_cast<float*>(workspace);
   p.mid_cap = c->mid_capacity;
+  p.v_mid_rows = v_rows(c->mid_capacity);
+  p.v_sl_rows = v_rows(static_cast<int64_t>(c->n_sink) + c->window);
   p.n_kv = c->n_kv_heads;
   p.n_q = c->n_q_heads;
   p.slots = c->n_sink + c->window;

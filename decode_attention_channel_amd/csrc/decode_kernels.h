@@ -1,38 +1,42 @@
-// Device code of leank_decode_attn: single-token decode attention over the channel-pruned
-// cache (LeanK page, section 3.1 item 3 and section 3.2; GQA as in section
-// 5.2.3 of the KV-pruning white paper; scale as in FastGen page 5.3).
+// Device code of leank_decode_attn: single-token decode attention over the
+// channel-pruned cache (LeanK page, section 3.1 item 3 and section 3.2; GQA
+// as in section 5.2.3 of the KV-pruning white paper; scale as in FastGen
+// page 5.3).
 //
 // Work items.  Each (batch row b, KV head h) pair is split into items over
 // its full-width rows (K_sl/V_sl, 128 channels) and, for a live head, over
-// its middle rows (K_prun with the head's kept channels, V_mid).  One
-// 256-thread workgroup runs one item; its 4 wavefronts take the item's row
-// tiles round-robin.  All G query heads of the group share every K and V
-// load.
+// its middle rows (K_prun with the head's kept channels c, V_mid).  One
+// 256-thread workgroup runs one item; its 4 wavefronts take 32-row tiles
+// round-robin.  All G query heads of the group share every K and V load.
 //
-// Lane layout inside a wavefront (4 rows of 16 lanes):
-//   V: lane (r, i) loads 16 bytes (channels 8i..8i+7) of token row 4j + r
-//      for V-load j, so a V-load moves 4 whole 256-byte rows.
-//   K: a K row of C = 8R channels is loaded by R lanes, 16 bytes each; a
-//      K-load moves 64/R rows (1 KB).  Lane (r, i) takes chunk i % R of row
-//      4 * (i / R) + r of the load, so the K row that V-load j needs sits in
-//      the same 16-lane row r as that V row.
-// Scores: bf16 dot2 products of the lane's 8 channels, summed over the R
-// lanes of the K row with DPP (quad_perm, half-mirror, mirror), scaled by
-// scale*log2(e).  Softmax runs in base 2 with one running max per
-// wavefront; the exp2 of each score is computed once in the K layout and
-// broadcast to the 16 lanes of its V row with DPP row_newbcast.
+// Matrix instructions (v_mfma_f32_16x16x32_bf16; lane l, col = l % 16,
+// grp = l / 16):
+//   scores  S[head][row] = Q[head][ch] K[row][ch]^T: the A operand is the
+//           group's q (head = col, 8 channels per lane, gathered through
+//           kept_idx), the B operand is K as stored (row = col, the same 8
+//           channels: one 16-byte load of a K row), one instruction per 16
+//           rows and 32 channels;
+//   output  O[head][ch] += P[head][row] V[row][ch]: the A operand is P
+//           (head = col, rows 8 grp .. 8 grp + 7), the B operand is V as
+//           stored in 8-row blocks (channel = col, one 16-byte load = the
+//           8 rows), one instruction per 32 rows and 16 channels.  P goes
+//           in as two bf16 parts (hi + lo), which keeps about 16 bits of
+//           each weight.
+// Results of both land with head 4 grp + i in register i, so the softmax of
+// a head runs inside one 16-lane row: DPP reductions only, base-2 exp of
+// scores pre-scaled by scale * log2(e), and a reference max that moves only
+// when a tile's max exceeds it by more than 2^8.  P reaches the A-operand
+// layout through a 2 KiB per-wavefront LDS transpose.
 //
-// Merge.  The 4 rows of a wavefront share the running max, so their sums
-// and V accumulators add directly (permlane16/32 swaps).  The 4 wavefronts
-// merge through LDS into one (max, sum, acc[G][128]) record per item.  A
-// second kernel merges each (b, h) pair's records in item order and writes
-// the output, so the result does not depend on scheduling and no workgroup
-// waits on another.
-
+// Merge.  The 4 wavefronts merge through LDS into one (max, sum,
+// acc[G][128]) record per item.  A second kernel merges each (b, h) pair's
+// records in item order and writes the output, so the result does not
+// depend on scheduling and no workgroup waits on another.
+//
 // Compile-time tuning knobs (defaults are the measured best on MI355X):
-//   LEANK_NT_LOADS         1 = stream K/V with non-temporal loads
-//   LEANK_TILE_ROWS_NARROW rows per tile when a K row is <= 32 channels and G <= 4
-//   LEANK_TILE_ROWS_WIDE   rows per tile for 64/128-channel K rows and G <= 4
+//   LEANK_NT_LOADS      1 = stream K/V with non-temporal loads
+//   LEANK_PREFETCH      1 = load the next tile while the current one computes
+//   LEANK_WAVES_PER_EU  register budget hint for the split kernel (0 = none)
 
 #pragma once
 
@@ -43,19 +47,29 @@
 #ifndef LEANK_NT_LOADS
 #define LEANK_NT_LOADS 1
 #endif
-#ifndef LEANK_TILE_ROWS_NARROW
-#define LEANK_TILE_ROWS_NARROW 64
+#ifndef LEANK_PREFETCH
+#define LEANK_PREFETCH 0
 #endif
-#ifndef LEANK_TILE_ROWS_WIDE
-#define LEANK_TILE_ROWS_WIDE 32
+#ifndef LEANK_WAVES_PER_EU
+#define LEANK_WAVES_PER_EU 3
+#endif
+#if LEANK_WAVES_PER_EU
+#define LEANK_SPLIT_ATTRS __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LEANK_WAVES_PER_EU)))
+#else
+#define LEANK_SPLIT_ATTRS __launch_bounds__(kThreads)
 #endif
 
 namespace leank {
 
-
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kTileRows = 32;
 constexpr float kLog2e = 1.4426950408889634f;
+
+// The reference max only moves when a tile's max exceeds it by more than
+// this (base-2 units), so weights stay <= 2^kRescaleSlack and most tiles
+// skip the rescale; the softmax is unchanged because the reference cancels.
+constexpr float kRescaleSlack = 8.0f;
 
 struct DecodeHead {
   int64_t k_off;   // elements of K_prun, -1 for a dead head
@@ -76,6 +90,8 @@ struct DecodeParams {
   float* out;
   float* partials;
   int64_t mid_cap;
+  int64_t v_mid_rows;  // stored V rows per batch row of a middle segment
+  int64_t v_sl_rows;   // stored V rows per (batch row, head) of the ring
   int32_t n_kv;
   int32_t n_q;
   int32_t slots;
@@ -86,238 +102,242 @@ struct DecodeParams {
   int32_t items_per_b;
   int32_t partial_stride;
   int32_t combine_slices;  // channel slices per (pair, query head) in the combine
-  float qk_scale;  // softmax scale * log2(e)
+  float qk_scale;          // softmax scale * log2(e)
   DecodeHead heads[LEANK_MAX_KV_HEADS];
 };
 
-// The running max only moves when a tile's max exceeds it by more than this
-// (base-2 units), so weights stay <= 2^kRescaleSlack and most tiles skip
-// the rescale; the softmax is unchanged because the reference cancels.
-constexpr float kRescaleSlack = 8.0f;
-
-template <int G>
-struct Running {
-  float m[G];       // reference max (base-2 units), uniform over the wavefront
-  float l[G];       // sum of exp2 weights of this lane's K rows (K layout)
-  float acc[G][8];  // weighted V for this lane's 8 channels (V layout)
-};
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// x + x of the row at lane distance 16 / 32, as a VALU swap (no LDS).
-__device__ __forceinline__ float add_xor16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float add_xor32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float max_xor16(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_xor32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
 // 16-byte load of streamed cache data (read once per call).
-__device__ __forceinline__ uint4 load_stream16(const uint16_t* p) {
+__device__ __forceinline__ u32x4_t load_stream16(const uint16_t* p) {
 #if LEANK_NT_LOADS
-  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 #else
-  const u32x4_t t = *reinterpret_cast<const u32x4_t*>(p);
+  return *reinterpret_cast<const u32x4_t*>(p);
 #endif
-  return make_uint4(t[0], t[1], t[2], t[3]);
 }
 
-template <int G, int R>
-struct TileShape {
-  static constexpr int kRowsPerKLoad = 64 / R;
-  static constexpr int kWant =
-      G > 4 ? (R == 16 ? 16 : 32) : (R >= 8 ? LEANK_TILE_ROWS_WIDE : LEANK_TILE_ROWS_NARROW);
-  static constexpr int kRows = kWant > kRowsPerKLoad ? kWant : kRowsPerKLoad;
-  static constexpr int kVLoads = kRows / 4;
-  static constexpr int kKLoads = kRows / kRowsPerKLoad;
-  static constexpr int kRowsPerGroup = 16 / R;  // K rows per 16-lane row per K-load
+__device__ __forceinline__ f32x4_t mfma_bf16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// max / sum over the 16 lanes of a row, result in every lane of the row
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+  return fmaxf(x, dpp_f32<kDppRowMirror>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_f32<kDppQuadXor1>(x);
+  x += dpp_f32<kDppQuadXor2>(x);
+  x += dpp_f32<kDppHalfMirror>(x);
+  return x + dpp_f32<kDppRowMirror>(x);
+}
+
+// Per-wavefront running state.  Register i of lane l belongs to query head
+// 4 * (l / 16) + i of the group; o[n] holds channels 16 n + l % 16.
+struct WaveState {
+  f32x4_t o[8];  // weighted V
+  float m[4];    // reference max of the head (uniform over the 16-lane row)
+  float l[4];    // this lane's part of the head's weight sum
 };
 
-// One tile of kRows rows starting at row t0 of the stream (rows >= nvalid
-// are outside the item when kTail).  kb/vb point at row 0 of the K and V
-// streams; kstride is the K row length in elements (= 8R unless kGeneric,
-// where R = 16 and only lanes with k_active hold K data).
-template <int G, int R, bool kTail, bool kGeneric>
-__device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ kb,
-                                            const uint16_t* __restrict__ vb, int kstride, int t0,
-                                            int nvalid, bool k_active, const uint32_t (&qw)[G][4],
-                                            float qk_scale, Running<G>& st) {
-  using S = TileShape<G, R>;
+// K and V operands of one 32-row tile.
+template <int KB>
+struct TileRegs {
+  u32x4_t kf[2][KB];  // K rows t0 + 16 j + col, channels 32 kk + 8 grp .. +7
+  u32x4_t vf[8];      // V block t0 / 8 + grp, channel 16 n + col
+};
+
+// Issues the loads of the tile starting at row t0 (rows >= nvalid are
+// outside the item).  kb: K row 0 (row length kstride = c elements); vb: V
+// block 0 of the stream.
+template <int KB>
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ kb, int kstride,
+                                          const uint16_t* __restrict__ vb, int t0, int nvalid,
+                                          int c, TileRegs<KB>& tr) {
   const int lane = threadIdx.x & 63;
-  const int row16 = lane >> 4;
-  const int i = lane & 15;
-  const int grp = i / R;
-  const int chunk = i % R;
-
+  const int col = lane & 15;
+  const int grp = lane >> 4;
   const uint16_t* kt = kb + static_cast<int64_t>(t0) * kstride;
-  const uint16_t* vt = vb + static_cast<int64_t>(t0) * LEANK_HEAD_DIM;
-  uint4 kv[S::kKLoads];
-  uint4 vv[S::kVLoads];
-  static_for<S::kKLoads>([&](auto KK) {
-    constexpr int kk = decltype(KK)::value;
-    const int row = kk * S::kRowsPerKLoad + 4 * grp + row16;
-    const bool ok = (!kTail || row < nvalid) && (!kGeneric || k_active);
-    kv[kk] = ok ? load_stream16(kt + row * kstride + chunk * 8) : make_uint4(0u, 0u, 0u, 0u);
-  });
-  static_for<S::kVLoads>([&](auto JJ) {
-    constexpr int jj = decltype(JJ)::value;
-    const int row = 4 * jj + row16;
-    const bool ok = !kTail || row < nvalid;
-    vv[jj] = ok ? load_stream16(vt + row * LEANK_HEAD_DIM + i * 8) : make_uint4(0u, 0u, 0u, 0u);
-  });
-
-  // scores (base-2 logits) of the K rows this lane's group holds
-  float s[S::kKLoads][G];
-  static_for<S::kKLoads>([&](auto KK) {
-    constexpr int kk = decltype(KK)::value;
-    const int row = kk * S::kRowsPerKLoad + 4 * grp + row16;
-    static_for<G>([&](auto GG) {
-      constexpr int g = decltype(GG)::value;
-      float a = dot2_bf16(qw[g][0], kv[kk].x, 0.0f);
-      a = dot2_bf16(qw[g][1], kv[kk].y, a);
-      a = dot2_bf16(qw[g][2], kv[kk].z, a);
-      a = dot2_bf16(qw[g][3], kv[kk].w, a);
-      if constexpr (R >= 2) a += dpp_f32<kDppQuadXor1>(a);
-      if constexpr (R >= 4) a += dpp_f32<kDppQuadXor2>(a);
-      if constexpr (R >= 8) a += dpp_f32<kDppHalfMirror>(a);
-      if constexpr (R >= 16) a += dpp_f32<kDppRowMirror>(a);
-      a *= qk_scale;
-      if (kTail && row >= nvalid) a = -INFINITY;
-      s[kk][g] = a;
-    });
-  });
-
-  // running max over the wavefront, lazy rescale, exp2 in the K layout
-  static_for<G>([&](auto GG) {
-    constexpr int g = decltype(GG)::value;
-    float mx = s[0][g];
-    static_for<S::kKLoads>([&](auto KK) {
-      constexpr int kk = decltype(KK)::value;
-      if constexpr (kk > 0) mx = fmaxf(mx, s[kk][g]);
-    });
-    if constexpr (R < 2) mx = fmaxf(mx, dpp_f32<kDppQuadXor1>(mx));
-    if constexpr (R < 4) mx = fmaxf(mx, dpp_f32<kDppQuadXor2>(mx));
-    if constexpr (R < 8) mx = fmaxf(mx, dpp_f32<kDppHalfMirror>(mx));
-    if constexpr (R < 16) mx = fmaxf(mx, dpp_f32<kDppRowMirror>(mx));
-    mx = max_xor32(max_xor16(mx));
-    mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mx)));
-    if (mx > st.m[g] + kRescaleSlack) {  // uniform over the wavefront
-      const float corr = st.m[g] == -INFINITY ? 0.0f : fast_exp2(st.m[g] - mx);
-      st.m[g] = mx;
-      st.l[g] *= corr;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) st.acc[g][c] *= corr;
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int row = 16 * j + col;
+      const int ch = 32 * kk + 8 * grp;
+      const bool ok = ch < c && row < nvalid;
+      tr.kf[j][kk] = ok ? load_stream16(kt + row * kstride + ch) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    const float m_use = st.m[g] == -INFINITY ? 0.0f : st.m[g];
-    static_for<S::kKLoads>([&](auto KK) {
-      constexpr int kk = decltype(KK)::value;
-      s[kk][g] = fast_exp2(s[kk][g] - m_use);
-      st.l[g] += s[kk][g];
-    });
-  });
+  }
+  const uint16_t* vt = vb + (static_cast<int64_t>(t0 / 8 + grp) * LEANK_HEAD_DIM + col) * 8;
+  const bool v_ok = 8 * grp < nvalid;
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+    tr.vf[n] = v_ok ? load_stream16(vt + n * 16 * 8) : u32x4_t{0u, 0u, 0u, 0u};
+}
 
-  // weighted V: V-load jj holds row 4jj + row16, whose weight sits in K-load
-  // jj / kRowsPerGroup, lane group jj % kRowsPerGroup of the same 16-lane row
-  static_for<S::kVLoads>([&](auto JJ) {
-    constexpr int jj = decltype(JJ)::value;
-    constexpr int kk = jj / S::kRowsPerGroup;
-    constexpr int src_lane = R * (jj % S::kRowsPerGroup);
-    float v[8];
-    v[0] = bf16_lo(vv[jj].x);
-    v[1] = bf16_hi(vv[jj].x);
-    v[2] = bf16_lo(vv[jj].y);
-    v[3] = bf16_hi(vv[jj].y);
-    v[4] = bf16_lo(vv[jj].z);
-    v[5] = bf16_hi(vv[jj].z);
-    v[6] = bf16_lo(vv[jj].w);
-    v[7] = bf16_hi(vv[jj].w);
-    static_for<G>([&](auto GG) {
-      constexpr int g = decltype(GG)::value;
-      float p;
-      if constexpr (S::kRowsPerGroup == 1) {
-        p = s[kk][g];
-      } else {
-        p = dpp_f32<kDppRowNewBcast + src_lane>(s[kk][g]);
+// Scores, softmax bookkeeping and weighted V of one loaded tile.
+template <int G, int KB, bool kTail>
+__device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, const u32x4_t (&qa)[KB],
+                                             float qk_scale, uint16_t* __restrict__ p_lds,
+                                             WaveState& st) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  // scores: s[j][i] = head 4 grp + i, row 16 j + col
+  f32x4_t s[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    s[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) s[j] = mfma_bf16(qa[kk], tr.kf[j][kk], s[j]);
+  }
+
+  float mx[4];
+  bool grow = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float v = s[j][i] * qk_scale;
+      if (kTail && 16 * j + col >= nvalid) v = -INFINITY;
+      s[j][i] = v;
+    }
+    mx[i] = row_max16(fmaxf(s[0][i], s[1][i]));
+    grow |= mx[i] > st.m[i] + kRescaleSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float corr = 1.0f;
+      if (mx[i] > st.m[i] + kRescaleSlack) {
+        corr = st.m[i] == -INFINITY ? 0.0f : fast_exp2(st.m[i] - mx[i]);
+        st.m[i] = mx[i];
       }
+      st.l[i] *= corr;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) st.acc[g][c] = fmaf(p, v[c], st.acc[g][c]);
-    });
-  });
+      for (int n = 0; n < 8; ++n) st.o[n][i] *= corr;
+    }
+  }
+
+  // weights, staged in LDS as bf16 hi/lo parts: p_lds[part][head][row]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float m_use = st.m[i] == -INFINITY ? 0.0f : st.m[i];
+    const int head = 4 * grp + i;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float p = fast_exp2(s[j][i] - m_use);
+      st.l[i] += p;
+      if (head < G) {
+        const __bf16 hi = static_cast<__bf16>(p);
+        const __bf16 lo = static_cast<__bf16>(p - static_cast<float>(hi));
+        p_lds[head * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, hi);
+        p_lds[(16 + head) * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, lo);
+      }
+    }
+  }
+  const u32x4_t pa_hi = *reinterpret_cast<const u32x4_t*>(p_lds + col * kTileRows + 8 * grp);
+  const u32x4_t pa_lo = *reinterpret_cast<const u32x4_t*>(p_lds + (16 + col) * kTileRows + 8 * grp);
+
+  if (kTail) {
+    // zero the V rows of the lane's block that lie past the item
+    const int valid = min(max(nvalid - 8 * grp, 0), 8);
+    u32x4_t keep;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      keep[w] = (2 * w < valid ? 0x0000ffffu : 0u) | (2 * w + 1 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) tr.vf[n] &= keep;
+  }
+
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    st.o[n] = mfma_bf16(pa_hi, tr.vf[n], st.o[n]);
+    st.o[n] = mfma_bf16(pa_lo, tr.vf[n], st.o[n]);
+  }
 }
 
-template <int G, int R, bool kGeneric>
-__device__ __forceinline__ void attend_range(const uint16_t* kb, const uint16_t* vb, int kstride,
-                                             int r0, int r1, bool k_active,
-                                             const uint32_t (&qw)[G][4], float qk_scale,
-                                             Running<G>& st) {
-  constexpr int kRows = TileShape<G, R>::kRows;
+template <int G, int KB>
+__device__ __forceinline__ void attend_range(const uint16_t* kb, int kstride, const uint16_t* vb,
+                                             int r0, int r1, int c, const u32x4_t (&qa)[KB],
+                                             float qk_scale, uint16_t* p_lds, WaveState& st) {
   const int wave = threadIdx.x >> 6;
-  for (int t0 = r0 + wave * kRows; t0 < r1; t0 += kWaves * kRows) {
+  int t0 = r0 + wave * kTileRows;
+#if LEANK_PREFETCH
+  // the next tile's loads are in flight while this one computes
+  TileRegs<KB> cur;
+  if (t0 < r1) load_tile<KB>(kb, kstride, vb, t0, r1 - t0, c, cur);
+  for (; t0 < r1; t0 += kWaves * kTileRows) {
+    const int tn = t0 + kWaves * kTileRows;
+    TileRegs<KB> nxt;
+    if (tn < r1) load_tile<KB>(kb, kstride, vb, tn, r1 - tn, c, nxt);
     const int nvalid = r1 - t0;
-    if (nvalid >= kRows) {
-      attend_tile<G, R, false, kGeneric>(kb, vb, kstride, t0, kRows, k_active, qw, qk_scale, st);
+    if (nvalid >= kTileRows) {
+      compute_tile<G, KB, false>(cur, kTileRows, qa, qk_scale, p_lds, st);
     } else {
-      attend_tile<G, R, true, kGeneric>(kb, vb, kstride, t0, nvalid, k_active, qw, qk_scale, st);
+      compute_tile<G, KB, true>(cur, nvalid, qa, qk_scale, p_lds, st);
+    }
+    cur = nxt;
+  }
+#else
+  for (; t0 < r1; t0 += kWaves * kTileRows) {
+    const int nvalid = r1 - t0;
+    TileRegs<KB> cur;
+    load_tile<KB>(kb, kstride, vb, t0, nvalid, c, cur);
+    if (nvalid >= kTileRows) {
+      compute_tile<G, KB, false>(cur, kTileRows, qa, qk_scale, p_lds, st);
+    } else {
+      compute_tile<G, KB, true>(cur, nvalid, qa, qk_scale, p_lds, st);
     }
   }
-  // each lane group of R lanes summed the weights of its own K rows: add the
-  // groups of the 16-lane row so that l covers the row's V rows like acc
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if constexpr (R < 2) st.l[g] += dpp_f32<kDppQuadXor1>(st.l[g]);
-    if constexpr (R < 4) st.l[g] += dpp_f32<kDppQuadXor2>(st.l[g]);
-    if constexpr (R < 8) st.l[g] += dpp_f32<kDppHalfMirror>(st.l[g]);
-    if constexpr (R < 16) st.l[g] += dpp_f32<kDppRowMirror>(st.l[g]);
-  }
+#endif
 }
 
-// q channels of the lane's K chunk for the G query heads, packed bf16 pairs.
-template <int G>
-__device__ __forceinline__ void load_q_dense(const uint16_t* qh, int chunk, uint32_t (&qw)[G][4]) {
+// A operand of the score product for this lane: query head col of the
+// group, kept channels 32 kk + 8 grp .. +7 (zero past c or for col >= G).
+template <int G, int KB>
+__device__ __forceinline__ void gather_q(const uint16_t* s_q, const int16_t* s_idx, bool dense,
+                                         int c, u32x4_t (&qa)[KB]) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const uint4 w = *reinterpret_cast<const uint4*>(qh + g * LEANK_HEAD_DIM + chunk * 8);
-    qw[g][0] = w.x;
-    qw[g][1] = w.y;
-    qw[g][2] = w.z;
-    qw[g][3] = w.w;
-  }
-}
-
-template <int G>
-__device__ __forceinline__ void load_q_gather(const uint16_t* qh, const int16_t* idx, int chunk,
-                                              bool active, uint32_t (&qw)[G][4]) {
-  int ch[8];
+  for (int kk = 0; kk < KB; ++kk) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) ch[k] = active ? (idx[chunk * 8 + k] & (LEANK_HEAD_DIM - 1)) : 0;
+    for (int w = 0; w < 4; ++w) {
+      uint32_t word = 0;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = active ? qh[g * LEANK_HEAD_DIM + ch[2 * k]] : 0u;
-      const uint32_t hi = active ? qh[g * LEANK_HEAD_DIM + ch[2 * k + 1]] : 0u;
-      qw[g][k] = lo | (hi << 16);
+      for (int half = 0; half < 2; ++half) {
+        const int j = 32 * kk + 8 * grp + 2 * w + half;
+        uint32_t v = 0;
+        if (col < G && j < c) {
+          const int ch = dense ? j : (s_idx[j] & (LEANK_HEAD_DIM - 1));
+          v = s_q[col * LEANK_HEAD_DIM + ch];
+        }
+        word |= v << (16 * half);
+      }
+      qa[kk][w] = word;
     }
   }
 }
 
 template <int G>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeParams p) {
+__global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ float s_acc[kWaves][G][LEANK_HEAD_DIM];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
+  __shared__ uint16_t s_q[G * LEANK_HEAD_DIM];
+  __shared__ int16_t s_idx[LEANK_HEAD_DIM];
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[kWaves][2 * 16 * kTileRows];
 
   const int item = blockIdx.x;
   const int b = item / p.items_per_b;
@@ -327,97 +347,98 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
   const DecodeHead hd = p.heads[h];
   const int local = r - hd.base;
   const bool middle = local >= p.n_sl_items;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
 
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15;
+  // stage the group's q rows and the head's kept ids; clear the P staging
   const uint16_t* qh = p.q + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM;
+  if (t < G * 16)
+    *reinterpret_cast<u32x4_t*>(s_q + t * 8) = *reinterpret_cast<const u32x4_t*>(qh + t * 8);
+  if (middle && t >= 128 && t < 144)
+    *reinterpret_cast<u32x4_t*>(s_idx + (t - 128) * 8) =
+        *reinterpret_cast<const u32x4_t*>(p.kept_idx + h * LEANK_HEAD_DIM + (t - 128) * 8);
+  for (int k = lane; k < 2 * 16 * kTileRows / 8; k += 64)
+    reinterpret_cast<u32x4_t*>(s_p[wave])[k] = u32x4_t{0u, 0u, 0u, 0u};
+  __syncthreads();
 
-  Running<G> st;
+  WaveState st;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    st.m[g] = -INFINITY;
-    st.l[g] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) st.acc[g][c] = 0.0f;
+  for (int i = 0; i < 4; ++i) {
+    st.m[i] = -INFINITY;
+    st.l[i] = 0.0f;
   }
-  uint32_t qw[G][4];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) st.o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint16_t* p_lds = s_p[wave];
 
   if (!middle) {
     const int r0 = local * p.sl_rows;
     const int r1 = min(p.t_sl, r0 + p.sl_rows);
     const int64_t pair = static_cast<int64_t>(b) * p.n_kv + h;
     const uint16_t* kb = p.k_sl + pair * p.slots * LEANK_HEAD_DIM;
-    const uint16_t* vb = p.v_sl + pair * p.slots * LEANK_HEAD_DIM;
-    load_q_dense<G>(qh, i, qw);
-    attend_range<G, 16, false>(kb, vb, LEANK_HEAD_DIM, r0, r1, true, qw, p.qk_scale, st);
+    const uint16_t* vb = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM;
+    u32x4_t qa[4];
+    gather_q<G, 4>(s_q, s_idx, true, LEANK_HEAD_DIM, qa);
+    attend_range<G, 4>(kb, LEANK_HEAD_DIM, vb, r0, r1, LEANK_HEAD_DIM, qa, p.qk_scale, p_lds, st);
   } else {
     const int chunk_id = local - p.n_sl_items;
     const int r0 = chunk_id * hd.mid_rows;
     const int r1 = min(p.t_mid, r0 + hd.mid_rows);
-    const int kept = hd.kept;
-    const int64_t brow = static_cast<int64_t>(b) * p.mid_cap;
-    const uint16_t* kb = p.k_prun + hd.k_off + brow * kept;
-    const uint16_t* vb = p.v_mid + hd.v_off + brow * LEANK_HEAD_DIM;
-    const int16_t* idx = p.kept_idx + h * LEANK_HEAD_DIM;
-    switch (kept) {
-      case 8:
-        load_q_gather<G>(qh, idx, i % 1, true, qw);
-        attend_range<G, 1, false>(kb, vb, 8, r0, r1, true, qw, p.qk_scale, st);
+    const int c = hd.kept;
+    const uint16_t* kb = p.k_prun + hd.k_off + static_cast<int64_t>(b) * p.mid_cap * c;
+    const uint16_t* vb = p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM;
+    switch ((c + 31) / 32) {
+      case 1: {
+        u32x4_t qa[1];
+        gather_q<G, 1>(s_q, s_idx, false, c, qa);
+        attend_range<G, 1>(kb, c, vb, r0, r1, c, qa, p.qk_scale, p_lds, st);
         break;
-      case 16:
-        load_q_gather<G>(qh, idx, i % 2, true, qw);
-        attend_range<G, 2, false>(kb, vb, 16, r0, r1, true, qw, p.qk_scale, st);
+      }
+      case 2: {
+        u32x4_t qa[2];
+        gather_q<G, 2>(s_q, s_idx, false, c, qa);
+        attend_range<G, 2>(kb, c, vb, r0, r1, c, qa, p.qk_scale, p_lds, st);
         break;
-      case 32:
-        load_q_gather<G>(qh, idx, i % 4, true, qw);
-        attend_range<G, 4, false>(kb, vb, 32, r0, r1, true, qw, p.qk_scale, st);
+      }
+      case 3: {
+        u32x4_t qa[3];
+        gather_q<G, 3>(s_q, s_idx, false, c, qa);
+        attend_range<G, 3>(kb, c, vb, r0, r1, c, qa, p.qk_scale, p_lds, st);
         break;
-      case 64:
-        load_q_gather<G>(qh, idx, i % 8, true, qw);
-        attend_range<G, 8, false>(kb, vb, 64, r0, r1, true, qw, p.qk_scale, st);
-        break;
-      case 128:
-        load_q_gather<G>(qh, idx, i, true, qw);
-        attend_range<G, 16, false>(kb, vb, 128, r0, r1, true, qw, p.qk_scale, st);
-        break;
+      }
       default: {
-        const bool active = i < kept / 8;
-        load_q_gather<G>(qh, idx, i, active, qw);
-        attend_range<G, 16, true>(kb, vb, kept, r0, r1, active, qw, p.qk_scale, st);
+        u32x4_t qa[4];
+        gather_q<G, 4>(s_q, s_idx, false, c, qa);
+        attend_range<G, 4>(kb, c, vb, r0, r1, c, qa, p.qk_scale, p_lds, st);
         break;
       }
     }
   }
 
-  // the 4 rows of the wavefront share st.m: add their sums and accumulators
+  // this wavefront's part of the record: heads 4 grp + i, channels 16 n + col
+  const int col = lane & 15;
+  const int grp = lane >> 4;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    st.l[g] = add_xor32(add_xor16(st.l[g]));
+  for (int i = 0; i < 4; ++i) {
+    const float l = row_sum16(st.l[i]);
+    const int head = 4 * grp + i;
+    if (head < G) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) st.acc[g][c] = add_xor32(add_xor16(st.acc[g][c]));
-  }
-  const int wave = threadIdx.x >> 6;
-  if (lane < 16) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) s_acc[wave][g][lane * 8 + c] = st.acc[g][c];
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      s_m[wave][g] = st.m[g];
-      s_l[wave][g] = st.l[g];
+      for (int n = 0; n < 8; ++n) s_acc[wave][head][16 * n + col] = st.o[n][i];
+      if (col == 0) {
+        s_m[wave][head] = st.m[i];
+        s_l[wave][head] = l;
+      }
     }
   }
   __syncthreads();
 
   // one record per item: (acc[G][128], m[G], l[G]) merged over the wavefronts
   float* rec = p.partials + static_cast<int64_t>(item) * p.partial_stride;
-  for (int t = threadIdx.x; t < G * LEANK_HEAD_DIM; t += kThreads) {
-    const int g = t / LEANK_HEAD_DIM;
-    const int ch = t - g * LEANK_HEAD_DIM;
+  for (int k = t; k < G * LEANK_HEAD_DIM; k += kThreads) {
+    const int g = k / LEANK_HEAD_DIM;
+    const int ch = k - g * LEANK_HEAD_DIM;
     float m = s_m[0][g];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_m[w][g]);
@@ -429,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
       a = fmaf(s_acc[w][g][ch], f, a);
       l = fmaf(s_l[w][g], f, l);
     }
-    rec[t] = a;
+    rec[k] = a;
     if (ch == 0) {
       rec[G * LEANK_HEAD_DIM + g] = m;
       rec[G * LEANK_HEAD_DIM + G + g] = l;

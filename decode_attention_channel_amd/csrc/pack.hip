@@ -2,9 +2,11 @@
 // (LeanK page, section 3.1 item 2; section 3.2 for heads without middle V).
 //
 // One wavefront handles one (batch row, KV head, token) unit and moves one
-// 256-byte K row and one V row: lane l carries 32-bit word l (channels 2l,
-// 2l+1).  The kept-channel gather into K_prun reads the source word of each
-// kept channel from the lane that holds it (ds_bpermute).
+// 256-byte K row and one V row: lane l carries channels 2l, 2l+1.  K rows
+// are row-major; V rows live in 8-row blocks (element (r, c) of a region at
+// ((r / 8) * 128 + c) * 8 + r % 8), so a lane writes its two V values
+// 16 bytes apart.  The kept-channel gather into K_prun reads the source
+// word of each kept channel from the lane that holds it (ds_bpermute).
 
 #include "common.h"
 
@@ -28,14 +30,16 @@ struct PackParams {
   const uint32_t* k_new;
   const uint32_t* v_new;
   uint32_t* k_sl;
-  uint32_t* v_sl;
+  uint16_t* v_sl;
   uint32_t* k_prun;
-  uint32_t* v_mid;
+  uint16_t* v_mid;
   const int16_t* kept_idx;
   int64_t t_old;       // tokens in the cache before the append
   int64_t t_new;       // tokens after it
   int64_t n_new;
   int64_t mid_cap;
+  int64_t v_mid_rows;  // stored V rows per batch row of a middle segment (multiple of 8)
+  int64_t v_sl_rows;   // stored V rows per (batch row, head) of the ring (multiple of 8)
   int64_t unit_lo;     // kMigrate: position of unit 0
   int64_t units_per_pair;
   int64_t n_units;
@@ -50,6 +54,17 @@ struct PackParams {
 
 constexpr int kWordsPerRow = LEANK_HEAD_DIM / 2;  // 64 words of two bf16
 constexpr int kUnitsPerBlock = 4;
+
+__device__ __forceinline__ uint32_t load_v_row_word(const uint16_t* region, int64_t r, int lane) {
+  const uint32_t lo = region[v_elem(r, 2 * lane)];
+  const uint32_t hi = region[v_elem(r, 2 * lane + 1)];
+  return lo | (hi << 16);
+}
+
+__device__ __forceinline__ void store_v_row_word(uint16_t* region, int64_t r, int lane, uint32_t w) {
+  region[v_elem(r, 2 * lane)] = static_cast<uint16_t>(w & 0xffffu);
+  region[v_elem(r, 2 * lane + 1)] = static_cast<uint16_t>(w >> 16);
+}
 
 // Writes one token's K (kept channels) and V (live heads) to middle row r.
 __device__ __forceinline__ void write_middle(const PackParams& p, int b, int h, int64_t r,
@@ -66,7 +81,8 @@ __device__ __forceinline__ void write_middle(const PackParams& p, int b, int h, 
   const uint32_t hi = (c1 & 1) ? (w1 >> 16) : (w1 & 0xffffu);
   const int64_t row = static_cast<int64_t>(b) * p.mid_cap + r;
   if (j0 < hd.kept) p.k_prun[(hd.k_off + row * hd.kept) / 2 + lane] = lo | (hi << 16);
-  p.v_mid[(hd.v_off + row * LEANK_HEAD_DIM) / 2 + lane] = vw;
+  store_v_row_word(p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM, r,
+                   lane, vw);
 }
 
 __global__ __launch_bounds__(64 * kUnitsPerBlock) void pack_kernel(const PackParams p) {
@@ -78,13 +94,13 @@ __global__ __launch_bounds__(64 * kUnitsPerBlock) void pack_kernel(const PackPar
   const int b = static_cast<int>(pair / p.n_kv);
   const int h = static_cast<int>(pair - static_cast<int64_t>(b) * p.n_kv);
   uint32_t* ring_k = p.k_sl + (pair * p.slots) * kWordsPerRow;
-  uint32_t* ring_v = p.v_sl + (pair * p.slots) * kWordsPerRow;
+  uint16_t* ring_v = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM;
 
   if (p.mode == kMigrate) {
     const int64_t q = p.unit_lo + i;
     const int64_t slot = p.n_sink + (q - p.n_sink) % p.window;
     const uint32_t kw = ring_k[slot * kWordsPerRow + lane];
-    const uint32_t vw = ring_v[slot * kWordsPerRow + lane];
+    const uint32_t vw = load_v_row_word(ring_v, slot, lane);
     write_middle(p, b, h, q - p.n_sink, kw, vw, lane);
     return;
   }
@@ -95,7 +111,7 @@ __global__ __launch_bounds__(64 * kUnitsPerBlock) void pack_kernel(const PackPar
   const uint32_t vw = p.v_new[src];
   if (pos < p.n_sink) {
     ring_k[pos * kWordsPerRow + lane] = kw;
-    ring_v[pos * kWordsPerRow + lane] = vw;
+    store_v_row_word(ring_v, pos, lane, vw);
     return;
   }
   if (p.mode == kPlace && pos < p.t_new - p.window) {
@@ -107,12 +123,12 @@ __global__ __launch_bounds__(64 * kUnitsPerBlock) void pack_kernel(const PackPar
     const int64_t leaving = pos - p.window;  // token held by this ring row until now
     if (leaving >= p.n_sink) {
       const uint32_t old_k = ring_k[slot * kWordsPerRow + lane];
-      const uint32_t old_v = ring_v[slot * kWordsPerRow + lane];
+      const uint32_t old_v = load_v_row_word(ring_v, slot, lane);
       write_middle(p, b, h, leaving - p.n_sink, old_k, old_v, lane);
     }
   }
   ring_k[slot * kWordsPerRow + lane] = kw;
-  ring_v[slot * kWordsPerRow + lane] = vw;
+  store_v_row_word(ring_v, slot, lane, vw);
 }
 
 int launch(PackParams& p, int64_t units_per_pair, int64_t pairs, hipStream_t s) {
@@ -145,14 +161,16 @@ extern "C" int leank_pack_k(const leank_layer_cache* c, const void* k_new, const
   p.k_new = static_cast<const uint32_t*>(k_new);
   p.v_new = static_cast<const uint32_t*>(v_new);
   p.k_sl = static_cast<uint32_t*>(c->k_sl);
-  p.v_sl = static_cast<uint32_t*>(c->v_sl);
+  p.v_sl = static_cast<uint16_t*>(c->v_sl);
   p.k_prun = static_cast<uint32_t*>(c->k_prun);
-  p.v_mid = static_cast<uint32_t*>(c->v_mid);
+  p.v_mid = static_cast<uint16_t*>(c->v_mid);
   p.kept_idx = c->kept_idx;
   p.t_old = pos0;
   p.t_new = pos0 + n_new;
   p.n_new = n_new;
   p.mid_cap = c->mid_capacity;
+  p.v_mid_rows = v_rows(c->mid_capacity);
+  p.v_sl_rows = v_rows(static_cast<int64_t>(c->n_sink) + c->window);
   p.n_kv = c->n_kv_heads;
   p.n_sink = c->n_sink;
   p.window = c->window;

@@ -77,7 +77,8 @@ int validate_cache(const leank_layer_cache* c, bool need_buffers) {
     if (k > 0) {
       ++live;
       if (c->k_prun_off[h] < 0 || c->v_mid_off[h] < 0) return LEANK_EINVAL;
-      if (c->k_prun_off[h] % LEANK_CHANNEL_QUANTUM || c->v_mid_off[h] % LEANK_HEAD_DIM) return LEANK_EINVAL;
+      if (c->k_prun_off[h] % LEANK_CHANNEL_QUANTUM || c->v_mid_off[h] % (LEANK_HEAD_DIM * LEANK_V_BLOCK))
+        return LEANK_EINVAL;
     }
   }
   if (live != c->n_live) return LEANK_EINVAL;
@@ -191,11 +192,11 @@ extern "C" int leank_plan_layer(const int32_t* kept_count_host, int32_t batch, i
     c.k_prun_off[h] = k_off;
     c.v_mid_off[h] = v_off;
     k_off += static_cast<int64_t>(batch) * c.mid_capacity * kept;
-    v_off += static_cast<int64_t>(batch) * c.mid_capacity * LEANK_HEAD_DIM;
+    v_off += static_cast<int64_t>(batch) * v_rows(c.mid_capacity) * LEANK_HEAD_DIM;
   }
   const int64_t slots = static_cast<int64_t>(n_sink) + window;
   c.k_sl_bytes = static_cast<uint64_t>(batch) * n_kv_heads * slots * LEANK_HEAD_DIM * 2;
-  c.v_sl_bytes = c.k_sl_bytes;
+  c.v_sl_bytes = static_cast<uint64_t>(batch) * n_kv_heads * v_rows(slots) * LEANK_HEAD_DIM * 2;
   c.k_prun_bytes = static_cast<uint64_t>(k_off) * 2;
   c.v_mid_bytes = static_cast<uint64_t>(v_off) * 2;
   int st = validate_cache(&c, false);

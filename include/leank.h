@@ -39,11 +39,12 @@
 extern "C" {
 #endif
 
-#define LEANK_ABI_VERSION 1
+#define LEANK_ABI_VERSION 2
 #define LEANK_HEAD_DIM 128      /* the only head_dim the kernels implement   */
 #define LEANK_MAX_KV_HEADS 64   /* per-layer KV heads a cache plan can hold  */
 #define LEANK_MAX_GROUP 8       /* query heads per KV head the kernels take  */
 #define LEANK_CHANNEL_QUANTUM 8 /* kept counts must be multiples of this     */
+#define LEANK_V_BLOCK 8         /* V rows per transposed storage block        */
 
 typedef enum {
   LEANK_OK = 0,
@@ -95,19 +96,29 @@ int leank_build_mask(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
  * One layer's channel-pruned KV cache: shape, head grouping and buffer
  * layout.  leank_plan_layer fills every field above `kept_idx`; the caller
  * allocates the four cache buffers with at least the *_bytes reported and
- * sets the pointers.  Layout (bf16 elements, row-major):
+ * sets the pointers.  Layout (bf16 elements):
  *
- *   k_sl, v_sl  [batch][n_kv_heads][n_sink + window][128]
- *               full-width sink + local-window rows (LeanK page, section
- *               3.1 item 2).  Token p < n_sink lives in row p; a window
- *               token p >= n_sink in ring row n_sink + (p - n_sink) % window.
+ *   k_sl        [batch][n_kv_heads][n_sink + window][128], row-major:
+ *               full-width keys of the sink and local-window tokens (LeanK
+ *               page, section 3.1 item 2).  Token p < n_sink lives in row p;
+ *               a window token p >= n_sink in ring row
+ *               n_sink + (p - n_sink) % window.
+ *   v_sl        [batch][n_kv_heads][V(n_sink + window)] with the same rows,
+ *               stored in V blocks (below).
  *   k_prun      per live head h, at element offset k_prun_off[h]:
- *               [batch][mid_capacity][kept_count[h]] -- middle-of-context
- *               keys reduced to the kept channels, in ascending channel
- *               order; middle token p is row p - n_sink.
+ *               [batch][mid_capacity][kept_count[h]], row-major --
+ *               middle-of-context keys reduced to the kept channels, in
+ *               ascending channel order; middle token p is row p - n_sink.
  *   v_mid       per live head h, at element offset v_mid_off[h]:
- *               [batch][mid_capacity][128] -- middle values.  Fully pruned
- *               heads have no segment (LeanK page, section 3.2).
+ *               [batch][V(mid_capacity)] middle values in V blocks.  Fully
+ *               pruned heads have no segment (LeanK page, section 3.2).
+ *
+ * V blocks: a region of R rows x 128 channels takes ceil(R / 8) blocks of
+ * 128 x 8 elements; element (row r, channel c) sits at
+ * ((r / 8) * 128 + c) * 8 + r % 8, so each 16-byte piece holds 8
+ * consecutive rows of one channel (the operand layout of the decode
+ * kernel's matrix instructions).  V(R) denotes that storage, 128 * 8 *
+ * ceil(R / 8) elements.
  *
  * Live heads are grouped by kept count (descending, then head id): their
  * segments follow `group_order`, so heads of one width form one contiguous

@@ -58,6 +58,17 @@ def random_bf16(shape, gen, scale=1.0, device="cuda"):
     return (x * scale).to(torch.bfloat16)
 
 
+def _v_rows(rows):
+    return (rows + 7) // 8 * 8
+
+
+def _unblock_v(flat, rows):
+    """Rows [rows, 128] of a V region stored in 8-row blocks
+    (element (r, c) at ((r // 8) * 128 + c) * 8 + r % 8)."""
+    blocks = flat.reshape(-1, 128, 8)          # [block][channel][row in block]
+    return blocks.transpose(0, 2, 1).reshape(-1, 128)[:rows]
+
+
 def read_pair(cache, b, h, n_mid=None):
     """Host uint16 copies of one (batch row, KV head) pair's cache rows:
     ring K/V [slots, 128], K_prun [n_mid, kept] and V_mid [n_mid, 128] (None
@@ -68,14 +79,18 @@ def read_pair(cache, b, h, n_mid=None):
     n_mid = mid_cap if n_mid is None else n_mid
     base = ((b * d.n_kv_heads) + h) * slots * 128
     ring_k = bf16_bits(cache.k_sl[base: base + slots * 128]).reshape(slots, 128)
-    ring_v = bf16_bits(cache.v_sl[base: base + slots * 128]).reshape(slots, 128)
+    vs = _v_rows(slots)
+    vbase = ((b * d.n_kv_heads) + h) * vs * 128
+    ring_v = _unblock_v(bf16_bits(cache.v_sl[vbase: vbase + vs * 128]), slots)
     c = d.kept_count[h]
     if c == 0:
         return ring_k, ring_v, None, None
     ko = d.k_prun_off[h] + b * mid_cap * c
-    vo = d.v_mid_off[h] + b * mid_cap * 128
     k_prun = bf16_bits(cache.k_prun[ko: ko + n_mid * c]).reshape(n_mid, c)
-    v_mid = bf16_bits(cache.v_mid[vo: vo + n_mid * 128]).reshape(n_mid, 128)
+    vm = _v_rows(mid_cap)
+    vo = d.v_mid_off[h] + b * vm * 128
+    nv = _v_rows(n_mid)
+    v_mid = _unblock_v(bf16_bits(cache.v_mid[vo: vo + nv * 128]), n_mid)
     return ring_k, ring_v, k_prun, v_mid
 
 

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert "leank_build_mask" in names and "leank_pack_k" in names and "leank_decode_attn" in names
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.leank_abi_version() == 1
+    assert lib.leank_abi_version() == 2
     assert lib.leank_layer_cache_size() == ctypes.sizeof(_lib.LayerCacheDesc)
 
 
@@ -45,9 +45,11 @@ def test_status_strings():
 
 def test_plan_groups_heads_by_kept_count():
     kept = [32, 0, 64, 32, 128, 0, 96, 32]
-    batch, max_ctx, n_sink, window = 3, 1000, 4, 60
+    batch, max_ctx, n_sink, window = 3, 1003, 4, 61
     d = dac.leank_plan_layer(kept, batch, 16, 8, 128, n_sink, window, max_ctx)
-    mid_cap = max_ctx - n_sink - window
+    mid_cap = max_ctx - n_sink - window          # 938 rows
+    v_mid_rows = -(-mid_cap // 8) * 8            # V is stored in blocks of 8 rows: 944
+    slots = n_sink + window                      # 65 rows
     assert d.mid_capacity == mid_cap and d.n_live == 6
     order = [d.group_order[n] for n in range(8)]
     assert order == [4, 6, 2, 0, 3, 7, 1, 5]
@@ -58,9 +60,10 @@ def test_plan_groups_heads_by_kept_count():
             continue
         assert d.k_prun_off[h] == k_off and d.v_mid_off[h] == v_off
         k_off += batch * mid_cap * kept[h]
-        v_off += batch * mid_cap * 128
+        v_off += batch * v_mid_rows * 128
     assert d.k_prun_bytes == 2 * k_off and d.v_mid_bytes == 2 * v_off
-    assert d.k_sl_bytes == d.v_sl_bytes == batch * 8 * (n_sink + window) * 128 * 2
+    assert d.k_sl_bytes == batch * 8 * slots * 128 * 2
+    assert d.v_sl_bytes == batch * 8 * 72 * 128 * 2
     assert [d.kept_count[h] for h in range(8)] == kept
 
 
