@@ -43,6 +43,9 @@ __all__ = [
     "leank_workspace_init",
     "leank_decode_attn",
     "leank_decode_bytes",
+    "leank_pair_retention",
+    "leank_head_hf_ratio",
+    "leank_rank_correlation",
     "status_string",
 ]
 
@@ -224,3 +227,51 @@ def leank_decode_attn(cache, q, ctx_len=None, scale=None, out=None, workspace=No
                                      stream_handle(stream))
     check(status, "leank_decode_attn")
     return out
+
+
+# ---------------------------------------------------------------- host analysis helpers
+
+def _host_array(x, dtype):
+    import numpy as np
+
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(x, dtype=dtype)
+
+
+def leank_pair_retention(mask):
+    """Per channel-pair retention of a mask uint8 [L, H, d] -> float64 [d/2]."""
+    import numpy as np
+
+    m = _host_array(mask, np.uint8)
+    n_layers, n_heads, d = m.shape
+    out = np.zeros(d // 2, dtype=np.float64)
+    check(lib().leank_pair_retention(m.ctypes.data, n_layers, n_heads, d, out.ctypes.data),
+          "leank_pair_retention")
+    return out
+
+
+def leank_head_hf_ratio(alpha, n_hf_pairs):
+    """Per-head share of |alpha| on the n_hf_pairs highest-frequency pairs -> float64 [L, H]."""
+    import numpy as np
+
+    a = _host_array(alpha, np.float32)
+    n_layers, n_heads, d = a.shape
+    out = np.zeros((n_layers, n_heads), dtype=np.float64)
+    check(lib().leank_head_hf_ratio(a.ctypes.data, n_layers, n_heads, d, int(n_hf_pairs),
+                                    out.ctypes.data), "leank_head_hf_ratio")
+    return out
+
+
+def leank_rank_correlation(a, b):
+    """(Pearson of the values, Pearson of the ranks) of two alpha arrays."""
+    import numpy as np
+
+    x = _host_array(a, np.float32).ravel()
+    y = _host_array(b, np.float32).ravel()
+    if x.size != y.size:
+        raise ValueError("a and b differ in size")
+    pear, rank = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    check(lib().leank_rank_correlation(x.ctypes.data, y.ctypes.data, x.size, ctypes.byref(pear),
+                                       ctypes.byref(rank)), "leank_rank_correlation")
+    return pear.value, rank.value

@@ -238,6 +238,32 @@ int leank_decode_attn(const leank_layer_cache* cache, const void* q,
 int leank_decode_bytes(const leank_layer_cache* cache, int64_t ctx_len,
                        int64_t* bytes_out);
 
+/*
+ * Analysis helpers (host, synchronous, pure; host pointers).  Offline tools
+ * over alpha and masks, from the LeanK page's section 6 (which channel
+ * pairs and heads the learned importance keeps) and section 2.1 (the
+ * channel-importance ranking is stable across tasks and lengths).  Channel
+ * pair i joins channels i and i + head_dim/2 (rotate-half RoPE pairing); a
+ * lower pair index is a higher rotary frequency.
+ *
+ * leank_pair_retention -- retention_out[i], i < head_dim/2: mean over the
+ *   n_layers*n_kv_heads rows of mask (uint8 [L][H][d]) of
+ *   (kept(i) + kept(i + d/2)) / 2.
+ * leank_head_hf_ratio -- w_hf_out[l*H + h]: share of the row's |alpha| mass
+ *   on its n_hf_pairs highest-frequency pairs (0 for an all-zero row).
+ *   NaN in alpha -> LEANK_EINVAL.
+ * leank_rank_correlation -- Pearson correlation of two alpha arrays of n
+ *   values, and Pearson correlation of their ranks (equal values get the
+ *   mean of the ranks they span).  n >= 2; NaN -> LEANK_EINVAL; a constant
+ *   input gives 0.
+ */
+int leank_pair_retention(const uint8_t* mask, int32_t n_layers, int32_t n_kv_heads,
+                         int32_t head_dim, double* retention_out);
+int leank_head_hf_ratio(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
+                        int32_t head_dim, int32_t n_hf_pairs, double* w_hf_out);
+int leank_rank_correlation(const float* a, const float* b, int64_t n, double* pearson_out,
+                           double* rank_pearson_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,9 @@ __all__ = [
     "decode",
     "kv_cache_bytes",
     "decode_traffic_bytes",
+    "pair_retention",
+    "head_hf_ratio",
+    "rank_correlation",
 ]
 
 
@@ -282,3 +285,75 @@ def decode_traffic_bytes(batch, n_q_heads, n_kv_heads, head_dim, ctx_len,
     total += batch * live * n_mid * head_dim * 2                   # middle V, live heads
     total += batch * n_q_heads * head_dim * 4                      # out
     return total
+
+
+# ---------------------------------------------------------------------------
+# alpha / mask analysis (LeanK page, section 6 and section 2.1)
+
+def pair_retention(mask):
+    """Fraction of (layer, head) rows keeping each rotate-half channel pair.
+
+    LeanK page, section 6: lower pair indices (higher RoPE frequencies) are
+    kept less often.  Pair i joins channels i and i + d/2; a head counts 1
+    for a pair if both channels are kept, 1/2 if one is.
+    mask: uint8 [L, H, d]  ->  float64 [d/2].
+    """
+    mask = np.asarray(mask)
+    d = mask.shape[-1]
+    half = d // 2
+    rows = mask.reshape(-1, d).astype(np.float64)
+    per_pair = (rows[:, :half] + rows[:, half:]) / 2.0
+    return per_pair.mean(axis=0)
+
+
+def head_hf_ratio(alpha, n_hf_pairs):
+    """Share of each head's alpha mass on its n_hf_pairs highest-frequency pairs.
+
+    LeanK page, section 6 (w_hf per head).  Reading: a pair's RoPE frequency
+    falls with its index, so the highest-frequency pairs are the first
+    n_hf_pairs; w_hf = sum of |alpha| over their channels / sum over all.
+    alpha: float [L, H, d]  ->  float64 [L, H].
+    """
+    a = np.abs(np.asarray(alpha, dtype=np.float64))
+    d = a.shape[-1]
+    half = d // 2
+    hf = a[..., :n_hf_pairs].sum(axis=-1) + a[..., half:half + n_hf_pairs].sum(axis=-1)
+    total = a.sum(axis=-1)
+    return np.where(total > 0, hf / np.where(total > 0, total, 1.0), 0.0)
+
+
+def _average_ranks(x):
+    """Ranks 1..n of x, ties given the mean of the ranks they span."""
+    x = np.asarray(x, dtype=np.float64)
+    order = sorted(range(x.size), key=lambda i: x[i])
+    ranks = np.empty(x.size, dtype=np.float64)
+    i = 0
+    while i < x.size:
+        j = i
+        while j + 1 < x.size and x[order[j + 1]] == x[order[i]]:
+            j += 1
+        for k in range(i, j + 1):
+            ranks[order[k]] = (i + j) / 2.0 + 1.0
+        i = j + 1
+    return ranks
+
+
+def _pearson(x, y):
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    dx = x - x.mean()
+    dy = y - y.mean()
+    den = np.sqrt((dx * dx).sum() * (dy * dy).sum())
+    return float((dx * dy).sum() / den) if den > 0 else 0.0
+
+
+def rank_correlation(a, b):
+    """(Pearson of the values, Pearson of the average ranks) of two alphas.
+
+    LeanK page, section 2.1: the channel-importance ranking is stable across
+    tasks and lengths (a correlation near 0.98); comparing two alpha draws by
+    the correlation of their rankings measures that stability.
+    """
+    a = np.asarray(a, dtype=np.float64).ravel()
+    b = np.asarray(b, dtype=np.float64).ravel()
+    return _pearson(a, b), _pearson(_average_ranks(a), _average_ranks(b))

@@ -478,6 +478,41 @@ def pin_traffic_bytes(O):
         assert mixed == expect
 
 
+# ----------------------------------------------------------------------------
+# alpha / mask analysis
+
+def pin_analysis(O):
+    from scipy import stats
+
+    rng = np.random.default_rng(47)
+    # retention: closed forms and a hand count
+    d = 16
+    mask = np.zeros((2, 3, d), dtype=np.uint8)
+    mask[0, 0, [0, 8]] = 1          # pair 0 fully kept by one head
+    mask[1, 2, 3] = 1               # half of pair 3 in one head
+    ret = O.pair_retention(mask)
+    assert ret.shape == (8,)
+    assert ret[0] == 1.0 / 6 and ret[3] == 0.5 / 6 and ret[[1, 2, 4, 5, 6, 7]].sum() == 0
+    assert np.all(O.pair_retention(np.ones((2, 2, d), dtype=np.uint8)) == 1.0)
+    # w_hf: uniform alpha gives n_hf / (d/2); mass only on the first pair gives 1
+    a = np.ones((2, 2, 32))
+    assert np.allclose(O.head_hf_ratio(a, 4), 4 / 16)
+    b = np.zeros((1, 1, 32))
+    b[0, 0, [0, 16]] = [3.0, 1.0]
+    assert O.head_hf_ratio(b, 1)[0, 0] == 1.0 and O.head_hf_ratio(b, 0)[0, 0] == 0.0
+    # correlations against scipy, with and without ties
+    for x, y in ((rng.standard_normal(200), rng.standard_normal(200)),
+                 (rng.integers(0, 5, 300).astype(float), rng.integers(0, 5, 300).astype(float))):
+        y2 = x + 0.3 * y
+        pear, spear = O.rank_correlation(x, y2)
+        assert abs(pear - stats.pearsonr(x, y2)[0]) < 1e-12
+        assert abs(spear - stats.spearmanr(x, y2)[0]) < 1e-12
+    x = rng.standard_normal(50)
+    assert abs(O.rank_correlation(x, x)[1] - 1.0) < 1e-12
+    assert abs(O.rank_correlation(x, -x)[1] + 1.0) < 1e-12
+    assert abs(O.rank_correlation(x, np.exp(x))[1] - 1.0) < 1e-12   # monotone map keeps ranks
+
+
 ALL_PINS = [
     pin_mask_page_procedure,
     pin_mask_closed_forms,
@@ -491,4 +526,5 @@ ALL_PINS = [
     pin_decode_bruteforce,
     pin_cache_bytes,
     pin_traffic_bytes,
+    pin_analysis,
 ]

@@ -68,6 +68,15 @@ MUTANTS = [
     ("middle V counted for dead heads",
      "live = sum(1 for c in kept if c > 0)",
      "live = len(kept)"),
+    ("retention counts one channel of the pair",
+     "per_pair = (rows[:, :half] + rows[:, half:]) / 2.0",
+     "per_pair = rows[:, :half]"),
+    ("w_hf from the low-frequency end",
+     "hf = a[..., :n_hf_pairs].sum(axis=-1) + a[..., half:half + n_hf_pairs].sum(axis=-1)",
+     "hf = a[..., half - n_hf_pairs:half].sum(axis=-1) + a[..., d - n_hf_pairs:].sum(axis=-1)"),
+    ("ties ranked by position",
+     "            ranks[order[k]] = (i + j) / 2.0 + 1.0",
+     "            ranks[order[k]] = k + 1.0"),
     ("exp without the max shift, weights unnormalised",
      "put(b, j, (w @ vals) / w.sum())",
      "put(b, j, (w @ vals) / len(w))"),
