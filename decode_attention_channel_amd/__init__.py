@@ -43,6 +43,8 @@ __all__ = [
     "leank_workspace_init",
     "leank_decode_attn",
     "leank_decode_bytes",
+    "leank_pack_k_rows",
+    "leank_decode_attn_rows",
     "leank_pair_retention",
     "leank_head_hf_ratio",
     "leank_rank_correlation",
@@ -226,6 +228,61 @@ def leank_decode_attn(cache, q, ctx_len=None, scale=None, out=None, workspace=No
                                      ptr(workspace), workspace.numel() * workspace.element_size(),
                                      stream_handle(stream))
     check(status, "leank_decode_attn")
+    return out
+
+
+# ---------------------------------------------------------------- ragged batches
+
+def leank_pack_k_rows(cache, k_new, v_new, row_pos, row_count=None, stream=None):
+    """Append row_count[b] tokens of K, V bf16 [B, H_kv, n, 128] at row_pos[b] per row.
+
+    row_pos: int64 [B] on the GPU (each row's current length); row_count:
+    int32 [B] on the GPU with values in [0, n], or None for n everywhere.
+    Rows whose positions fall outside the cache are left unchanged.
+    """
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _require(t, torch.bfloat16, name, ndim=4, device=cache.device)
+        if tuple(t.shape[:2]) != (cache.batch, cache.n_kv_heads) or t.shape[3] != HEAD_DIM:
+            raise ValueError(f"{name} must be [batch, n_kv_heads, n, {HEAD_DIM}]")
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new differ in shape")
+    _require(row_pos, torch.int64, "row_pos", ndim=1, device=cache.device)
+    if row_pos.numel() != cache.batch:
+        raise ValueError("row_pos needs one entry per batch row")
+    if row_count is not None:
+        _require(row_count, torch.int32, "row_count", ndim=1, device=cache.device)
+        if row_count.numel() != cache.batch:
+            raise ValueError("row_count needs one entry per batch row")
+    status = lib().leank_pack_k_rows(_desc(cache), ptr(k_new), ptr(v_new), ptr(row_pos),
+                                     ptr(row_count), int(k_new.shape[2]), stream_handle(stream))
+    check(status, "leank_pack_k_rows")
+
+
+def leank_decode_attn_rows(cache, q, ctx_lens, max_ctx_len=None, scale=None, out=None,
+                           workspace=None, stream=None):
+    """Decode attention with row b over its first ctx_lens[b] tokens (int32 [B] on the GPU).
+
+    max_ctx_len bounds every entry of ctx_lens (default: the cache capacity).
+    """
+    if max_ctx_len is None:
+        max_ctx_len = cache.max_ctx
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    _require(q, torch.bfloat16, "q", ndim=3, device=cache.device)
+    if tuple(q.shape) != (cache.batch, cache.n_q_heads, HEAD_DIM):
+        raise ValueError("q must be [batch, n_q_heads, 128]")
+    _require(ctx_lens, torch.int32, "ctx_lens", ndim=1, device=cache.device)
+    if ctx_lens.numel() != cache.batch:
+        raise ValueError("ctx_lens needs one entry per batch row")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = cache.workspace()
+    status = lib().leank_decode_attn_rows(_desc(cache), ptr(q), ptr(ctx_lens), int(max_ctx_len),
+                                          float(scale), ptr(out), ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          stream_handle(stream))
+    check(status, "leank_decode_attn_rows")
     return out
 
 

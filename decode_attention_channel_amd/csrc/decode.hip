@@ -40,9 +40,11 @@ extern "C" int leank_workspace_init(void* workspace, size_t workspace_bytes, voi
   return LEANK_OK;
 }
 
-extern "C" int leank_decode_attn(const leank_layer_cache* c, const void* q, int64_t ctx_len,
-                                 float scale, float* out, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+namespace {
+
+int decode_impl(const leank_layer_cache* c, const void* q, const int32_t* ctx_lens,
+                int64_t ctx_len, float scale, float* out, void* workspace,
+                size_t workspace_bytes, void* stream) {
   int st = validate_cache(c, true);
   if (st != LEANK_OK) return st;
   if (!q || !out || !aligned16(q) || !aligned16(out)) return LEANK_EINVAL;
@@ -64,6 +66,8 @@ extern "C" int leank_decode_attn(const leank_layer_cache* c, const void* q, int6
   p.v_mid = static_cast<const uint16_t*>(c->v_mid);
   p.kept_idx = c->kept_idx;
   p.out = out;
+  p.ctx_lens = ctx_lens;
+  p.max_len = static_cast<int32_t>(ctx_len);
   p.partials = static_cast<float*>(workspace);
   p.mid_cap = c->mid_capacity;
   p.v_mid_rows = v_rows(c->mid_capacity);
@@ -103,4 +107,20 @@ extern "C" int leank_decode_attn(const leank_layer_cache* c, const void* q, int6
     case 8: return launch_decode<8>(p, w.n_items, n_pairs, s);
     default: return LEANK_EUNSUPPORTED;
   }
+}
+
+}  // namespace
+
+extern "C" int leank_decode_attn(const leank_layer_cache* c, const void* q, int64_t ctx_len,
+                                 float scale, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return decode_impl(c, q, nullptr, ctx_len, scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int leank_decode_attn_rows(const leank_layer_cache* c, const void* q,
+                                      const int32_t* ctx_lens, int64_t max_ctx_len, float scale,
+                                      float* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!ctx_lens) return LEANK_EINVAL;
+  return decode_impl(c, q, ctx_lens, max_ctx_len, scale, out, workspace, workspace_bytes, stream);
 }

@@ -89,11 +89,13 @@ struct DecodeParams {
   const int16_t* kept_idx;
   float* out;
   float* partials;
+  const int32_t* ctx_lens;  // per-row context lengths (ragged batches), or null
   int64_t mid_cap;
   int64_t v_mid_rows;  // stored V rows per batch row of a middle segment
   int64_t v_sl_rows;   // stored V rows per (batch row, head) of the ring
   int32_t n_kv;
   int32_t n_q;
+  int32_t max_len;  // context length the work plan was made for
   int32_t slots;
   int32_t t_sl;
   int32_t t_mid;
@@ -372,9 +374,15 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   for (int n = 0; n < 8; ++n) st.o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   uint16_t* p_lds = s_p[wave];
 
+  int t_sl = p.t_sl, t_mid = p.t_mid;
+  if (p.ctx_lens) {  // ragged batch: this row may hold fewer tokens than the plan
+    const int len = min(max(p.ctx_lens[b], 0), p.max_len);
+    t_sl = min(len, p.slots);
+    t_mid = max(0, len - p.slots);
+  }
   if (!middle) {
     const int r0 = local * p.sl_rows;
-    const int r1 = min(p.t_sl, r0 + p.sl_rows);
+    const int r1 = min(t_sl, r0 + p.sl_rows);
     const int64_t pair = static_cast<int64_t>(b) * p.n_kv + h;
     const uint16_t* kb = p.k_sl + pair * p.slots * LEANK_HEAD_DIM;
     const uint16_t* vb = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM;
@@ -384,7 +392,7 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   } else {
     const int chunk_id = local - p.n_sl_items;
     const int r0 = chunk_id * hd.mid_rows;
-    const int r1 = min(p.t_mid, r0 + hd.mid_rows);
+    const int r1 = min(t_mid, r0 + hd.mid_rows);
     const int c = hd.kept;
     const uint16_t* kb = p.k_prun + hd.k_off + static_cast<int64_t>(b) * p.mid_cap * c;
     const uint16_t* vb = p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM;
@@ -548,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodePa
       o.w += x.w;
       total += s_sum[j * quads + t];
     }
-    const float inv = 1.0f / total;
+    const float inv = total > 0.0f ? 1.0f / total : 0.0f;  // an empty row gives zeros
     float* out = p.out + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM + ch;
     *reinterpret_cast<float4*>(out) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
   }

@@ -43,6 +43,9 @@ struct PackParams {
   int64_t unit_lo;     // kMigrate: position of unit 0
   int64_t units_per_pair;
   int64_t n_units;
+  int64_t max_ctx;
+  const int64_t* row_pos;    // per-row append position (ragged batches), or null
+  const int32_t* row_count;  // per-row token count (ragged batches), or null = n_new
   int32_t n_kv;
   int32_t n_sink;
   int32_t window;
@@ -96,8 +99,19 @@ __global__ __launch_bounds__(64 * kUnitsPerBlock) void pack_kernel(const PackPar
   uint32_t* ring_k = p.k_sl + (pair * p.slots) * kWordsPerRow;
   uint16_t* ring_v = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM;
 
+  int64_t t_old = p.t_old, t_new = p.t_new;
+  if (p.row_pos) {
+    t_old = p.row_pos[b];
+    const int64_t cnt = p.row_count ? p.row_count[b] : p.n_new;
+    // a row whose positions fall outside the cache is left untouched
+    if (t_old < 0 || cnt < 0 || cnt > p.n_new || t_old + cnt > p.max_ctx) return;
+    t_new = t_old + cnt;
+  }
+
   if (p.mode == kMigrate) {
-    const int64_t q = p.unit_lo + i;
+    const int64_t lo = max(static_cast<int64_t>(p.n_sink), t_old - p.window);
+    const int64_t q = (p.row_pos ? lo : p.unit_lo) + i;
+    if (q >= min(t_old, t_new - p.window)) return;  // this row moves fewer tokens
     const int64_t slot = p.n_sink + (q - p.n_sink) % p.window;
     const uint32_t kw = ring_k[slot * kWordsPerRow + lane];
     const uint32_t vw = load_v_row_word(ring_v, slot, lane);
@@ -105,7 +119,8 @@ __global__ __launch_bounds__(64 * kUnitsPerBlock) void pack_kernel(const PackPar
     return;
   }
 
-  const int64_t pos = p.t_old + i;
+  if (i >= t_new - t_old) return;  // this row appends fewer tokens
+  const int64_t pos = t_old + i;
   const int64_t src = (pair * p.n_new + i) * kWordsPerRow + lane;
   const uint32_t kw = p.k_new[src];
   const uint32_t vw = p.v_new[src];
@@ -114,7 +129,7 @@ __global__ __launch_bounds__(64 * kUnitsPerBlock) void pack_kernel(const PackPar
     store_v_row_word(ring_v, pos, lane, vw);
     return;
   }
-  if (p.mode == kPlace && pos < p.t_new - p.window) {
+  if (p.mode == kPlace && pos < t_new - p.window) {
     write_middle(p, b, h, pos - p.n_sink, kw, vw, lane);  // already outside the window
     return;
   }
@@ -147,6 +162,37 @@ int launch(PackParams& p, int64_t units_per_pair, int64_t pairs, hipStream_t s) 
 
 using namespace leank;
 
+namespace {
+
+int fill_params(const leank_layer_cache* c, const void* k_new, const void* v_new, int64_t n_new,
+                PackParams* p) {
+  memset(p, 0, sizeof(*p));
+  p->k_new = static_cast<const uint32_t*>(k_new);
+  p->v_new = static_cast<const uint32_t*>(v_new);
+  p->k_sl = static_cast<uint32_t*>(c->k_sl);
+  p->v_sl = static_cast<uint16_t*>(c->v_sl);
+  p->k_prun = static_cast<uint32_t*>(c->k_prun);
+  p->v_mid = static_cast<uint16_t*>(c->v_mid);
+  p->kept_idx = c->kept_idx;
+  p->n_new = n_new;
+  p->mid_cap = c->mid_capacity;
+  p->v_mid_rows = v_rows(c->mid_capacity);
+  p->v_sl_rows = v_rows(static_cast<int64_t>(c->n_sink) + c->window);
+  p->max_ctx = c->max_ctx;
+  p->n_kv = c->n_kv_heads;
+  p->n_sink = c->n_sink;
+  p->window = c->window;
+  p->slots = c->n_sink + c->window;
+  for (int h = 0; h < c->n_kv_heads; ++h) {
+    p->heads[h].k_off = c->k_prun_off[h];
+    p->heads[h].v_off = c->v_mid_off[h];
+    p->heads[h].kept = c->kept_count[h];
+  }
+  return LEANK_OK;
+}
+
+}  // namespace
+
 extern "C" int leank_pack_k(const leank_layer_cache* c, const void* k_new, const void* v_new,
                             int64_t pos0, int64_t n_new, void* stream) {
   int st = validate_cache(c, true);
@@ -157,29 +203,9 @@ extern "C" int leank_pack_k(const leank_layer_cache* c, const void* k_new, const
   if (pos0 + n_new > c->max_ctx) return LEANK_ECAPACITY;
 
   PackParams p;
-  memset(&p, 0, sizeof(p));
-  p.k_new = static_cast<const uint32_t*>(k_new);
-  p.v_new = static_cast<const uint32_t*>(v_new);
-  p.k_sl = static_cast<uint32_t*>(c->k_sl);
-  p.v_sl = static_cast<uint16_t*>(c->v_sl);
-  p.k_prun = static_cast<uint32_t*>(c->k_prun);
-  p.v_mid = static_cast<uint16_t*>(c->v_mid);
-  p.kept_idx = c->kept_idx;
+  fill_params(c, k_new, v_new, n_new, &p);
   p.t_old = pos0;
   p.t_new = pos0 + n_new;
-  p.n_new = n_new;
-  p.mid_cap = c->mid_capacity;
-  p.v_mid_rows = v_rows(c->mid_capacity);
-  p.v_sl_rows = v_rows(static_cast<int64_t>(c->n_sink) + c->window);
-  p.n_kv = c->n_kv_heads;
-  p.n_sink = c->n_sink;
-  p.window = c->window;
-  p.slots = c->n_sink + c->window;
-  for (int h = 0; h < c->n_kv_heads; ++h) {
-    p.heads[h].k_off = c->k_prun_off[h];
-    p.heads[h].v_off = c->v_mid_off[h];
-    p.heads[h].kept = c->kept_count[h];
-  }
   const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -200,5 +226,34 @@ extern "C" int leank_pack_k(const leank_layer_cache* c, const void* k_new, const
   }
   p.mode = kPlace;
   p.unit_lo = 0;
+  return launch(p, n_new, pairs, s);
+}
+
+extern "C" int leank_pack_k_rows(const leank_layer_cache* c, const void* k_new, const void* v_new,
+                                 const int64_t* row_pos, const int32_t* row_count, int64_t n_new,
+                                 void* stream) {
+  int st = validate_cache(c, true);
+  if (st != LEANK_OK) return st;
+  if (n_new < 0 || !row_pos) return LEANK_EINVAL;
+  if (n_new == 0) return LEANK_OK;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return LEANK_EINVAL;
+  if (n_new > c->max_ctx) return LEANK_ECAPACITY;
+
+  PackParams p;
+  fill_params(c, k_new, v_new, n_new, &p);
+  p.row_pos = row_pos;
+  p.row_count = row_count;
+  const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c->window > 0 && n_new <= c->window) {
+    p.mode = kFused;
+    return launch(p, n_new, pairs, s);
+  }
+  if (c->window > 0) {
+    p.mode = kMigrate;
+    st = launch(p, std::min<int64_t>(c->window, n_new), pairs, s);
+    if (st != LEANK_OK) return st;
+  }
+  p.mode = kPlace;
   return launch(p, n_new, pairs, s);
 }

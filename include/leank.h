@@ -230,6 +230,31 @@ int leank_decode_attn(const leank_layer_cache* cache, const void* q,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Ragged batches (rows at different context lengths).
+ *
+ * leank_pack_k_rows -- like leank_pack_k, but batch row b appends
+ *   row_count[b] tokens (tokens [0, row_count[b]) of its slice of k_new /
+ *   v_new, bf16 [batch][n_kv_heads][n_new][128]) at positions
+ *   [row_pos[b], row_pos[b] + row_count[b]).  row_pos: device int64
+ *   [batch], the row's current length; row_count: device int32 [batch]
+ *   with values in [0, n_new], or NULL for n_new everywhere.  The arrays
+ *   are read on the device, so they are not validated on the host: a row
+ *   whose positions fall outside [0, max_ctx] is left unchanged.  One
+ *   kernel when n_new <= window, two otherwise; asynchronous on `stream`.
+ *
+ * leank_decode_attn_rows -- like leank_decode_attn, with batch row b
+ *   attending over its first ctx_lens[b] tokens (device int32 [batch],
+ *   values clamped to [0, max_ctx_len]); max_ctx_len (1..max_ctx) sizes the
+ *   work plan and the workspace.  A row of length 0 gets a zero output.
+ */
+int leank_pack_k_rows(const leank_layer_cache* cache, const void* k_new, const void* v_new,
+                      const int64_t* row_pos, const int32_t* row_count, int64_t n_new,
+                      void* stream);
+int leank_decode_attn_rows(const leank_layer_cache* cache, const void* q,
+                           const int32_t* ctx_lens, int64_t max_ctx_len, float scale,
+                           float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * leank_decode_bytes -- host.  Algorithmic HBM bytes of one
  * leank_decode_attn call: q (bf16) + full-width K and V of every head +
  * kept K channels and V of live heads over the middle + out (float32).
