@@ -6,17 +6,18 @@ head_dim 128, batch 64, context 4096 (64 sink tokens, 512-token window),
 LogNormal(0, 0.5) K channel scales.
 
 A step is what a generation loop does per layer: append the new token's K/V
-(leank_pack_k, which also moves the token leaving the window into the
-pruned middle) and run decode attention over the whole cache
-(leank_decode_attn).  Each step appends one token, so the context grows by
-one per step on each cache copy; copies rotate so that consecutive steps
-read different HBM data (the copies together exceed the 256 MB Infinity
-Cache many times over).
+(the token leaving the window moves into the pruned middle) and run decode
+attention over the whole cache, here as one leank_decode_step call (the
+append runs inside the two decode kernels).  Each step appends one token,
+so the context grows by one per step on each cache copy; copies rotate so
+that consecutive steps read different HBM data (the copies together exceed
+the 256 MB Infinity Cache many times over).
 
-Reported on one JSON line: microseconds per step (value), the decode
-kernel's roofline figures from HIP events on the launch stream, the same
-kernel at 0% pruning, the Qwen2.5-7B-shaped cache, and the CPU oracle's time
-for the same step (a baseline, not a target).
+Reported on one JSON line: microseconds per step (value), the step's
+roofline figures from HIP events on the launch stream, the same step as two
+calls (leank_pack_k, then leank_decode_attn), the same kernels at 0%
+pruning, the Qwen2.5-7B-shaped cache, and the CPU oracle's time for the
+same step (a baseline, not a target).
 """
 
 import argparse
@@ -64,8 +65,10 @@ def setup_caches(cfg, mask_counts, kept_idx_dev, k, v, copies, max_ctx):
     return caches
 
 
-def run_steps(cfg, caches, q, new_k, new_v, steps, warmup):
-    """Warm-up, then `steps` timed (append + decode) steps.  Returns timings."""
+def run_steps(cfg, caches, q, new_k, new_v, steps, warmup, fused=True):
+    """Warm-up, then `steps` timed (append + decode) steps: one
+    leank_decode_step call each (fused) or leank_pack_k + leank_decode_attn.
+    Returns timings."""
     import torch
 
     import decode_attention_channel_amd as dac
@@ -80,12 +83,18 @@ def run_steps(cfg, caches, q, new_k, new_v, steps, warmup):
         vv = new_v[idx % new_v.shape[0]]
         if events is not None:
             events[0].record(stream)
-        dac.leank_pack_k(cache, kk, vv)
-        if events is not None:
-            events[1].record(stream)
-        dac.leank_decode_attn(cache, q, out=outs[idx % n])
-        if events is not None:
-            events[2].record(stream)
+        if fused:
+            dac.leank_decode_step(cache, q, kk, vv, out=outs[idx % n])
+            if events is not None:
+                events[1].record(stream)
+                events[2].record(stream)
+        else:
+            dac.leank_pack_k(cache, kk, vv)
+            if events is not None:
+                events[1].record(stream)
+            dac.leank_decode_attn(cache, q, out=outs[idx % n])
+            if events is not None:
+                events[2].record(stream)
         return cache.length
 
     for idx in range(warmup):
@@ -105,8 +114,9 @@ def run_steps(cfg, caches, q, new_k, new_v, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_begin.elapsed_time(t_end)
-    append_us = [ev[s][0].elapsed_time(ev[s][1]) * 1e3 for s in range(steps)]
-    decode_us = [ev[s][1].elapsed_time(ev[s][2]) * 1e3 for s in range(steps)]
+    # fused: the whole step is one launch (ev 0 -> 2); unfused: append, then decode
+    append_us = [ev[s][0].elapsed_time(ev[s][1]) * 1e3 for s in range(steps)] if not fused else []
+    decode_us = [ev[s][0 if fused else 1].elapsed_time(ev[s][2]) * 1e3 for s in range(steps)]
     bytes_per = [dac.leank_decode_bytes(caches[(warmup + s) % n], ctxs[s]) for s in range(steps)]
     return {
         "total_ms": total_ms,
@@ -119,6 +129,8 @@ def run_steps(cfg, caches, q, new_k, new_v, steps, warmup):
 
 
 def summarize(t):
+    """decode_us_*: the attention launch -- the whole leank_decode_step call
+    in a fused step, the leank_decode_attn call in an unfused one."""
     import numpy as np
 
     d = np.asarray(t["decode_us"])
@@ -131,7 +143,7 @@ def summarize(t):
         "decode_us_p10": float(np.percentile(d, 10)),
         "decode_us_p50": float(np.percentile(d, 50)),
         "decode_us_p90": float(np.percentile(d, 90)),
-        "append_us_mean": float(np.mean(t["append_us"])),
+        "append_us_mean": float(np.mean(t["append_us"])) if t["append_us"] else None,
         "decode_bytes_mean": byt,
         "achieved_GBps": gbps,
         "frac_of_peak": gbps / HBM_PEAK_GBPS,
@@ -140,7 +152,7 @@ def summarize(t):
     }
 
 
-def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20):
+def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20, fused=True):
     """Prepare one workload and time it.  prune_override=0 keeps every channel."""
     import numpy as np
     import torch
@@ -162,7 +174,7 @@ def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20):
     max_ctx = cfg.ctx + (steps + warmup) // copies + 2
     caches = setup_caches(cfg, counts, kept_idx[0].contiguous(), k, v, copies, max_ctx)
     torch.cuda.synchronize()
-    timings = run_steps(cfg, caches, q, new_k, new_v, steps, warmup)
+    timings = run_steps(cfg, caches, q, new_k, new_v, steps, warmup, fused=fused)
     res = summarize(timings)
     res["kept_count"] = counts
     res["dead_heads"] = int(sum(1 for c in counts if c == 0))
@@ -295,6 +307,8 @@ def main():
     main_res = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup)
     extras = {}
     if not args.skip_extras:
+        unfused = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup,
+                           fused=False)
         dense = workload(cfg, prune_override=0, copies=args.copies, steps=args.steps,
                          warmup=args.warmup)
         qwen_cfg = get_config("qwen_b16_32k")
@@ -302,6 +316,7 @@ def main():
         qwen_dense = workload(qwen_cfg, prune_override=0, copies=max(2, args.copies // 2),
                               steps=args.steps, warmup=args.warmup)
         extras = {
+            "unfused_pack_then_decode": unfused,
             "dense_0pct": dense,
             "speedup_vs_0pct_decode": dense["decode_us_mean"] / main_res["decode_us_mean"],
             "speedup_vs_0pct_step": dense["us_per_step"] / main_res["us_per_step"],
@@ -341,12 +356,12 @@ def main():
             "window": cfg.window,
             "prune_pct": cfg.prune_pct,
             "align": cfg.align,
-            "step": "leank_pack_k (1 token) + leank_decode_attn",
+            "step": "leank_decode_step (append 1 token + decode attention, fused)",
             "cache_copies": args.copies,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "leank_decode_attn = decode_split_kernel<4> + decode_combine_kernel<4>",
+            "kernel": "leank_decode_step = decode_split_kernel<4> + decode_combine_kernel<4>",
             "achieved": main_res["achieved_GBps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

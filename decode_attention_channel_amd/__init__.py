@@ -11,6 +11,7 @@ streams only; every step runs in the library's HIP kernels.
     leank_pack_k(cache, k_prefill, v_prefill)        # appends, tracks length
     leank_pack_k(cache, k_step, v_step)              # one decode step's token
     out = leank_decode_attn(cache, q)                # float32 [B, Hq, 128]
+    out = leank_decode_step(cache, q, k_tok, v_tok)  # append + attend, fused
 """
 
 import ctypes
@@ -45,6 +46,8 @@ __all__ = [
     "leank_decode_bytes",
     "leank_pack_k_rows",
     "leank_decode_attn_rows",
+    "leank_decode_step",
+    "leank_decode_step_rows",
     "leank_pair_retention",
     "leank_head_hf_ratio",
     "leank_rank_correlation",
@@ -283,6 +286,74 @@ def leank_decode_attn_rows(cache, q, ctx_lens, max_ctx_len=None, scale=None, out
                                           workspace.numel() * workspace.element_size(),
                                           stream_handle(stream))
     check(status, "leank_decode_attn_rows")
+    return out
+
+
+# ---------------------------------------------------------------- fused decode step
+
+def _step_token(cache, t, name):
+    _require(t, torch.bfloat16, name, device=cache.device)
+    shape = tuple(t.shape)
+    if shape not in ((cache.batch, cache.n_kv_heads, HEAD_DIM),
+                     (cache.batch, cache.n_kv_heads, 1, HEAD_DIM)):
+        raise ValueError(f"{name} must be [batch, n_kv_heads, 128] (or with a length-1 token axis)")
+
+
+def _step_common(cache, q, k_new, v_new, scale, out, workspace):
+    _require(q, torch.bfloat16, "q", ndim=3, device=cache.device)
+    if tuple(q.shape) != (cache.batch, cache.n_q_heads, HEAD_DIM):
+        raise ValueError("q must be [batch, n_q_heads, 128]")
+    _step_token(cache, k_new, "k_new")
+    _step_token(cache, v_new, "v_new")
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    else:
+        _require(out, torch.float32, "out", ndim=3, device=cache.device)
+        if out.shape != q.shape:
+            raise ValueError("out must match q's shape")
+    if workspace is None:
+        workspace = cache.workspace()
+    return scale, out, workspace
+
+
+def leank_decode_step(cache, q, k_new, v_new, pos=None, scale=None, out=None, workspace=None,
+                      stream=None):
+    """Append one token per row (K, V bf16 [B, H_kv, 128]) at pos (default:
+    cache.length) and return q's attention over the pos + 1 tokens, float32
+    [B, Hq, 128] -- the result of leank_pack_k then leank_decode_attn, in
+    the two decode kernels."""
+    if pos is None:
+        pos = cache.length
+    scale, out, workspace = _step_common(cache, q, k_new, v_new, scale, out, workspace)
+    status = lib().leank_decode_step(_desc(cache), ptr(q), ptr(k_new), ptr(v_new), int(pos),
+                                     float(scale), ptr(out), ptr(workspace),
+                                     workspace.numel() * workspace.element_size(),
+                                     stream_handle(stream))
+    check(status, "leank_decode_step")
+    cache.length = int(pos) + 1
+    return out
+
+
+def leank_decode_step_rows(cache, q, k_new, v_new, row_pos, max_ctx_len=None, scale=None,
+                           out=None, workspace=None, stream=None):
+    """Fused step with row b appending at row_pos[b] (int64 [B] on the GPU)
+    and attending over row_pos[b] + 1 tokens; max_ctx_len bounds
+    row_pos[b] + 1 (default: the cache capacity).  A row outside that range
+    is left unchanged and gets zeros."""
+    if max_ctx_len is None:
+        max_ctx_len = cache.max_ctx
+    scale, out, workspace = _step_common(cache, q, k_new, v_new, scale, out, workspace)
+    _require(row_pos, torch.int64, "row_pos", ndim=1, device=cache.device)
+    if row_pos.numel() != cache.batch:
+        raise ValueError("row_pos needs one entry per batch row")
+    status = lib().leank_decode_step_rows(_desc(cache), ptr(q), ptr(k_new), ptr(v_new),
+                                          ptr(row_pos), int(max_ctx_len), float(scale), ptr(out),
+                                          ptr(workspace),
+                                          workspace.numel() * workspace.element_size(),
+                                          stream_handle(stream))
+    check(status, "leank_decode_step_rows")
     return out
 
 

@@ -90,6 +90,14 @@ _SIGNATURES = {
                                               ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                               ctypes.c_void_p]),
+    "leank_decode_step": (ctypes.c_int, [ctypes.POINTER(LayerCacheDesc), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]),
+    "leank_decode_step_rows": (ctypes.c_int, [ctypes.POINTER(LayerCacheDesc), ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "leank_pair_retention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_void_p]),
     "leank_head_hf_ratio": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,

@@ -37,7 +37,9 @@ __host__ __device__ inline int64_t v_elem(int64_t r, int ch) {
 // Decomposition of one decode call into work items.  Every (batch row,
 // KV head) pair owns n_sl_items items over its full-width rows followed by
 // n_mid[h] items over its middle rows; the pairs of one batch row are laid
-// out head by head, and batch rows follow each other.
+// out head by head, and batch rows follow each other.  In a fused decode
+// step, full-width item 0 of each pair also carries the append (so a step
+// has at least one full-width item per pair, even over no cached rows).
 struct WorkPlan {
   int32_t group;          // query heads per KV head
   int32_t t_sl;           // valid full-width rows: min(ctx, n_sink + window)
@@ -46,6 +48,7 @@ struct WorkPlan {
   int32_t sl_rows;        // rows per full-width item
   int32_t n_mid[LEANK_MAX_KV_HEADS];
   int32_t mid_rows[LEANK_MAX_KV_HEADS];
+  int32_t step;           // 1 for a fused decode step
   int32_t head_base[LEANK_MAX_KV_HEADS + 1];  // first item of head h within a batch row
   int32_t items_per_b;
   int64_t n_items;
@@ -55,7 +58,8 @@ struct WorkPlan {
 };
 
 int validate_cache(const leank_layer_cache* c, bool need_buffers);
-int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, WorkPlan* plan);
+// ctx_len: cached rows the items cover (0 allowed in a step, step = 1).
+int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPlan* plan);
 
 // ---------------------------------------------------------------- device side
 
@@ -83,6 +87,31 @@ template <int kCtrl>
 __device__ __forceinline__ float dpp_f32(float x) {
   // every pattern used here reads a valid lane, so no "old" value is needed
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
+
+// One lane's word (channels 2 lane, 2 lane + 1) of row r of a V region
+// stored in blocks of LEANK_V_BLOCK rows.
+__device__ __forceinline__ uint32_t load_v_row_word(const uint16_t* region, int64_t r, int lane) {
+  const uint32_t lo = region[v_elem(r, 2 * lane)];
+  const uint32_t hi = region[v_elem(r, 2 * lane + 1)];
+  return lo | (hi << 16);
+}
+__device__ __forceinline__ void store_v_row_word(uint16_t* region, int64_t r, int lane, uint32_t w) {
+  region[v_elem(r, 2 * lane)] = static_cast<uint16_t>(w & 0xffffu);
+  region[v_elem(r, 2 * lane + 1)] = static_cast<uint16_t>(w >> 16);
+}
+
+// Word `lane` of a token's compacted K row (kept channels j = 2 lane,
+// 2 lane + 1 of the head) from its full row, whose channels 2 m, 2 m + 1
+// are held by lane m in `full`.  c0, c1 are the kept channel ids (any
+// value in [0, 128) when 2 lane >= kept).  Every lane of the wavefront must
+// call it (cross-lane reads).
+__device__ __forceinline__ uint32_t compact_k_word(uint32_t full, int c0, int c1) {
+  const uint32_t w0 = static_cast<uint32_t>(__shfl(static_cast<int>(full), c0 >> 1));
+  const uint32_t w1 = static_cast<uint32_t>(__shfl(static_cast<int>(full), c1 >> 1));
+  const uint32_t lo = (c0 & 1) ? (w0 >> 16) : (w0 & 0xffffu);
+  const uint32_t hi = (c1 & 1) ? (w1 >> 16) : (w1 & 0xffffu);
+  return lo | (hi << 16);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -1,7 +1,8 @@
-// Host entry points of the decode path: leank_decode_attn (argument checks,
-// work plan, dispatch on the group size) and leank_workspace_init.  The
-// kernels live in decode_kernels.h, instantiated per group size in
-// decode_g1.hip .. decode_g8.hip.
+// Host entry points of the decode path: leank_decode_attn and its ragged
+// form, the fused decode step (append + attention in the same two kernels)
+// and its ragged form, and leank_workspace_init.  The kernels live in
+// decode_kernels.h, instantiated per group size in decode_g1.hip ..
+// decode_g8.hip.
 
 #include "decode_kernels.h"
 
@@ -42,17 +43,34 @@ extern "C" int leank_workspace_init(void* workspace, size_t workspace_bytes, voi
 
 namespace {
 
-int decode_impl(const leank_layer_cache* c, const void* q, const int32_t* ctx_lens,
-                int64_t ctx_len, float scale, float* out, void* workspace,
-                size_t workspace_bytes, void* stream) {
+// What a call adds to plain decode attention over the cached rows.
+struct CallExtras {
+  const int32_t* ctx_lens = nullptr;  // ragged decode: per-row lengths
+  bool step = false;                  // fused step: append one token, then attend
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int64_t* row_pos = nullptr;   // ragged step: per-row positions
+};
+
+// plan_len: rows the regular items cover -- the context length of a decode
+// call, the rows cached before the append in a step (whose context is one
+// more).
+int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, int64_t plan_len,
+                float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
   int st = validate_cache(c, true);
   if (st != LEANK_OK) return st;
   if (!q || !out || !aligned16(q) || !aligned16(out)) return LEANK_EINVAL;
-  if (ctx_len < 1) return LEANK_EINVAL;
-  if (ctx_len > c->max_ctx) return LEANK_ECAPACITY;
+  if (x.step) {
+    if (!x.k_new || !x.v_new || !aligned16(x.k_new) || !aligned16(x.v_new)) return LEANK_EINVAL;
+    if (plan_len < 0) return LEANK_EINVAL;
+    if (plan_len + 1 > c->max_ctx) return LEANK_ECAPACITY;
+  } else {
+    if (plan_len < 1) return LEANK_EINVAL;
+    if (plan_len > c->max_ctx) return LEANK_ECAPACITY;
+  }
   if (!(scale > 0.0f) || !isfinite(scale)) return LEANK_EINVAL;
   WorkPlan w;
-  make_work_plan(c, ctx_len, &w);
+  make_work_plan(c, plan_len, x.step ? 1 : 0, &w);
   if (!workspace || !aligned16(workspace) || workspace_bytes < w.workspace_bytes)
     return LEANK_EWORKSPACE;
   if (w.n_items > INT32_MAX) return LEANK_EUNSUPPORTED;
@@ -66,8 +84,15 @@ int decode_impl(const leank_layer_cache* c, const void* q, const int32_t* ctx_le
   p.v_mid = static_cast<const uint16_t*>(c->v_mid);
   p.kept_idx = c->kept_idx;
   p.out = out;
-  p.ctx_lens = ctx_lens;
-  p.max_len = static_cast<int32_t>(ctx_len);
+  p.ctx_lens = x.ctx_lens;
+  p.k_new = static_cast<const uint16_t*>(x.k_new);
+  p.v_new = static_cast<const uint16_t*>(x.v_new);
+  p.row_pos = x.row_pos;
+  p.step_pos = plan_len;
+  p.step = w.step;
+  p.n_sink = c->n_sink;
+  p.window = c->window;
+  p.max_len = static_cast<int32_t>(plan_len);
   p.partials = static_cast<float*>(workspace);
   p.mid_cap = c->mid_capacity;
   p.v_mid_rows = v_rows(c->mid_capacity);
@@ -83,7 +108,8 @@ int decode_impl(const leank_layer_cache* c, const void* q, const int32_t* ctx_le
   p.partial_stride = w.partial_stride;
   // pairs with many items get their channels split over several combine workgroups
   int32_t max_items = 0;
-  for (int h = 0; h < c->n_kv_heads; ++h) max_items = std::max(max_items, w.n_sl_items + w.n_mid[h]);
+  for (int h = 0; h < c->n_kv_heads; ++h)
+    max_items = std::max(max_items, w.n_sl_items + w.n_mid[h]);
   p.combine_slices = max_items > 256 ? 8 : max_items > 64 ? 4 : max_items > 16 ? 2 : 1;
   p.qk_scale = scale * kLog2e;
   for (int h = 0; h < c->n_kv_heads; ++h) {
@@ -114,7 +140,7 @@ int decode_impl(const leank_layer_cache* c, const void* q, const int32_t* ctx_le
 extern "C" int leank_decode_attn(const leank_layer_cache* c, const void* q, int64_t ctx_len,
                                  float scale, float* out, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  return decode_impl(c, q, nullptr, ctx_len, scale, out, workspace, workspace_bytes, stream);
+  return decode_impl(c, q, CallExtras{}, ctx_len, scale, out, workspace, workspace_bytes, stream);
 }
 
 extern "C" int leank_decode_attn_rows(const leank_layer_cache* c, const void* q,
@@ -122,5 +148,31 @@ extern "C" int leank_decode_attn_rows(const leank_layer_cache* c, const void* q,
                                       float* out, void* workspace, size_t workspace_bytes,
                                       void* stream) {
   if (!ctx_lens) return LEANK_EINVAL;
-  return decode_impl(c, q, ctx_lens, max_ctx_len, scale, out, workspace, workspace_bytes, stream);
+  CallExtras x;
+  x.ctx_lens = ctx_lens;
+  return decode_impl(c, q, x, max_ctx_len, scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int leank_decode_step(const leank_layer_cache* c, const void* q, const void* k_new,
+                                 const void* v_new, int64_t pos, float scale, float* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  CallExtras x;
+  x.step = true;
+  x.k_new = k_new;
+  x.v_new = v_new;
+  return decode_impl(c, q, x, pos, scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int leank_decode_step_rows(const leank_layer_cache* c, const void* q,
+                                      const void* k_new, const void* v_new,
+                                      const int64_t* row_pos, int64_t max_ctx_len, float scale,
+                                      float* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!row_pos || max_ctx_len < 1) return LEANK_EINVAL;
+  CallExtras x;
+  x.step = true;
+  x.k_new = k_new;
+  x.v_new = v_new;
+  x.row_pos = row_pos;
+  return decode_impl(c, q, x, max_ctx_len - 1, scale, out, workspace, workspace_bytes, stream);
 }

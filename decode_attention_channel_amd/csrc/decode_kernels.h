@@ -90,12 +90,21 @@ struct DecodeParams {
   float* out;
   float* partials;
   const int32_t* ctx_lens;  // per-row context lengths (ragged batches), or null
+  // fused decode step: the appended token's K and V [B][H_kv][128], and its
+  // position per row (row_pos, ragged) or for every row (step_pos)
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int64_t* row_pos;
+  int64_t step_pos;
   int64_t mid_cap;
   int64_t v_mid_rows;  // stored V rows per batch row of a middle segment
   int64_t v_sl_rows;   // stored V rows per (batch row, head) of the ring
   int32_t n_kv;
   int32_t n_q;
-  int32_t max_len;  // context length the work plan was made for
+  int32_t max_len;  // context length the work plan was made for (rows before the append in a step)
+  int32_t step;     // 1 in a fused decode step: full-width item 0 of each pair carries the append
+  int32_t n_sink;
+  int32_t window;
   int32_t slots;
   int32_t t_sl;
   int32_t t_mid;
@@ -185,9 +194,12 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ kb, int k
     tr.vf[n] = v_ok ? load_stream16(vt + n * 16 * 8) : u32x4_t{0u, 0u, 0u, 0u};
 }
 
-// Scores, softmax bookkeeping and weighted V of one loaded tile.
+// Scores, softmax bookkeeping and weighted V of one loaded tile.  The
+// masked variant (kTail) drops rows >= nvalid and row excl_rel (a ring row
+// that a fused step replaces; any value outside [0, 32) drops nothing).
 template <int G, int KB, bool kTail>
-__device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, const u32x4_t (&qa)[KB],
+__device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, int excl_rel,
+                                             const u32x4_t (&qa)[KB],
                                              float qk_scale, uint16_t* __restrict__ p_lds,
                                              WaveState& st) {
   const int lane = threadIdx.x & 63;
@@ -210,7 +222,7 @@ __device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, const
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       float v = s[j][i] * qk_scale;
-      if (kTail && 16 * j + col >= nvalid) v = -INFINITY;
+      if (kTail && (16 * j + col >= nvalid || 16 * j + col == excl_rel)) v = -INFINITY;
       s[j][i] = v;
     }
     mx[i] = row_max16(fmaxf(s[0][i], s[1][i]));
@@ -251,12 +263,14 @@ __device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, const
   const u32x4_t pa_lo = *reinterpret_cast<const u32x4_t*>(p_lds + (16 + col) * kTileRows + 8 * grp);
 
   if (kTail) {
-    // zero the V rows of the lane's block that lie past the item
-    const int valid = min(max(nvalid - 8 * grp, 0), 8);
+    // zero the V rows of the lane's block that are dropped
     u32x4_t keep;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      keep[w] = (2 * w < valid ? 0x0000ffffu : 0u) | (2 * w + 1 < valid ? 0xffff0000u : 0u);
+    for (int w = 0; w < 4; ++w) {
+      const int e0 = 8 * grp + 2 * w, e1 = e0 + 1;
+      keep[w] = (e0 < nvalid && e0 != excl_rel ? 0x0000ffffu : 0u) |
+                (e1 < nvalid && e1 != excl_rel ? 0xffff0000u : 0u);
+    }
 #pragma unroll
     for (int n = 0; n < 8; ++n) tr.vf[n] &= keep;
   }
@@ -268,10 +282,12 @@ __device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, const
   }
 }
 
+// Rows [r0, r1) of one stream, except row excl (-1: none).
 template <int G, int KB>
 __device__ __forceinline__ void attend_range(const uint16_t* kb, int kstride, const uint16_t* vb,
-                                             int r0, int r1, int c, const u32x4_t (&qa)[KB],
-                                             float qk_scale, uint16_t* p_lds, WaveState& st) {
+                                             int r0, int r1, int excl, int c,
+                                             const u32x4_t (&qa)[KB], float qk_scale,
+                                             uint16_t* p_lds, WaveState& st) {
   const int wave = threadIdx.x >> 6;
   int t0 = r0 + wave * kTileRows;
 #if LEANK_PREFETCH
@@ -283,10 +299,10 @@ __device__ __forceinline__ void attend_range(const uint16_t* kb, int kstride, co
     TileRegs<KB> nxt;
     if (tn < r1) load_tile<KB>(kb, kstride, vb, tn, r1 - tn, c, nxt);
     const int nvalid = r1 - t0;
-    if (nvalid >= kTileRows) {
-      compute_tile<G, KB, false>(cur, kTileRows, qa, qk_scale, p_lds, st);
+    if (nvalid >= kTileRows && static_cast<unsigned>(excl - t0) >= kTileRows) {
+      compute_tile<G, KB, false>(cur, kTileRows, -1, qa, qk_scale, p_lds, st);
     } else {
-      compute_tile<G, KB, true>(cur, nvalid, qa, qk_scale, p_lds, st);
+      compute_tile<G, KB, true>(cur, nvalid, excl - t0, qa, qk_scale, p_lds, st);
     }
     cur = nxt;
   }
@@ -295,10 +311,10 @@ __device__ __forceinline__ void attend_range(const uint16_t* kb, int kstride, co
     const int nvalid = r1 - t0;
     TileRegs<KB> cur;
     load_tile<KB>(kb, kstride, vb, t0, nvalid, c, cur);
-    if (nvalid >= kTileRows) {
-      compute_tile<G, KB, false>(cur, kTileRows, qa, qk_scale, p_lds, st);
+    if (nvalid >= kTileRows && static_cast<unsigned>(excl - t0) >= kTileRows) {
+      compute_tile<G, KB, false>(cur, kTileRows, -1, qa, qk_scale, p_lds, st);
     } else {
-      compute_tile<G, KB, true>(cur, nvalid, qa, qk_scale, p_lds, st);
+      compute_tile<G, KB, true>(cur, nvalid, excl - t0, qa, qk_scale, p_lds, st);
     }
   }
 #endif
@@ -332,6 +348,52 @@ __device__ __forceinline__ void gather_q(const uint16_t* s_q, const int16_t* s_i
   }
 }
 
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum16(x);
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+// The append of a fused decode step for one (batch row, KV head) pair
+// (LeanK page, section 3.1 item 2): the token at position pos goes to its
+// sink or ring row (with no window, to the middle), and the token it pushes
+// out of the window, ring row `slot`, moves its kept K channels and -- for
+// a live head -- its V to the middle.  The regular items of the call
+// cover the rows cached before the append, minus that ring row; the two
+// tokens are scored by the pair's full-width item 0, which stages them in
+// LDS before its tile loop and writes the append after it.
+struct StepTokens {
+  bool ok;        // the row takes part (its position lies in the plan)
+  bool new_full;  // the new token is a sink or window row (full width)
+  bool new_in;    // the new token is attended (not a middle token of a dead head)
+  bool leave_in;  // a token leaves the window of a live head
+  int pos;
+  int slot;       // ring row of the new token (and of the leaving one)
+};
+
+__device__ __forceinline__ StepTokens step_tokens(const DecodeParams& p, int b, bool live) {
+  StepTokens st;
+  const int64_t pos = p.row_pos ? p.row_pos[b] : p.step_pos;
+  st.ok = pos >= 0 && pos <= p.max_len;
+  st.pos = st.ok ? static_cast<int>(pos) : 0;
+  const int S = p.n_sink, W = p.window;
+  st.new_full = st.pos < S || W > 0;
+  st.new_in = st.ok && (st.new_full || live);
+  st.leave_in = st.ok && live && W > 0 && st.pos - W >= S;
+  st.slot = st.pos < S ? st.pos : (W > 0 ? S + (st.pos - S) % W : 0);
+  return st;
+}
+
+// Word `lane` of a token's compacted K row (kept channels 2 lane, 2 lane + 1
+// of the head) from its full row in LDS.
+__device__ __forceinline__ uint32_t compact_from_lds(const uint16_t* row, const int16_t* s_idx,
+                                                     int kept, int lane) {
+  const int j0 = 2 * lane;
+  if (j0 >= kept) return 0u;
+  return static_cast<uint32_t>(row[s_idx[j0] & (LEANK_HEAD_DIM - 1)]) |
+         (static_cast<uint32_t>(row[s_idx[j0 + 1] & (LEANK_HEAD_DIM - 1)]) << 16);
+}
+
 template <int G>
 __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ float s_acc[kWaves][G][LEANK_HEAD_DIM];
@@ -340,6 +402,11 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ uint16_t s_q[G * LEANK_HEAD_DIM];
   __shared__ int16_t s_idx[LEANK_HEAD_DIM];
   __shared__ __attribute__((aligned(16))) uint16_t s_p[kWaves][2 * 16 * kTileRows];
+  // fused step: K and V rows of the new token [0] and the leaving token [1],
+  // and their scaled scores per query head (-inf when not attended)
+  __shared__ __attribute__((aligned(16))) uint16_t s_tok_k[2][LEANK_HEAD_DIM];
+  __shared__ __attribute__((aligned(16))) uint16_t s_tok_v[2][LEANK_HEAD_DIM];
+  __shared__ float s_tok_s[2][G];
 
   const int item = blockIdx.x;
   const int b = item / p.items_per_b;
@@ -349,6 +416,7 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   const DecodeHead hd = p.heads[h];
   const int local = r - hd.base;
   const bool middle = local >= p.n_sl_items;
+  const bool carries_step = p.step && local == 0;  // block-uniform
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -357,11 +425,37 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   const uint16_t* qh = p.q + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM;
   if (t < G * 16)
     *reinterpret_cast<u32x4_t*>(s_q + t * 8) = *reinterpret_cast<const u32x4_t*>(qh + t * 8);
-  if (middle && t >= 128 && t < 144)
+  if ((middle || carries_step) && t >= 128 && t < 144)
     *reinterpret_cast<u32x4_t*>(s_idx + (t - 128) * 8) =
         *reinterpret_cast<const u32x4_t*>(p.kept_idx + h * LEANK_HEAD_DIM + (t - 128) * 8);
   for (int k = lane; k < 2 * 16 * kTileRows / 8; k += 64)
     reinterpret_cast<u32x4_t*>(s_p[wave])[k] = u32x4_t{0u, 0u, 0u, 0u};
+  const int64_t pair = static_cast<int64_t>(b) * p.n_kv + h;
+  StepTokens tok{};
+  if (carries_step) {
+    // the new token from k_new / v_new, the leaving one from its ring row
+    tok = step_tokens(p, b, hd.kept > 0);
+    const uint16_t* ring_k = p.k_sl + (pair * p.slots + tok.slot) * LEANK_HEAD_DIM;
+    const uint16_t* ring_v = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM;
+    const u32x4_t zero4{0u, 0u, 0u, 0u};
+    if (t >= 144 && t < 160) {
+      const int c8 = (t - 144) * 8;
+      *reinterpret_cast<u32x4_t*>(s_tok_k[0] + c8) =
+          tok.ok ? *reinterpret_cast<const u32x4_t*>(p.k_new + pair * LEANK_HEAD_DIM + c8) : zero4;
+    } else if (t >= 160 && t < 176) {
+      const int c8 = (t - 160) * 8;
+      *reinterpret_cast<u32x4_t*>(s_tok_v[0] + c8) =
+          tok.ok ? *reinterpret_cast<const u32x4_t*>(p.v_new + pair * LEANK_HEAD_DIM + c8) : zero4;
+    } else if (t >= 176 && t < 192) {
+      const int c8 = (t - 176) * 8;
+      *reinterpret_cast<u32x4_t*>(s_tok_k[1] + c8) =
+          tok.leave_in ? *reinterpret_cast<const u32x4_t*>(ring_k + c8) : zero4;
+    } else if (t >= 192) {
+      const int c2 = (t - 192) * 2;
+      s_tok_v[1][c2] = tok.leave_in ? ring_v[v_elem(tok.slot, c2)] : uint16_t{0};
+      s_tok_v[1][c2 + 1] = tok.leave_in ? ring_v[v_elem(tok.slot, c2 + 1)] : uint16_t{0};
+    }
+  }
   __syncthreads();
 
   WaveState st;
@@ -375,7 +469,18 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   uint16_t* p_lds = s_p[wave];
 
   int t_sl = p.t_sl, t_mid = p.t_mid;
-  if (p.ctx_lens) {  // ragged batch: this row may hold fewer tokens than the plan
+  int excl = -1;  // ring row replaced by a fused step's append
+  if (p.step) {
+    // rows cached before the append; the row of the token leaving the
+    // window is scored by the step item
+    const int64_t pos = p.row_pos ? p.row_pos[b] : p.step_pos;
+    const bool ok = pos >= 0 && pos <= p.max_len;
+    const int len = ok ? static_cast<int>(pos) : 0;
+    if (ok && p.window > 0 && len - p.window >= p.n_sink)
+      excl = p.n_sink + (len - p.n_sink) % p.window;
+    t_sl = min(len, p.slots);
+    t_mid = max(0, len - p.slots);
+  } else if (p.ctx_lens) {  // ragged batch: this row may hold fewer tokens than the plan
     const int len = min(max(p.ctx_lens[b], 0), p.max_len);
     t_sl = min(len, p.slots);
     t_mid = max(0, len - p.slots);
@@ -383,12 +488,12 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   if (!middle) {
     const int r0 = local * p.sl_rows;
     const int r1 = min(t_sl, r0 + p.sl_rows);
-    const int64_t pair = static_cast<int64_t>(b) * p.n_kv + h;
     const uint16_t* kb = p.k_sl + pair * p.slots * LEANK_HEAD_DIM;
     const uint16_t* vb = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM;
     u32x4_t qa[4];
     gather_q<G, 4>(s_q, s_idx, true, LEANK_HEAD_DIM, qa);
-    attend_range<G, 4>(kb, LEANK_HEAD_DIM, vb, r0, r1, LEANK_HEAD_DIM, qa, p.qk_scale, p_lds, st);
+    attend_range<G, 4>(kb, LEANK_HEAD_DIM, vb, r0, r1, excl, LEANK_HEAD_DIM, qa, p.qk_scale, p_lds,
+                       st);
   } else {
     const int chunk_id = local - p.n_sl_items;
     const int r0 = chunk_id * hd.mid_rows;
@@ -400,27 +505,49 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
       case 1: {
         u32x4_t qa[1];
         gather_q<G, 1>(s_q, s_idx, false, c, qa);
-        attend_range<G, 1>(kb, c, vb, r0, r1, c, qa, p.qk_scale, p_lds, st);
+        attend_range<G, 1>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
         break;
       }
       case 2: {
         u32x4_t qa[2];
         gather_q<G, 2>(s_q, s_idx, false, c, qa);
-        attend_range<G, 2>(kb, c, vb, r0, r1, c, qa, p.qk_scale, p_lds, st);
+        attend_range<G, 2>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
         break;
       }
       case 3: {
         u32x4_t qa[3];
         gather_q<G, 3>(s_q, s_idx, false, c, qa);
-        attend_range<G, 3>(kb, c, vb, r0, r1, c, qa, p.qk_scale, p_lds, st);
+        attend_range<G, 3>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
         break;
       }
       default: {
         u32x4_t qa[4];
         gather_q<G, 4>(s_q, s_idx, false, c, qa);
-        attend_range<G, 4>(kb, c, vb, r0, r1, c, qa, p.qk_scale, p_lds, st);
+        attend_range<G, 4>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
         break;
       }
+    }
+  }
+
+  if (carries_step) {
+    // scores of the two step tokens: full width for a sink / window row,
+    // kept channels for a middle row (the leaving token, or the new one
+    // when there is no window)
+    for (int d = wave; d < 2 * G; d += kWaves) {
+      const int g = d >> 1;
+      const int which = d & 1;
+      const bool full = which == 0 && tok.new_full;
+      float part;
+      if (full) {
+        part = dot2_bf16(reinterpret_cast<const uint32_t*>(s_q)[g * 64 + lane],
+                         reinterpret_cast<const uint32_t*>(s_tok_k[0])[lane], 0.0f);
+      } else {
+        part = dot2_bf16(compact_from_lds(s_q + g * LEANK_HEAD_DIM, s_idx, hd.kept, lane),
+                         compact_from_lds(s_tok_k[which], s_idx, hd.kept, lane), 0.0f);
+      }
+      const float sum = wave_sum(part);
+      const bool in = which == 0 ? tok.new_in : tok.leave_in;
+      if (lane == 0) s_tok_s[which][g] = in ? sum * p.qk_scale : -INFINITY;
     }
   }
 
@@ -442,7 +569,8 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   }
   __syncthreads();
 
-  // one record per item: (acc[G][128], m[G], l[G]) merged over the wavefronts
+  // one record per item: (acc[G][128], m[G], l[G]) merged over the
+  // wavefronts (and, in a step, the two step tokens)
   float* rec = p.partials + static_cast<int64_t>(item) * p.partial_stride;
   for (int k = t; k < G * LEANK_HEAD_DIM; k += kThreads) {
     const int g = k / LEANK_HEAD_DIM;
@@ -450,6 +578,12 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     float m = s_m[0][g];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_m[w][g]);
+    float s_new = -INFINITY, s_leave = -INFINITY;
+    if (carries_step) {
+      s_new = s_tok_s[0][g];
+      s_leave = s_tok_s[1][g];
+      m = fmaxf(m, fmaxf(s_new, s_leave));
+    }
     const float m_use = m == -INFINITY ? 0.0f : m;
     float a = 0.0f, l = 0.0f;
 #pragma unroll
@@ -458,10 +592,45 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
       a = fmaf(s_acc[w][g][ch], f, a);
       l = fmaf(s_l[w][g], f, l);
     }
+    if (carries_step) {
+      // weights are 0 for a token not attended; its staged V is zero too
+      const float w_new = fast_exp2(s_new - m_use);
+      const float w_leave = fast_exp2(s_leave - m_use);
+      a = fmaf(w_new, __uint_as_float(static_cast<uint32_t>(s_tok_v[0][ch]) << 16), a);
+      a = fmaf(w_leave, __uint_as_float(static_cast<uint32_t>(s_tok_v[1][ch]) << 16), a);
+      l += w_new + w_leave;
+    }
     rec[k] = a;
     if (ch == 0) {
       rec[G * LEANK_HEAD_DIM + g] = m;
       rec[G * LEANK_HEAD_DIM + G + g] = l;
+    }
+  }
+
+  if (carries_step && tok.ok && wave == 0) {
+    // the append; this workgroup's reads of the ring row ended before the
+    // merge, and no other item of the call uses the rows written here
+    const int S = p.n_sink, W = p.window;
+    const uint32_t kn = reinterpret_cast<const uint32_t*>(s_tok_k[0])[lane];
+    const uint32_t vn = reinterpret_cast<const uint32_t*>(s_tok_v[0])[lane];
+    auto write_middle = [&](int64_t r, int which) {
+      uint32_t* k_prun = reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(p.k_prun));
+      const int64_t row = static_cast<int64_t>(b) * p.mid_cap + r;
+      if (2 * lane < hd.kept)
+        k_prun[(hd.k_off + row * hd.kept) / 2 + lane] =
+            compact_from_lds(s_tok_k[which], s_idx, hd.kept, lane);
+      store_v_row_word(const_cast<uint16_t*>(p.v_mid) + hd.v_off +
+                           static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM,
+                       r, lane, reinterpret_cast<const uint32_t*>(s_tok_v[which])[lane]);
+    };
+    if (tok.pos >= S && W == 0) {  // no window: the new token is a middle token
+      if (hd.kept > 0) write_middle(tok.pos - S, 0);
+    } else {
+      if (tok.leave_in) write_middle(tok.pos - W - S, 1);
+      uint16_t* ring_k = const_cast<uint16_t*>(p.k_sl) + pair * p.slots * LEANK_HEAD_DIM;
+      uint16_t* ring_v = const_cast<uint16_t*>(p.v_sl) + pair * p.v_sl_rows * LEANK_HEAD_DIM;
+      reinterpret_cast<uint32_t*>(ring_k)[tok.slot * 64 + lane] = kn;
+      store_v_row_word(ring_v, tok.slot, lane, vn);
     }
   }
 }

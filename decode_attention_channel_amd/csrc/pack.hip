@@ -58,17 +58,6 @@ struct PackParams {
 constexpr int kWordsPerRow = LEANK_HEAD_DIM / 2;  // 64 words of two bf16
 constexpr int kUnitsPerBlock = 4;
 
-__device__ __forceinline__ uint32_t load_v_row_word(const uint16_t* region, int64_t r, int lane) {
-  const uint32_t lo = region[v_elem(r, 2 * lane)];
-  const uint32_t hi = region[v_elem(r, 2 * lane + 1)];
-  return lo | (hi << 16);
-}
-
-__device__ __forceinline__ void store_v_row_word(uint16_t* region, int64_t r, int lane, uint32_t w) {
-  region[v_elem(r, 2 * lane)] = static_cast<uint16_t>(w & 0xffffu);
-  region[v_elem(r, 2 * lane + 1)] = static_cast<uint16_t>(w >> 16);
-}
-
 // Writes one token's K (kept channels) and V (live heads) to middle row r.
 __device__ __forceinline__ void write_middle(const PackParams& p, int b, int h, int64_t r,
                                              uint32_t kw, uint32_t vw, int lane) {
@@ -78,12 +67,9 @@ __device__ __forceinline__ void write_middle(const PackParams& p, int b, int h, 
   // channel ids are masked into [0, 128) so that bad ids cannot leave the row
   const int c0 = j0 < hd.kept ? (p.kept_idx[h * LEANK_HEAD_DIM + j0] & (LEANK_HEAD_DIM - 1)) : 0;
   const int c1 = j0 < hd.kept ? (p.kept_idx[h * LEANK_HEAD_DIM + j0 + 1] & (LEANK_HEAD_DIM - 1)) : 0;
-  const uint32_t w0 = static_cast<uint32_t>(__shfl(static_cast<int>(kw), c0 >> 1));
-  const uint32_t w1 = static_cast<uint32_t>(__shfl(static_cast<int>(kw), c1 >> 1));
-  const uint32_t lo = (c0 & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-  const uint32_t hi = (c1 & 1) ? (w1 >> 16) : (w1 & 0xffffu);
+  const uint32_t kc = compact_k_word(kw, c0, c1);
   const int64_t row = static_cast<int64_t>(b) * p.mid_cap + r;
-  if (j0 < hd.kept) p.k_prun[(hd.k_off + row * hd.kept) / 2 + lane] = lo | (hi << 16);
+  if (j0 < hd.kept) p.k_prun[(hd.k_off + row * hd.kept) / 2 + lane] = kc;
   store_v_row_word(p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM, r,
                    lane, vw);
 }

@@ -91,8 +91,9 @@ int validate_cache(const leank_layer_cache* c, bool need_buffers) {
   return LEANK_OK;
 }
 
-int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, WorkPlan* w) {
+int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPlan* w) {
   memset(w, 0, sizeof(*w));
+  w->step = step;
   const int64_t slots = static_cast<int64_t>(c->n_sink) + c->window;
   w->group = c->n_q_heads / c->n_kv_heads;
   w->t_sl = static_cast<int32_t>(std::min<int64_t>(ctx_len, slots));
@@ -111,6 +112,10 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, WorkPlan* w) {
   split_rows(w->t_sl, row_target(4 * LEANK_HEAD_DIM, kItemBytesMin), &n32, &rows32, &b);
   bound_per_b += b * c->n_kv_heads;
   split_rows(w->t_sl, row_target(4 * LEANK_HEAD_DIM, target), &w->n_sl_items, &w->sl_rows, &unused_n);
+  if (step && w->n_sl_items == 0) {  // item 0 carries the append even over no cached rows
+    w->n_sl_items = 1;
+    bound_per_b += c->n_kv_heads;
+  }
   int32_t base = 0;
   for (int h = 0; h < c->n_kv_heads; ++h) {
     w->head_base[h] = base;
@@ -212,7 +217,7 @@ extern "C" int leank_workspace_bytes(const leank_layer_cache* cache, int64_t ctx
   if (!bytes_out || ctx_len < 1) return LEANK_EINVAL;
   if (ctx_len > cache->max_ctx) return LEANK_ECAPACITY;
   WorkPlan w;
-  make_work_plan(cache, ctx_len, &w);
+  make_work_plan(cache, ctx_len, 0, &w);
   *bytes_out = w.workspace_bytes;
   return LEANK_OK;
 }

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define LEANK_ABI_VERSION 2
+#define LEANK_ABI_VERSION 3
 #define LEANK_HEAD_DIM 128      /* the only head_dim the kernels implement   */
 #define LEANK_MAX_KV_HEADS 64   /* per-layer KV heads a cache plan can hold  */
 #define LEANK_MAX_GROUP 8       /* query heads per KV head the kernels take  */
@@ -187,8 +187,10 @@ int leank_pack_k(const leank_layer_cache* cache, const void* k_new,
 
 /*
  * leank_workspace_bytes -- host.  Bytes of device workspace
- * leank_decode_attn needs for a context of ctx_len tokens (non-decreasing
- * in ctx_len, so the size for max_ctx serves every call).
+ * leank_decode_attn (and its ragged form) needs for a context of ctx_len
+ * tokens, which also covers a fused step (leank_decode_step and its ragged
+ * form) whose context after the append is ctx_len.  Non-decreasing in
+ * ctx_len, so the size for max_ctx serves every call.
  */
 int leank_workspace_bytes(const leank_layer_cache* cache, int64_t ctx_len,
                           size_t* bytes_out);
@@ -253,6 +255,39 @@ int leank_pack_k_rows(const leank_layer_cache* cache, const void* k_new, const v
 int leank_decode_attn_rows(const leank_layer_cache* cache, const void* q,
                            const int32_t* ctx_lens, int64_t max_ctx_len, float scale,
                            float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused decode step: the append of one token per batch row and the decode
+ * attention that follows it, in the two kernels of leank_decode_attn.
+ *
+ * leank_decode_step -- same result as leank_pack_k(cache, k_new, v_new,
+ *   pos, 1) followed by leank_decode_attn(cache, q, pos + 1, ...): the
+ *   cache afterwards holds bit for bit what that append writes (LeanK page,
+ *   section 3.1 item 2: the token leaving the window moves its kept K
+ *   channels and, for a live head, its V to the middle), and out holds the
+ *   attention of q over the pos + 1 tokens (section 3.1 item 3, 3.2).
+ *   k_new, v_new: device bf16 [batch][n_kv_heads][128] (16-byte aligned),
+ *   the token at position pos = the cache's current length (0..max_ctx-1;
+ *   pos + 1 > max_ctx -> LEANK_ECAPACITY).  q, scale, out, workspace as in
+ *   leank_decode_attn; the workspace needs leank_workspace_bytes(cache,
+ *   pos + 1) bytes.  No cache row is written before every read of it in
+ *   the call is done, so the step is safe without any extra ordering.
+ *
+ * leank_decode_step_rows -- the same with batch row b appending at its own
+ *   position row_pos[b] (device int64 [batch], the row's current length)
+ *   and attending over row_pos[b] + 1 tokens.  max_ctx_len (1..max_ctx)
+ *   bounds row_pos[b] + 1 and sizes the work plan and the workspace
+ *   (leank_workspace_bytes(cache, max_ctx_len)).  row_pos is read on the
+ *   device: a row with row_pos[b] outside [0, max_ctx_len - 1] is left
+ *   unchanged and gets a zero output.
+ */
+int leank_decode_step(const leank_layer_cache* cache, const void* q, const void* k_new,
+                      const void* v_new, int64_t pos, float scale, float* out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+int leank_decode_step_rows(const leank_layer_cache* cache, const void* q, const void* k_new,
+                           const void* v_new, const int64_t* row_pos, int64_t max_ctx_len,
+                           float scale, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * leank_decode_bytes -- host.  Algorithmic HBM bytes of one

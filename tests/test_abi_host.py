@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert "leank_build_mask" in names and "leank_pack_k" in names and "leank_decode_attn" in names
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.leank_abi_version() == 2
+    assert lib.leank_abi_version() == 3
     assert lib.leank_layer_cache_size() == ctypes.sizeof(_lib.LayerCacheDesc)
 
 
@@ -152,6 +152,49 @@ def test_calls_rejected_before_launch():
     assert L.leank_pack_k(ref, 0x1000, 0x1008, 0, 1, None) == _lib.EINVAL
     assert L.leank_pack_k(ref, 0x1000, 0x1000, 5, 0, None) == _lib.OK   # empty append: no launch
     assert L.leank_decode_attn(None, 0x1000, 1, 0.1, 0x1000, 0x1000, ws, None) == _lib.EINVAL
+
+
+def test_step_calls_rejected_before_launch():
+    L = _lib.lib()
+    desc = _fake_buffers(dac.leank_plan_layer([32, 0], 2, 4, 2, 128, 4, 8, 100))
+    ref = ctypes.byref(desc)
+    ws = dac.leank_workspace_bytes(desc, 100)
+    p = 0x1000
+
+    def step(pos, k=p, v=p, q=p, scale=0.1, out=p, work=p, nbytes=ws):
+        return L.leank_decode_step(ref, q, k, v, pos, scale, out, work, nbytes, None)
+
+    def step_rows(row_pos, max_len, k=p, nbytes=ws):
+        return L.leank_decode_step_rows(ref, p, k, p, row_pos, max_len, 0.1, p, p, nbytes, None)
+
+    assert step(100) == _lib.ECAPACITY         # the appended token would be row 101
+    assert step(-1) == _lib.EINVAL
+    assert step(5, k=None) == _lib.EINVAL
+    assert step(5, v=0x1008) == _lib.EINVAL    # not 16-byte aligned
+    assert step(5, q=0x1002) == _lib.EINVAL
+    assert step(5, scale=0.0) == _lib.EINVAL
+    assert step(5, work=None) == _lib.EWORKSPACE
+    assert step(5, nbytes=16) == _lib.EWORKSPACE
+    assert step_rows(None, 10) == _lib.EINVAL
+    assert step_rows(p, 0) == _lib.EINVAL
+    assert step_rows(p, 101) == _lib.ECAPACITY
+    assert step_rows(p, 10, k=0x1004) == _lib.EINVAL
+    assert L.leank_decode_step(None, p, p, p, 5, 0.1, p, p, ws, None) == _lib.EINVAL
+
+
+def test_workspace_covers_a_step_at_the_same_context():
+    """A step whose context after the append is n plans n - 1 regular rows
+    plus one record per pair; the size for n must hold that."""
+    rng = np.random.default_rng(9)
+    for _ in range(20):
+        n_kv = int(rng.integers(1, 9))
+        kept = [int(x) for x in rng.integers(0, 17, size=n_kv) * 8]
+        batch = int(rng.integers(1, 70))
+        max_ctx = int(rng.integers(2, 20000))
+        desc = dac.leank_plan_layer(kept, batch, n_kv, n_kv, 128, 4, 32, max_ctx)
+        stride = 128 + 4   # floats per record at one query head per KV head
+        for ctx in sorted(set(rng.integers(1, max_ctx + 1, size=10).tolist())):
+            assert dac.leank_workspace_bytes(desc, ctx) >= batch * n_kv * stride * 4
 
 
 def test_build_mask_rejected_before_launch():
