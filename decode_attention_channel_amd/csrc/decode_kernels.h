@@ -361,14 +361,20 @@ __device__ __forceinline__ float wave_sum(float x) {
 // a live head -- its V to the middle.  The regular items of the call
 // cover the rows cached before the append, minus that ring row; the two
 // tokens are scored by the pair's full-width item 0, which stages them in
-// LDS before its tile loop and writes the append after it.
+// LDS before its tile loop and writes the append after it.  V rows are
+// written as whole 8-row blocks (read in the prologue, one row replaced in
+// LDS, written back with 16-byte stores): a single row of a block is 128
+// scattered 2-byte pieces, which the memory system handles far more slowly
+// than the 2 KiB block.
 struct StepTokens {
   bool ok;        // the row takes part (its position lies in the plan)
   bool new_full;  // the new token is a sink or window row (full width)
   bool new_in;    // the new token is attended (not a middle token of a dead head)
   bool leave_in;  // a token leaves the window of a live head
+  bool to_ring;   // the new token is written to a sink or ring row
   int pos;
   int slot;       // ring row of the new token (and of the leaving one)
+  int mid_row;    // middle row written by the append, -1 for none
 };
 
 __device__ __forceinline__ StepTokens step_tokens(const DecodeParams& p, int b, bool live) {
@@ -380,7 +386,9 @@ __device__ __forceinline__ StepTokens step_tokens(const DecodeParams& p, int b, 
   st.new_full = st.pos < S || W > 0;
   st.new_in = st.ok && (st.new_full || live);
   st.leave_in = st.ok && live && W > 0 && st.pos - W >= S;
+  st.to_ring = st.ok && st.new_full;
   st.slot = st.pos < S ? st.pos : (W > 0 ? S + (st.pos - S) % W : 0);
+  st.mid_row = st.leave_in ? st.pos - W - S : (st.ok && live && !st.new_full ? st.pos - S : -1);
   return st;
 }
 
@@ -402,10 +410,13 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ uint16_t s_q[G * LEANK_HEAD_DIM];
   __shared__ int16_t s_idx[LEANK_HEAD_DIM];
   __shared__ __attribute__((aligned(16))) uint16_t s_p[kWaves][2 * 16 * kTileRows];
-  // fused step: K and V rows of the new token [0] and the leaving token [1],
-  // and their scaled scores per query head (-inf when not attended)
+  // fused step: K rows of the new token [0] and the leaving token [1], the
+  // new token's V, the V blocks (8 rows, as stored) of the ring row [0] and
+  // of the middle row [1] the append writes, and the two tokens' scaled
+  // scores per query head (-inf when not attended)
   __shared__ __attribute__((aligned(16))) uint16_t s_tok_k[2][LEANK_HEAD_DIM];
-  __shared__ __attribute__((aligned(16))) uint16_t s_tok_v[2][LEANK_HEAD_DIM];
+  __shared__ __attribute__((aligned(16))) uint16_t s_tok_v[LEANK_HEAD_DIM];
+  __shared__ __attribute__((aligned(16))) uint16_t s_vblk[2][LEANK_HEAD_DIM * LEANK_V_BLOCK];
   __shared__ float s_tok_s[2][G];
 
   const int item = blockIdx.x;
@@ -433,27 +444,40 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   const int64_t pair = static_cast<int64_t>(b) * p.n_kv + h;
   StepTokens tok{};
   if (carries_step) {
-    // the new token from k_new / v_new, the leaving one from its ring row
+    // the new token from k_new / v_new; the leaving one and the V blocks
+    // the append rewrites from the cache
     tok = step_tokens(p, b, hd.kept > 0);
-    const uint16_t* ring_k = p.k_sl + (pair * p.slots + tok.slot) * LEANK_HEAD_DIM;
-    const uint16_t* ring_v = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM;
     const u32x4_t zero4{0u, 0u, 0u, 0u};
-    if (t >= 144 && t < 160) {
-      const int c8 = (t - 144) * 8;
-      *reinterpret_cast<u32x4_t*>(s_tok_k[0] + c8) =
-          tok.ok ? *reinterpret_cast<const u32x4_t*>(p.k_new + pair * LEANK_HEAD_DIM + c8) : zero4;
-    } else if (t >= 160 && t < 176) {
-      const int c8 = (t - 160) * 8;
-      *reinterpret_cast<u32x4_t*>(s_tok_v[0] + c8) =
-          tok.ok ? *reinterpret_cast<const u32x4_t*>(p.v_new + pair * LEANK_HEAD_DIM + c8) : zero4;
-    } else if (t >= 176 && t < 192) {
-      const int c8 = (t - 176) * 8;
-      *reinterpret_cast<u32x4_t*>(s_tok_k[1] + c8) =
-          tok.leave_in ? *reinterpret_cast<const u32x4_t*>(ring_k + c8) : zero4;
-    } else if (t >= 192) {
-      const int c2 = (t - 192) * 2;
-      s_tok_v[1][c2] = tok.leave_in ? ring_v[v_elem(tok.slot, c2)] : uint16_t{0};
-      s_tok_v[1][c2 + 1] = tok.leave_in ? ring_v[v_elem(tok.slot, c2 + 1)] : uint16_t{0};
+    if (t < 128) {
+      // ring V block of the slot (16 bytes = one channel's 8 rows per thread)
+      const uint16_t* blk = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM +
+                            static_cast<int64_t>(tok.slot / LEANK_V_BLOCK) * (LEANK_HEAD_DIM * LEANK_V_BLOCK);
+      *reinterpret_cast<u32x4_t*>(s_vblk[0] + t * 8) =
+          tok.to_ring || tok.leave_in ? *reinterpret_cast<const u32x4_t*>(blk + t * 8) : zero4;
+    } else {
+      // V_mid block of the middle row written
+      const int c = t - 128;
+      u32x4_t x = zero4;
+      if (tok.mid_row >= 0) {
+        const uint16_t* blk = p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM +
+                              static_cast<int64_t>(tok.mid_row / LEANK_V_BLOCK) * (LEANK_HEAD_DIM * LEANK_V_BLOCK);
+        x = *reinterpret_cast<const u32x4_t*>(blk + c * 8);
+      }
+      *reinterpret_cast<u32x4_t*>(s_vblk[1] + c * 8) = x;
+      if (t >= 144 && t < 160) {
+        const int c8 = (t - 144) * 8;
+        *reinterpret_cast<u32x4_t*>(s_tok_k[0] + c8) =
+            tok.ok ? *reinterpret_cast<const u32x4_t*>(p.k_new + pair * LEANK_HEAD_DIM + c8) : zero4;
+      } else if (t >= 160 && t < 176) {
+        const int c8 = (t - 160) * 8;
+        *reinterpret_cast<u32x4_t*>(s_tok_v + c8) =
+            tok.ok ? *reinterpret_cast<const u32x4_t*>(p.v_new + pair * LEANK_HEAD_DIM + c8) : zero4;
+      } else if (t >= 176 && t < 192) {
+        const int c8 = (t - 176) * 8;
+        const uint16_t* ring_k = p.k_sl + (pair * p.slots + tok.slot) * LEANK_HEAD_DIM;
+        *reinterpret_cast<u32x4_t*>(s_tok_k[1] + c8) =
+            tok.leave_in ? *reinterpret_cast<const u32x4_t*>(ring_k + c8) : zero4;
+      }
     }
   }
   __syncthreads();
@@ -596,8 +620,10 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
       // weights are 0 for a token not attended; its staged V is zero too
       const float w_new = fast_exp2(s_new - m_use);
       const float w_leave = fast_exp2(s_leave - m_use);
-      a = fmaf(w_new, __uint_as_float(static_cast<uint32_t>(s_tok_v[0][ch]) << 16), a);
-      a = fmaf(w_leave, __uint_as_float(static_cast<uint32_t>(s_tok_v[1][ch]) << 16), a);
+      const uint32_t v_leave =
+          tok.leave_in ? s_vblk[0][ch * LEANK_V_BLOCK + tok.slot % LEANK_V_BLOCK] : 0u;
+      a = fmaf(w_new, __uint_as_float(static_cast<uint32_t>(s_tok_v[ch]) << 16), a);
+      a = fmaf(w_leave, __uint_as_float(v_leave << 16), a);
       l += w_new + w_leave;
     }
     rec[k] = a;
@@ -609,28 +635,46 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
 
   if (carries_step && tok.ok && wave == 0) {
     // the append; this workgroup's reads of the ring row ended before the
-    // merge, and no other item of the call uses the rows written here
-    const int S = p.n_sink, W = p.window;
-    const uint32_t kn = reinterpret_cast<const uint32_t*>(s_tok_k[0])[lane];
-    const uint32_t vn = reinterpret_cast<const uint32_t*>(s_tok_v[0])[lane];
-    auto write_middle = [&](int64_t r, int which) {
+    // merge, and no other item of the call uses the rows written here.
+    // Lane `lane` owns channels 2 lane, 2 lane + 1: their K words and the
+    // 16-byte groups of the two V blocks, so no lane reads another's LDS.
+    const int e_ring = tok.slot % LEANK_V_BLOCK;
+    const int e_mid = tok.mid_row % LEANK_V_BLOCK;
+    if (tok.mid_row >= 0) {
+      // middle row: kept K channels (compacted) and V
+      const int which = tok.leave_in ? 1 : 0;
       uint32_t* k_prun = reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(p.k_prun));
-      const int64_t row = static_cast<int64_t>(b) * p.mid_cap + r;
+      const int64_t row = static_cast<int64_t>(b) * p.mid_cap + tok.mid_row;
       if (2 * lane < hd.kept)
         k_prun[(hd.k_off + row * hd.kept) / 2 + lane] =
             compact_from_lds(s_tok_k[which], s_idx, hd.kept, lane);
-      store_v_row_word(const_cast<uint16_t*>(p.v_mid) + hd.v_off +
-                           static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM,
-                       r, lane, reinterpret_cast<const uint32_t*>(s_tok_v[which])[lane]);
-    };
-    if (tok.pos >= S && W == 0) {  // no window: the new token is a middle token
-      if (hd.kept > 0) write_middle(tok.pos - S, 0);
-    } else {
-      if (tok.leave_in) write_middle(tok.pos - W - S, 1);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ch = 2 * lane + u;
+        s_vblk[1][ch * LEANK_V_BLOCK + e_mid] =
+            tok.leave_in ? s_vblk[0][ch * LEANK_V_BLOCK + e_ring] : s_tok_v[ch];
+      }
+      uint16_t* blk = const_cast<uint16_t*>(p.v_mid) + hd.v_off +
+                      static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM +
+                      static_cast<int64_t>(tok.mid_row / LEANK_V_BLOCK) * (LEANK_HEAD_DIM * LEANK_V_BLOCK);
+      reinterpret_cast<u32x4_t*>(blk)[2 * lane] = reinterpret_cast<const u32x4_t*>(s_vblk[1])[2 * lane];
+      reinterpret_cast<u32x4_t*>(blk)[2 * lane + 1] =
+          reinterpret_cast<const u32x4_t*>(s_vblk[1])[2 * lane + 1];
+    }
+    if (tok.to_ring) {
       uint16_t* ring_k = const_cast<uint16_t*>(p.k_sl) + pair * p.slots * LEANK_HEAD_DIM;
-      uint16_t* ring_v = const_cast<uint16_t*>(p.v_sl) + pair * p.v_sl_rows * LEANK_HEAD_DIM;
-      reinterpret_cast<uint32_t*>(ring_k)[tok.slot * 64 + lane] = kn;
-      store_v_row_word(ring_v, tok.slot, lane, vn);
+      reinterpret_cast<uint32_t*>(ring_k)[tok.slot * 64 + lane] =
+          reinterpret_cast<const uint32_t*>(s_tok_k[0])[lane];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ch = 2 * lane + u;
+        s_vblk[0][ch * LEANK_V_BLOCK + e_ring] = s_tok_v[ch];
+      }
+      uint16_t* blk = const_cast<uint16_t*>(p.v_sl) + pair * p.v_sl_rows * LEANK_HEAD_DIM +
+                      static_cast<int64_t>(tok.slot / LEANK_V_BLOCK) * (LEANK_HEAD_DIM * LEANK_V_BLOCK);
+      reinterpret_cast<u32x4_t*>(blk)[2 * lane] = reinterpret_cast<const u32x4_t*>(s_vblk[0])[2 * lane];
+      reinterpret_cast<u32x4_t*>(blk)[2 * lane + 1] =
+          reinterpret_cast<const u32x4_t*>(s_vblk[0])[2 * lane + 1];
     }
   }
 }
