@@ -46,7 +46,27 @@ the design notes of the repository):
 * cache layout of the full-width region: sink token p < S in slot p, a
   window token p >= S in ring slot S + (p - S) mod W.
 
-Every floating-point step runs in float64 on bf16 inputs widened exactly.
+Low-bit middle streams (LeanK page, section 4.2 and its deployment notes:
+quantization composes with the pruning and comes after prune and
+reorganisation; white paper section 5.2.1: INT8/INT4 codes, per-channel K
+and per-token V as in KIVI).  The pages give no formula; the reading taken:
+
+* asymmetric uniform quantization over a group of values x: lo = min x,
+  hi = max x, scale = (hi - lo) / (2^bits - 1), code = round-half-even of
+  (x - lo) / scale clamped to [0, 2^bits - 1] (code 0 when scale = 0); the
+  value represented is code * scale + lo;
+* the code is an integer decided by floating point, so it is decided in
+  IEEE float32 (one subtraction, one division, as written);
+* K (the kept channels of the middle) is quantized per channel over groups
+  of 64 consecutive middle rows of one (batch row, KV head); the rows of a
+  group that is not yet complete stay bf16 until the group fills;
+* V of the middle is quantized per token (one scale and minimum over the
+  token's 128 channels);
+* the sink and window rows stay bf16 (they play the part of KIVI's
+  full-precision residual).
+
+Every floating-point step runs in float64 on bf16 inputs widened exactly,
+except the quantization decision above (float32).
 """
 
 import numpy as np
@@ -59,8 +79,15 @@ __all__ = [
     "ring_slot",
     "pack_reference",
     "decode",
+    "QUANT_GROUP",
+    "quantize_asym",
+    "dequantize",
+    "quantize_middle",
+    "pack_reference_q",
+    "decode_q",
     "kv_cache_bytes",
     "decode_traffic_bytes",
+    "decode_traffic_bytes_q",
     "pair_retention",
     "head_hf_ratio",
     "rank_correlation",
@@ -196,27 +223,13 @@ def pack_reference(k_bits, v_bits, kept_count, kept_idx, n_sink, window):
             "k_prun": k_prun, "v_mid": v_mid}
 
 
-def decode(q_bits, k_bits, v_bits, mask, n_sink, window, scale=None, pairs=None):
-    """Single-token decode attention over a channel-pruned cache (one layer).
+def _attend(shape, get_q, get_k, get_v, mask, n_sink, window, scale, pairs):
+    """The attention definition over row accessors.
 
-    q_bits: uint16 [B, Hq, d]; k_bits, v_bits: uint16 [B, H, T, d] -- the
-    full, unpruned context of T tokens; mask: uint8 [H, d] (beta of the
-    LeanK page, section 2.2 stage 2).  Query head j reads KV head j // G.
-
-    For query head j with KV head h (definition, float64):
-      * sink and local-window tokens score q . k over all channels;
-      * middle tokens of a head with kept channels score q . (beta_h * k);
-      * middle tokens of a fully-pruned head are left out entirely;
-      * out = sum_t softmax(scale * s)_t v_t over the included tokens,
-        scale = 1/sqrt(d) by default (FastGen page, section 5.3).
-
-    Returns float64 [B, Hq, d], or [len(pairs), d] for a list of (b, j).
+    shape = (B, Hq, H, T, d); get_q(b, j) -> float64 [d]; get_k(b, h, rows)
+    and get_v(b, h, rows) -> float64 [len(rows), d].
     """
-    q_bits = np.asarray(q_bits, dtype=np.uint16)
-    k_bits = np.asarray(k_bits, dtype=np.uint16)
-    v_bits = np.asarray(v_bits, dtype=np.uint16)
-    batch, n_q_heads, d = q_bits.shape
-    _, n_heads, ctx_len, _ = k_bits.shape
+    batch, n_q_heads, n_heads, ctx_len, d = shape
     if ctx_len < 1:
         raise ValueError("empty context")
     group = n_q_heads // n_heads
@@ -241,21 +254,168 @@ def decode(q_bits, k_bits, v_bits, mask, n_sink, window, scale=None, pairs=None)
     for (b, h), heads in sorted(by_kv.items()):
         beta = np.asarray(mask[h], dtype=np.float64)
         live = bool(np.any(beta != 0))
-        keys_full = bf16_bits_to_f64(k_bits[b, h, full_rows])
-        vals_full = bf16_bits_to_f64(v_bits[b, h, full_rows])
+        keys_full = get_k(b, h, full_rows)
+        vals_full = get_v(b, h, full_rows)
         if live and mid_rows.size:
-            keys_mid = bf16_bits_to_f64(k_bits[b, h, mid_rows]) * beta
-            vals_mid = bf16_bits_to_f64(v_bits[b, h, mid_rows])
+            keys_mid = get_k(b, h, mid_rows) * beta
+            vals_mid = get_v(b, h, mid_rows)
             keys = np.concatenate([keys_full, keys_mid])
             vals = np.concatenate([vals_full, vals_mid])
         else:
             keys, vals = keys_full, vals_full
         for j in heads:
-            qv = bf16_bits_to_f64(q_bits[b, j])
+            qv = get_q(b, j)
             s = (keys @ qv) * scale
             w = np.exp(s - s.max())
             put(b, j, (w @ vals) / w.sum())
     return out
+
+
+def decode(q_bits, k_bits, v_bits, mask, n_sink, window, scale=None, pairs=None):
+    """Single-token decode attention over a channel-pruned cache (one layer).
+
+    q_bits: uint16 [B, Hq, d]; k_bits, v_bits: uint16 [B, H, T, d] -- the
+    full, unpruned context of T tokens; mask: uint8 [H, d] (beta of the
+    LeanK page, section 2.2 stage 2).  Query head j reads KV head j // G.
+
+    For query head j with KV head h (definition, float64):
+      * sink and local-window tokens score q . k over all channels;
+      * middle tokens of a head with kept channels score q . (beta_h * k);
+      * middle tokens of a fully-pruned head are left out entirely;
+      * out = sum_t softmax(scale * s)_t v_t over the included tokens,
+        scale = 1/sqrt(d) by default (FastGen page, section 5.3).
+
+    Returns float64 [B, Hq, d], or [len(pairs), d] for a list of (b, j).
+    """
+    q_bits = np.asarray(q_bits, dtype=np.uint16)
+    k_bits = np.asarray(k_bits, dtype=np.uint16)
+    v_bits = np.asarray(v_bits, dtype=np.uint16)
+    batch, n_q_heads, d = q_bits.shape
+    _, n_heads, ctx_len, _ = k_bits.shape
+    return _attend((batch, n_q_heads, n_heads, ctx_len, d),
+                   lambda b, j: bf16_bits_to_f64(q_bits[b, j]),
+                   lambda b, h, rows: bf16_bits_to_f64(k_bits[b, h, rows]),
+                   lambda b, h, rows: bf16_bits_to_f64(v_bits[b, h, rows]),
+                   mask, n_sink, window, scale, pairs)
+
+
+# ---------------------------------------------------------------------------
+# low-bit middle streams (LeanK page, section 4.2; white paper section 5.2.1)
+
+QUANT_GROUP = 64  # middle rows per K quantization group
+
+
+def quantize_asym(x, bits, axis):
+    """Asymmetric uniform quantization of x along `axis` (one group per
+    slice along the other axes).  Returns (codes uint8, scale float32, lo
+    float32), scale and lo with the reduced axis kept (size 1).
+
+    Decided in float32: lo = min, hi = max, scale = (hi - lo) / (2^bits - 1),
+    code = rint((x - lo) / scale) clamped to [0, 2^bits - 1]; 0 when scale = 0.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    levels = np.float32(2 ** bits - 1)
+    lo = x.min(axis=axis, keepdims=True)
+    hi = x.max(axis=axis, keepdims=True)
+    scale = (hi - lo) / levels
+    with np.errstate(divide="ignore", invalid="ignore"):
+        raw = np.rint((x - lo) / scale)
+    codes = np.where(scale > 0, np.clip(raw, 0, levels), 0).astype(np.uint8)
+    return codes, scale, lo
+
+
+def dequantize(codes, scale, lo):
+    """code * scale + lo, in float64 from the stored float32 scale and lo."""
+    return (np.asarray(codes, dtype=np.float64) * np.asarray(scale, dtype=np.float64)
+            + np.asarray(lo, dtype=np.float64))
+
+
+def quantize_middle(k_prun_bits, v_mid_bits, bits, group=QUANT_GROUP):
+    """Quantized middle of one (batch row, KV head) pair of a live head.
+
+    k_prun_bits: uint16 [T_mid, c] (kept channels, bf16); v_mid_bits: uint16
+    [T_mid, d].  Returns a dict:
+      k_codes uint8 [n_full * group, c], k_scale / k_lo float32 [n_full, c]
+        (per channel over each complete group of `group` rows),
+      k_stage uint16 [T_mid - n_full * group, c] (rows of the incomplete
+        group, bf16 as packed),
+      v_codes uint8 [T_mid, d], v_scale / v_lo float32 [T_mid] (per token).
+    """
+    k_prun_bits = np.asarray(k_prun_bits, dtype=np.uint16)
+    v_mid_bits = np.asarray(v_mid_bits, dtype=np.uint16)
+    t_mid, c = k_prun_bits.shape
+    n_full = t_mid // group
+    k32 = bf16_bits_to_f64(k_prun_bits[:n_full * group]).astype(np.float32)
+    k_codes, k_scale, k_lo = quantize_asym(k32.reshape(n_full, group, c), bits, axis=1)
+    v32 = bf16_bits_to_f64(v_mid_bits).astype(np.float32)
+    v_codes, v_scale, v_lo = quantize_asym(v32, bits, axis=1)
+    return {"k_codes": k_codes.reshape(n_full * group, c),
+            "k_scale": k_scale.reshape(n_full, c), "k_lo": k_lo.reshape(n_full, c),
+            "k_stage": k_prun_bits[n_full * group:].copy(),
+            "v_codes": v_codes, "v_scale": v_scale.reshape(t_mid), "v_lo": v_lo.reshape(t_mid)}
+
+
+def pack_reference_q(k_bits, v_bits, kept_count, kept_idx, n_sink, window, bits,
+                     group=QUANT_GROUP):
+    """Expected contents of a cache with low-bit middle streams: the ring as
+    in pack_reference, and for every (b, live h) the quantize_middle dict
+    (None for a dead head)."""
+    ref = pack_reference(k_bits, v_bits, kept_count, kept_idx, n_sink, window)
+    batch = np.asarray(k_bits).shape[0]
+    mid_q = []
+    for head, kp in enumerate(ref["k_prun"]):
+        if int(kept_count[head]) == 0:
+            mid_q.append(None)
+            continue
+        mid_q.append([quantize_middle(kp[b], ref["v_mid"][head][b], bits, group)
+                      for b in range(batch)])
+    ref["mid_q"] = mid_q
+    return ref
+
+
+def decode_q(q_bits, k_bits, v_bits, mask, n_sink, window, bits, group=QUANT_GROUP,
+             scale=None, pairs=None):
+    """decode() with the middle of every live head read back from its
+    low-bit streams: kept K channels of complete groups and every middle V
+    row are replaced by their dequantized values; the rows of the incomplete
+    K group, the sink and the window are exact."""
+    q_bits = np.asarray(q_bits, dtype=np.uint16)
+    k_bits = np.asarray(k_bits, dtype=np.uint16)
+    v_bits = np.asarray(v_bits, dtype=np.uint16)
+    batch, n_q_heads, d = q_bits.shape
+    _, n_heads, ctx_len, _ = k_bits.shape
+    _, middle, _ = regions(ctx_len, n_sink, window)
+    middle_pos = np.asarray(list(middle), dtype=np.int64)
+    cache = {}
+
+    def middle_of(b, h):
+        if (b, h) not in cache:
+            chans = np.flatnonzero(np.asarray(mask[h]))
+            kq = quantize_middle(k_bits[b, h][middle_pos][:, chans], v_bits[b, h][middle_pos], bits, group)
+            k = bf16_bits_to_f64(k_bits[b, h][middle_pos])
+            n_q = kq["k_codes"].shape[0]
+            k[:n_q, chans] = dequantize(kq["k_codes"].reshape(-1, group, chans.size),
+                                        kq["k_scale"][:, None, :],
+                                        kq["k_lo"][:, None, :]).reshape(n_q, chans.size)
+            v = dequantize(kq["v_codes"], kq["v_scale"][:, None], kq["v_lo"][:, None])
+            cache[(b, h)] = (k, v)
+        return cache[(b, h)]
+
+    def rows_of(bits_arr, which):
+        def get(b, h, rows):
+            out = bf16_bits_to_f64(bits_arr[b, h, rows])
+            if middle_pos.size and np.any(mask[h]):
+                at = rows - n_sink
+                inside = (rows >= n_sink) & (at < middle_pos.size)
+                if np.any(inside):
+                    out[inside] = middle_of(b, h)[which][at[inside]]
+            return out
+        return get
+
+    return _attend((batch, n_q_heads, n_heads, ctx_len, d),
+                   lambda b, j: bf16_bits_to_f64(q_bits[b, j]),
+                   rows_of(k_bits, 0), rows_of(v_bits, 1),
+                   mask, n_sink, window, scale, pairs)
 
 
 def kv_cache_bytes(n_layers, n_heads, head_dim, n_tokens, batch=1, bytes_per_elem=2):
@@ -283,6 +443,30 @@ def decode_traffic_bytes(batch, n_q_heads, n_kv_heads, head_dim, ctx_len,
     total += 2 * batch * n_kv_heads * n_full * head_dim * 2        # K, V full width
     total += batch * n_mid * sum(kept) * 2                         # kept K channels
     total += batch * live * n_mid * head_dim * 2                   # middle V, live heads
+    total += batch * n_q_heads * head_dim * 4                      # out
+    return total
+
+
+def decode_traffic_bytes_q(batch, n_q_heads, n_kv_heads, head_dim, ctx_len, n_sink, window,
+                           kept_count, bits, group=QUANT_GROUP):
+    """decode_traffic_bytes with low-bit middle streams: per live head and
+    batch row, the codes of the complete K groups (c * bits / 8 per row) and
+    their float32 scale and minimum per channel and group, the bf16 rows of
+    the incomplete group, and per middle row the V codes (d * bits / 8) and
+    the row's float32 scale and minimum."""
+    sink, middle, local = regions(ctx_len, n_sink, window)
+    n_full_rows = len(sink) + len(local)
+    n_mid = len(middle)
+    n_groups = n_mid // group
+    n_stage = n_mid - n_groups * group
+    total = batch * n_q_heads * head_dim * 2                      # q
+    total += 2 * batch * n_kv_heads * n_full_rows * head_dim * 2   # K, V full width
+    for c in (int(x) for x in kept_count):
+        if c == 0:
+            continue
+        k = n_groups * group * c * bits // 8 + n_groups * c * 8 + n_stage * c * 2
+        v = n_mid * (head_dim * bits // 8 + 8)
+        total += batch * (k + v)
     total += batch * n_q_heads * head_dim * 4                      # out
     return total
 

@@ -15,7 +15,12 @@ the module disagrees with:
 * closed forms of softmax attention (uniform weights, constant values,
   one-token contexts, a single dominant key);
 * a pure-Python attention loop on tiny inputs;
-* the KV-cache sizes the pages work out (tests/golden/kv_cache_sizes.json).
+* the KV-cache sizes the pages work out (tests/golden/kv_cache_sizes.json);
+* for the low-bit middle streams: values already on a quantization grid
+  come back exactly, every value lands on its nearest level (brute force
+  over all levels), each group's minimum and maximum land on the end
+  levels, attention over grid-exact caches equals the unquantized
+  definition, and the byte count equals the size of the packed arrays.
 
 The same functions run against deliberately broken copies of the oracle in
 test_oracle_mutants.py, which shows that each plausible slip is caught.
@@ -513,6 +518,143 @@ def pin_analysis(O):
     assert abs(O.rank_correlation(x, np.exp(x))[1] - 1.0) < 1e-12   # monotone map keeps ranks
 
 
+# ----------------------------------------------------------------------------
+# low-bit middle streams
+
+def pin_quant_closed_forms(O):
+    # a constant group has nothing to resolve: code 0, scale 0, exact
+    codes, scale, lo = O.quantize_asym(np.full((64, 5), 1.5, dtype=np.float32), 4, axis=0)
+    assert np.all(codes == 0) and np.all(scale == 0) and np.all(lo == np.float32(1.5))
+    assert np.all(O.dequantize(codes, scale, lo) == 1.5)
+    rng = np.random.default_rng(40)
+    for bits in (2, 4, 8):
+        top = 2 ** bits - 1
+        # values on the grid lo + k * step (exact in float32), both ends present
+        k = rng.integers(0, top + 1, size=(64, 7))
+        k[3], k[11] = 0, top
+        x = (-1.0 + k * 0.125).astype(np.float32)
+        codes, scale, lo = O.quantize_asym(x, bits, axis=0)
+        assert np.array_equal(codes.astype(np.int64), k), bits
+        assert np.all(scale == np.float32(0.125)) and np.all(lo == np.float32(-1.0))
+        assert np.array_equal(O.dequantize(codes, scale, lo), x.astype(np.float64))
+
+
+def pin_quant_nearest_level(O):
+    rng = np.random.default_rng(41)
+    for bits in (2, 4, 8):
+        top = 2 ** bits - 1
+        x = _bits_to_f64(_f32_to_bf16_bits(rng.standard_normal((64, 9)) * 3.0)).numpy().astype(np.float32)
+        codes, scale, lo = O.quantize_asym(x, bits, axis=0)
+        sc = scale.astype(np.float64)[0]
+        lo64 = lo.astype(np.float64)[0]
+        assert np.all(codes <= top)
+        for col in range(x.shape[1]):
+            levels = lo64[col] + np.arange(top + 1) * sc[col]
+            dist = np.abs(x[:, col, None].astype(np.float64) - levels[None, :])
+            chosen = dist[np.arange(64), codes[:, col].astype(np.int64)]
+            assert np.all(chosen <= dist.min(axis=1) + 1e-6 * sc[col]), (bits, col)
+            assert np.all(chosen <= 0.5 * sc[col] * (1 + 1e-5)), (bits, col)
+            # the group's extremes land on the end levels
+            assert codes[np.argmin(x[:, col]), col] == 0
+            assert codes[np.argmax(x[:, col]), col] == top
+
+
+def pin_quant_middle_groups(O):
+    rng = np.random.default_rng(42)
+    c, t_mid, group = 16, 3 * 64 + 21, 64
+    k_bits = _f32_to_bf16_bits(rng.standard_normal((t_mid, c)))
+    v_bits = _f32_to_bf16_bits(rng.standard_normal((t_mid, 128)))
+    for bits in (4, 8):
+        top = 2 ** bits - 1
+        qm = O.quantize_middle(k_bits, v_bits, bits, group)
+        assert qm["k_codes"].shape == (3 * group, c)
+        assert np.array_equal(qm["k_stage"], k_bits[3 * group:])   # incomplete group exact
+        kx = _bits_to_f64(k_bits).numpy()
+        for g in range(3):
+            rows = kx[g * group:(g + 1) * group]
+            codes = qm["k_codes"][g * group:(g + 1) * group]
+            for ch in range(c):    # per channel over the group's rows
+                assert codes[np.argmin(rows[:, ch]), ch] == 0
+                assert codes[np.argmax(rows[:, ch]), ch] == top
+        vx = _bits_to_f64(v_bits).numpy()
+        for r in range(t_mid):     # per token over its channels
+            assert qm["v_codes"][r, np.argmin(vx[r])] == 0
+            assert qm["v_codes"][r, np.argmax(vx[r])] == top
+
+
+def _grid_context(rng, batch, n_kv, ctx_len, d, bits, mid_lo, mid_hi, group):
+    """K, V bits whose middle rows [mid_lo, mid_hi) lie on per-group
+    (K, per channel) and per-row (V) grids with both ends present, so that
+    quantization is lossless; other rows are generic."""
+    top = 2 ** bits - 1
+    k = rng.standard_normal((batch, n_kv, ctx_len, d))
+    v = rng.standard_normal((batch, n_kv, ctx_len, d))
+    n_groups = (mid_hi - mid_lo) // group
+    for g in range(n_groups):
+        r0 = mid_lo + g * group
+        lvl = rng.integers(0, top + 1, size=(batch, n_kv, group, d))
+        lvl[:, :, 0], lvl[:, :, 1] = 0, top
+        k[:, :, r0:r0 + group] = -2.0 + lvl * 0.25
+    lvl = rng.integers(0, top + 1, size=(batch, n_kv, mid_hi - mid_lo, d))
+    lvl[..., 0], lvl[..., 1] = 0, top
+    v[:, :, mid_lo:mid_hi] = -1.0 + lvl * 0.125
+    return _f32_to_bf16_bits(k), _f32_to_bf16_bits(v)
+
+
+def pin_decode_q_grid_exact(O):
+    rng = np.random.default_rng(43)
+    n_sink, window, group, d = 4, 8, 64, 128
+    for bits in (4, 8):
+        ctx_len = n_sink + 2 * group + 37 + window     # two full groups + an open one
+        k, v = _grid_context(rng, 2, 2, ctx_len, d, bits, n_sink, n_sink + 2 * group + 37, group)
+        q = _f32_to_bf16_bits(rng.standard_normal((2, 4, d)))
+        mask = _random_mask(rng, 2, d, 32)
+        mask[1] = 0                                     # one dead head
+        mask[0, :] = 1                                  # one head keeps every channel
+        ref = O.decode(q, k, v, mask, n_sink, window)
+        got = O.decode_q(q, k, v, mask, n_sink, window, bits, group)
+        assert np.max(np.abs(got - ref)) < 1e-12, bits
+    # each stream on its own: with the other one grid-exact, quantizing
+    # generic values changes the result
+    ctx_len = n_sink + 2 * group + window
+    k2, v2 = _grid_context(rng, 2, 2, ctx_len, d, 2, n_sink, n_sink + 2 * group, group)
+    kg = _f32_to_bf16_bits(rng.standard_normal((2, 2, ctx_len, d)))
+    vg = _f32_to_bf16_bits(rng.standard_normal((2, 2, ctx_len, d)))
+    q = _f32_to_bf16_bits(rng.standard_normal((2, 4, d)) * 2.0)
+    mask = np.ones((2, d), dtype=np.uint8)
+    assert np.max(np.abs(O.decode_q(q, k2, v2, mask, n_sink, window, 2, group)
+                         - O.decode(q, k2, v2, mask, n_sink, window))) < 1e-12
+    for k, v, what in ((kg, v2, "K"), (k2, vg, "V")):
+        diff = np.max(np.abs(O.decode_q(q, k, v, mask, n_sink, window, 2, group)
+                             - O.decode(q, k, v, mask, n_sink, window)))
+        assert diff > 1e-3, what
+
+
+def pin_traffic_bytes_q(O):
+    rng = np.random.default_rng(44)
+    n_sink, window, d, group = 4, 8, 128, 64
+    for bits in (4, 8):
+        for ctx_len in (5, n_sink + window, n_sink + window + 63, n_sink + window + 64 + 29):
+            kept = [32, 0, 64]
+            mask = np.zeros((3, d), dtype=np.uint8)
+            for h, c in enumerate(kept):
+                mask[h, np.sort(rng.choice(d, size=c, replace=False))] = 1
+            kept_idx = np.full((3, d), -1, dtype=np.int64)
+            for h in range(3):
+                kept_idx[h, :kept[h]] = np.flatnonzero(mask[h])
+            k = _f32_to_bf16_bits(rng.standard_normal((2, 3, ctx_len, d)))
+            ref = O.pack_reference_q(k, k, kept, kept_idx, n_sink, window, bits, group)
+            n_full = min(ctx_len, n_sink) + max(0, min(window, ctx_len - n_sink))
+            total = 2 * 6 * d * 2 + 2 * 6 * d * 4 + 2 * 2 * 3 * n_full * d * 2
+            for per_b in ref["mid_q"]:
+                for m in per_b or []:
+                    total += (m["k_codes"].size + m["v_codes"].size) * bits // 8
+                    total += (m["k_scale"].nbytes + m["k_lo"].nbytes + m["k_stage"].nbytes
+                              + m["v_scale"].nbytes + m["v_lo"].nbytes)
+            assert O.decode_traffic_bytes_q(2, 6, 3, d, ctx_len, n_sink, window, kept, bits,
+                                            group) == total, (bits, ctx_len)
+
+
 ALL_PINS = [
     pin_mask_page_procedure,
     pin_mask_closed_forms,
@@ -527,4 +669,9 @@ ALL_PINS = [
     pin_cache_bytes,
     pin_traffic_bytes,
     pin_analysis,
+    pin_quant_closed_forms,
+    pin_quant_nearest_level,
+    pin_quant_middle_groups,
+    pin_decode_q_grid_exact,
+    pin_traffic_bytes_q,
 ]

@@ -30,11 +30,11 @@ MUTANTS = [
      "sink = range(0, min(n_sink, ctx_len))",
      "sink = range(0, min(n_sink + 1, ctx_len))"),
     ("inverted channel mask",
-     "keys_mid = bf16_bits_to_f64(k_bits[b, h, mid_rows]) * beta",
-     "keys_mid = bf16_bits_to_f64(k_bits[b, h, mid_rows]) * (1.0 - beta)"),
+     "keys_mid = get_k(b, h, mid_rows) * beta",
+     "keys_mid = get_k(b, h, mid_rows) * (1.0 - beta)"),
     ("mask applied to full-width rows too",
-     "keys_full = bf16_bits_to_f64(k_bits[b, h, full_rows])",
-     "keys_full = bf16_bits_to_f64(k_bits[b, h, full_rows]) * np.asarray(mask[h], dtype=np.float64)"),
+     "keys_full = get_k(b, h, full_rows)",
+     "keys_full = get_k(b, h, full_rows) * np.asarray(mask[h], dtype=np.float64)"),
     ("threshold rank floored",
      "return -((-(n - 1) * prune_pct) // 100)",
      "return ((n - 1) * prune_pct) // 100"),
@@ -80,6 +80,27 @@ MUTANTS = [
     ("exp without the max shift, weights unnormalised",
      "put(b, j, (w @ vals) / w.sum())",
      "put(b, j, (w @ vals) / len(w))"),
+    ("quantization rounds down",
+     "raw = np.rint((x - lo) / scale)",
+     "raw = np.floor((x - lo) / scale)"),
+    ("2^bits quantization steps",
+     "levels = np.float32(2 ** bits - 1)",
+     "levels = np.float32(2 ** bits)"),
+    ("K quantized per token",
+     "quantize_asym(k32.reshape(n_full, group, c), bits, axis=1)",
+     "quantize_asym(k32.reshape(n_full, group, c), bits, axis=2)"),
+    ("V quantized per channel",
+     "v_codes, v_scale, v_lo = quantize_asym(v32, bits, axis=1)",
+     "v_codes, v_scale, v_lo = quantize_asym(v32, bits, axis=0)"),
+    ("minimum not added back",
+     "            + np.asarray(lo, dtype=np.float64))",
+     "            + 0.0 * np.asarray(lo, dtype=np.float64))"),
+    ("quantized attention reads exact middle V",
+     "v = dequantize(kq[\"v_codes\"], kq[\"v_scale\"][:, None], kq[\"v_lo\"][:, None])",
+     "v = bf16_bits_to_f64(v_bits[b, h][middle_pos])"),
+    ("open K group left out of the byte count",
+     "k = n_groups * group * c * bits // 8 + n_groups * c * 8 + n_stage * c * 2",
+     "k = n_groups * group * c * bits // 8 + n_groups * c * 8"),
 ]
 
 
