@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     HEAD_DIM,
     MAX_GROUP,
     MAX_KV_HEADS,
+    QUANT_GROUP,
     LayerCacheDesc,
     LeankError,
     check,
@@ -39,6 +40,7 @@ __all__ = [
     "LeankError",
     "leank_build_mask",
     "leank_plan_layer",
+    "leank_plan_layer_q",
     "leank_pack_k",
     "leank_workspace_bytes",
     "leank_workspace_init",
@@ -93,14 +95,27 @@ def leank_build_mask(alpha, prune_pct, align, stream=None):
 
 def leank_plan_layer(kept_count, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window, max_ctx):
     """Host plan of one layer's cache (head grouping, offsets, byte sizes)."""
+    return leank_plan_layer_q(kept_count, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window,
+                              max_ctx, 0)
+
+
+def leank_plan_layer_q(kept_count, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window,
+                       max_ctx, quant_bits):
+    """Host plan with low-bit middle streams (quant_bits 4 or 8; 0 = bf16)."""
     counts = [int(c) for c in kept_count]
     if len(counts) != n_kv_heads:
         raise ValueError("kept_count must hold one count per KV head")
     arr = (ctypes.c_int32 * max(1, len(counts)))(*counts)
     desc = LayerCacheDesc()
-    status = lib().leank_plan_layer(arr, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window,
-                                    int(max_ctx), ctypes.byref(desc))
-    check(status, "leank_plan_layer")
+    if quant_bits:
+        status = lib().leank_plan_layer_q(arr, batch, n_q_heads, n_kv_heads, head_dim, n_sink,
+                                          window, int(max_ctx), int(quant_bits),
+                                          ctypes.byref(desc))
+        check(status, "leank_plan_layer_q")
+    else:
+        status = lib().leank_plan_layer(arr, batch, n_q_heads, n_kv_heads, head_dim, n_sink,
+                                        window, int(max_ctx), ctypes.byref(desc))
+        check(status, "leank_plan_layer")
     return desc
 
 
@@ -112,10 +127,10 @@ class LayerCache:
     """
 
     def __init__(self, kept_count, kept_idx, batch, n_q_heads, n_kv_heads, n_sink, window,
-                 max_ctx, head_dim=HEAD_DIM, device=None):
+                 max_ctx, head_dim=HEAD_DIM, device=None, quant_bits=0):
         device = _normalize_device(device if device is not None else kept_idx.device)
-        self.desc = leank_plan_layer(kept_count, batch, n_q_heads, n_kv_heads, head_dim,
-                                     n_sink, window, max_ctx)
+        self.desc = leank_plan_layer_q(kept_count, batch, n_q_heads, n_kv_heads, head_dim,
+                                       n_sink, window, max_ctx, quant_bits)
         _require(kept_idx, torch.int16, "kept_idx", ndim=2, device=device)
         if tuple(kept_idx.shape) != (n_kv_heads, head_dim):
             raise ValueError("kept_idx must be [n_kv_heads, head_dim]")
@@ -134,6 +149,13 @@ class LayerCache:
         self.desc.v_sl = self.v_sl.data_ptr()
         self.desc.k_prun = self.k_prun.data_ptr()
         self.desc.v_mid = self.v_mid.data_ptr()
+        self.quant = {}
+        if quant_bits:
+            for name in ("k_q", "k_qp", "k_stage", "v_q", "v_qp"):
+                nbytes = getattr(self.desc, name + "_bytes")
+                t = torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
+                self.quant[name] = t
+                setattr(self.desc, name, t.data_ptr())
         self.length = 0
         self._workspace = None
 
@@ -165,9 +187,14 @@ class LayerCache:
             self._workspace = torch.zeros(max(16, nbytes), dtype=torch.uint8, device=self.device)
         return self._workspace
 
+    @property
+    def quant_bits(self):
+        return self.desc.quant_bits
+
     def nbytes(self):
         d = self.desc
-        return d.k_sl_bytes + d.v_sl_bytes + d.k_prun_bytes + d.v_mid_bytes
+        return (d.k_sl_bytes + d.v_sl_bytes + d.k_prun_bytes + d.v_mid_bytes + d.k_q_bytes
+                + d.k_qp_bytes + d.k_stage_bytes + d.v_q_bytes + d.v_qp_bytes)
 
 
 def _desc(cache):

@@ -15,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libleank.so")
 
 HEAD_DIM = 128
+QUANT_GROUP = 64
 MAX_KV_HEADS = 64
 MAX_GROUP = 8
 CHANNEL_QUANTUM = 8
@@ -55,6 +56,23 @@ class LayerCacheDesc(ctypes.Structure):
         ("v_sl", ctypes.c_void_p),
         ("k_prun", ctypes.c_void_p),
         ("v_mid", ctypes.c_void_p),
+        ("quant_bits", ctypes.c_int32),
+        ("quant_group", ctypes.c_int32),
+        ("k_q_off", ctypes.c_int64 * MAX_KV_HEADS),
+        ("k_qp_off", ctypes.c_int64 * MAX_KV_HEADS),
+        ("k_stage_off", ctypes.c_int64 * MAX_KV_HEADS),
+        ("v_q_off", ctypes.c_int64 * MAX_KV_HEADS),
+        ("v_qp_off", ctypes.c_int64 * MAX_KV_HEADS),
+        ("k_q_bytes", ctypes.c_uint64),
+        ("k_qp_bytes", ctypes.c_uint64),
+        ("k_stage_bytes", ctypes.c_uint64),
+        ("v_q_bytes", ctypes.c_uint64),
+        ("v_qp_bytes", ctypes.c_uint64),
+        ("k_q", ctypes.c_void_p),
+        ("k_qp", ctypes.c_void_p),
+        ("k_stage", ctypes.c_void_p),
+        ("v_q", ctypes.c_void_p),
+        ("v_qp", ctypes.c_void_p),
     ]
 
 
@@ -72,6 +90,10 @@ _SIGNATURES = {
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                         ctypes.POINTER(LayerCacheDesc)]),
+    "leank_plan_layer_q": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                          ctypes.c_int32, ctypes.POINTER(LayerCacheDesc)]),
     "leank_pack_k": (ctypes.c_int, [ctypes.POINTER(LayerCacheDesc), ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_void_p]),

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libleank.so")
-SOURCES = ["plan.hip", "mask.hip", "pack.hip", "decode.hip", "analysis.hip"] + [f"decode_g{g}.hip" for g in range(1, 9)]
+SOURCES = ["plan.hip", "mask.hip", "pack.hip", "quant.hip", "decode.hip", "analysis.hip"] + [f"decode_g{g}.hip" for g in range(1, 9)]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms (v_pk_fma_f32 and friends) are switched off for the

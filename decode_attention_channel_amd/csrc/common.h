@@ -58,6 +58,9 @@ struct WorkPlan {
 };
 
 int validate_cache(const leank_layer_cache* c, bool need_buffers);
+// HBM bytes one middle row of a live head with `kept` channels streams
+// (bf16 or low-bit layout, K group parameters not counted).
+int64_t middle_row_bytes(const leank_layer_cache* c, int kept);
 // ctx_len: cached rows the items cover (0 allowed in a step, step = 1).
 int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPlan* plan);
 

@@ -59,6 +59,7 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
                 float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
   int st = validate_cache(c, true);
   if (st != LEANK_OK) return st;
+  if (c->quant_bits != 0) return LEANK_EUNSUPPORTED;  // low-bit middle streams: not read here yet
   if (!q || !out || !aligned16(q) || !aligned16(out)) return LEANK_EINVAL;
   if (x.step) {
     if (!x.k_new || !x.v_new || !aligned16(x.k_new) || !aligned16(x.v_new)) return LEANK_EINVAL;

@@ -8,7 +8,7 @@
 // 16 bytes apart.  The kept-channel gather into K_prun reads the source
 // word of each kept channel from the lane that holds it (ds_bpermute).
 
-#include "common.h"
+#include "quant.h"
 
 namespace leank {
 namespace {
@@ -34,6 +34,8 @@ struct PackParams {
   uint32_t* k_prun;
   uint16_t* v_mid;
   const int16_t* kept_idx;
+  int32_t ring_only;   // low-bit cache: middle rows are written by the quantizing kernels
+  int32_t pad0;
   int64_t t_old;       // tokens in the cache before the append
   int64_t t_new;       // tokens after it
   int64_t n_new;
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(64 * kUnitsPerBlock) void pack_kernel(const PackPar
     return;
   }
   if (p.mode == kPlace && pos < t_new - p.window) {
-    write_middle(p, b, h, pos - p.n_sink, kw, vw, lane);  // already outside the window
+    if (!p.ring_only) write_middle(p, b, h, pos - p.n_sink, kw, vw, lane);  // already outside the window
     return;
   }
   const int64_t slot = p.n_sink + (pos - p.n_sink) % p.window;
@@ -195,6 +197,17 @@ extern "C" int leank_pack_k(const leank_layer_cache* c, const void* k_new, const
   const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
+  if (c->quant_bits != 0) {
+    // low-bit middle: one token per call, or a prefill into an empty cache
+    if (n_new == 1) return quant_append_one(c, k_new, v_new, pos0, s);
+    if (pos0 != 0) return LEANK_EUNSUPPORTED;
+    p.ring_only = 1;
+    p.mode = n_new <= c->window ? kFused : kPlace;
+    st = launch(p, n_new, pairs, s);  // sink and window rows
+    if (st != LEANK_OK) return st;
+    return quant_pack_bulk(c, k_new, v_new, n_new, s);
+  }
+
   if (c->window > 0 && n_new <= c->window) {
     p.mode = kFused;
     return launch(p, n_new, pairs, s);
@@ -224,6 +237,7 @@ extern "C" int leank_pack_k_rows(const leank_layer_cache* c, const void* k_new, 
   if (n_new == 0) return LEANK_OK;
   if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return LEANK_EINVAL;
   if (n_new > c->max_ctx) return LEANK_ECAPACITY;
+  if (c->quant_bits != 0) return LEANK_EUNSUPPORTED;
 
   PackParams p;
   fill_params(c, k_new, v_new, n_new, &p);

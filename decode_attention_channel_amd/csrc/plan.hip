@@ -59,6 +59,12 @@ void split_rows(int64_t rows, int64_t target_rows, int32_t* n_items, int32_t* ro
 
 }  // namespace
 
+int64_t middle_row_bytes(const leank_layer_cache* c, int kept) {
+  if (c->quant_bits == 0) return 2 * static_cast<int64_t>(kept) + 2 * LEANK_HEAD_DIM;
+  // codes of K and V, the row's V scale and minimum (K parameters are per group)
+  return (static_cast<int64_t>(kept) + LEANK_HEAD_DIM) * c->quant_bits / 8 + 8;
+}
+
 int validate_cache(const leank_layer_cache* c, bool need_buffers) {
   if (!c) return LEANK_EINVAL;
   if (c->head_dim != LEANK_HEAD_DIM) return LEANK_EUNSUPPORTED;
@@ -69,6 +75,9 @@ int validate_cache(const leank_layer_cache* c, bool need_buffers) {
   if (static_cast<int64_t>(c->n_sink) + c->window < 1) return LEANK_EINVAL;
   if (c->max_ctx < 1 || c->max_ctx > INT32_MAX) return LEANK_EINVAL;
   if (c->mid_capacity != std::max<int64_t>(0, c->max_ctx - c->n_sink - c->window)) return LEANK_EINVAL;
+  const bool quant = c->quant_bits != 0;
+  if (quant && c->quant_bits != 4 && c->quant_bits != 8) return LEANK_EINVAL;
+  if (quant && c->quant_group != LEANK_QUANT_GROUP) return LEANK_EINVAL;
   int live = 0;
   for (int h = 0; h < c->n_kv_heads; ++h) {
     int k = c->kept_count[h];
@@ -76,17 +85,35 @@ int validate_cache(const leank_layer_cache* c, bool need_buffers) {
     if (k % LEANK_CHANNEL_QUANTUM) return LEANK_EUNSUPPORTED;
     if (k > 0) {
       ++live;
-      if (c->k_prun_off[h] < 0 || c->v_mid_off[h] < 0) return LEANK_EINVAL;
-      if (c->k_prun_off[h] % LEANK_CHANNEL_QUANTUM || c->v_mid_off[h] % (LEANK_HEAD_DIM * LEANK_V_BLOCK))
-        return LEANK_EINVAL;
+      if (!quant) {
+        if (c->k_prun_off[h] < 0 || c->v_mid_off[h] < 0) return LEANK_EINVAL;
+        if (c->k_prun_off[h] % LEANK_CHANNEL_QUANTUM || c->v_mid_off[h] % (LEANK_HEAD_DIM * LEANK_V_BLOCK))
+          return LEANK_EINVAL;
+      } else {
+        if (c->k_q_off[h] < 0 || c->k_qp_off[h] < 0 || c->k_stage_off[h] < 0 ||
+            c->v_q_off[h] < 0 || c->v_qp_off[h] < 0)
+          return LEANK_EINVAL;
+        // 16-byte aligned code and parameter segments, 8-byte aligned row parameters
+        if (c->k_q_off[h] % 16 || c->k_qp_off[h] % 4 || c->k_stage_off[h] % 8 ||
+            c->v_q_off[h] % 16 || c->v_qp_off[h] % 2)
+          return LEANK_EINVAL;
+      }
     }
   }
   if (live != c->n_live) return LEANK_EINVAL;
   if (need_buffers) {
     if (!c->k_sl || !c->v_sl || !c->kept_idx) return LEANK_EINVAL;
     if (!aligned16(c->k_sl) || !aligned16(c->v_sl)) return LEANK_EINVAL;
-    if (c->k_prun_bytes && (!c->k_prun || !aligned16(c->k_prun))) return LEANK_EINVAL;
-    if (c->v_mid_bytes && (!c->v_mid || !aligned16(c->v_mid))) return LEANK_EINVAL;
+    if (!quant) {
+      if (c->k_prun_bytes && (!c->k_prun || !aligned16(c->k_prun))) return LEANK_EINVAL;
+      if (c->v_mid_bytes && (!c->v_mid || !aligned16(c->v_mid))) return LEANK_EINVAL;
+    } else {
+      const void* bufs[5] = {c->k_q, c->k_qp, c->k_stage, c->v_q, c->v_qp};
+      const uint64_t sizes[5] = {c->k_q_bytes, c->k_qp_bytes, c->k_stage_bytes, c->v_q_bytes,
+                                 c->v_qp_bytes};
+      for (int i = 0; i < 5; ++i)
+        if (sizes[i] && (!bufs[i] || !aligned16(bufs[i]))) return LEANK_EINVAL;
+    }
   }
   return LEANK_OK;
 }
@@ -102,7 +129,7 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPl
   int64_t stream_bytes = static_cast<int64_t>(c->batch) * c->n_kv_heads * w->t_sl * 4 * LEANK_HEAD_DIM;
   for (int h = 0; h < c->n_kv_heads; ++h)
     if (c->kept_count[h] > 0)
-      stream_bytes += static_cast<int64_t>(c->batch) * w->t_mid * (2 * c->kept_count[h] + 2 * LEANK_HEAD_DIM);
+      stream_bytes += static_cast<int64_t>(c->batch) * w->t_mid * middle_row_bytes(c, c->kept_count[h]);
   const int64_t target = std::min(kItemBytesMax, std::max(kItemBytesMin,
                                   stream_bytes / (kTargetCUs * LEANK_ITEMS_PER_CU)));
 
@@ -121,7 +148,7 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPl
     w->head_base[h] = base;
     const int kept = c->kept_count[h];
     if (kept > 0) {
-      const int64_t row_bytes = 2 * kept + 2 * LEANK_HEAD_DIM;
+      const int64_t row_bytes = middle_row_bytes(c, kept);
       split_rows(w->t_mid, row_target(row_bytes, kItemBytesMin), &n32, &rows32, &b);
       bound_per_b += b;
       split_rows(w->t_mid, row_target(row_bytes, target), &w->n_mid[h], &w->mid_rows[h], &unused_n);
@@ -210,6 +237,55 @@ extern "C" int leank_plan_layer(const int32_t* kept_count_host, int32_t batch, i
   return LEANK_OK;
 }
 
+extern "C" int leank_plan_layer_q(const int32_t* kept_count_host, int32_t batch,
+                                  int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                  int32_t n_sink, int32_t window, int64_t max_ctx,
+                                  int32_t quant_bits, leank_layer_cache* out) {
+  if (quant_bits != 0 && quant_bits != 4 && quant_bits != 8) return LEANK_EUNSUPPORTED;
+  if (!out) return LEANK_EINVAL;
+  leank_layer_cache c;
+  int st = leank_plan_layer(kept_count_host, batch, n_q_heads, n_kv_heads, head_dim, n_sink,
+                            window, max_ctx, &c);
+  if (st != LEANK_OK || quant_bits == 0) {
+    if (st == LEANK_OK) *out = c;
+    return st;
+  }
+  c.quant_bits = quant_bits;
+  c.quant_group = LEANK_QUANT_GROUP;
+  const int64_t groups = (c.mid_capacity + LEANK_QUANT_GROUP - 1) / LEANK_QUANT_GROUP;
+  const int64_t g_rows = groups * LEANK_QUANT_GROUP;
+  int64_t kq = 0, kqp = 0, ks = 0, vq = 0, vqp = 0;
+  for (int h = 0; h < n_kv_heads; ++h) {
+    c.k_prun_off[h] = c.v_mid_off[h] = -1;
+    c.k_q_off[h] = c.k_qp_off[h] = c.k_stage_off[h] = c.v_q_off[h] = c.v_qp_off[h] = -1;
+  }
+  for (int n = 0; n < n_kv_heads; ++n) {
+    const int h = c.group_order[n];
+    const int64_t kept = c.kept_count[h];
+    if (kept <= 0) continue;
+    c.k_q_off[h] = kq;
+    c.k_qp_off[h] = kqp;
+    c.k_stage_off[h] = ks;
+    c.v_q_off[h] = vq;
+    c.v_qp_off[h] = vqp;
+    kq += static_cast<int64_t>(batch) * g_rows * kept * quant_bits / 8;
+    kqp += static_cast<int64_t>(batch) * groups * kept * 2;
+    ks += static_cast<int64_t>(batch) * LEANK_QUANT_GROUP * kept;
+    vq += static_cast<int64_t>(batch) * v_rows(c.mid_capacity) * LEANK_HEAD_DIM * quant_bits / 8;
+    vqp += static_cast<int64_t>(batch) * c.mid_capacity * 2;
+  }
+  c.k_prun_bytes = c.v_mid_bytes = 0;
+  c.k_q_bytes = static_cast<uint64_t>(kq);
+  c.k_qp_bytes = static_cast<uint64_t>(kqp) * 4;
+  c.k_stage_bytes = static_cast<uint64_t>(ks) * 2;
+  c.v_q_bytes = static_cast<uint64_t>(vq);
+  c.v_qp_bytes = static_cast<uint64_t>(vqp) * 4;
+  st = validate_cache(&c, false);
+  if (st != LEANK_OK) return st;
+  *out = c;
+  return LEANK_OK;
+}
+
 extern "C" int leank_workspace_bytes(const leank_layer_cache* cache, int64_t ctx_len,
                                      size_t* bytes_out) {
   int st = validate_cache(cache, false);
@@ -235,8 +311,19 @@ extern "C" int leank_decode_bytes(const leank_layer_cache* c, int64_t ctx_len, i
   for (int h = 0; h < c->n_kv_heads; ++h) kept_sum += c->kept_count[h];
   int64_t bytes = bq * 2 + bq * 4;
   bytes += 2 * static_cast<int64_t>(c->batch) * c->n_kv_heads * t_sl * LEANK_HEAD_DIM * 2;
-  bytes += static_cast<int64_t>(c->batch) * t_mid * kept_sum * 2;
-  bytes += static_cast<int64_t>(c->batch) * c->n_live * t_mid * LEANK_HEAD_DIM * 2;
+  if (c->quant_bits == 0) {
+    bytes += static_cast<int64_t>(c->batch) * t_mid * kept_sum * 2;
+    bytes += static_cast<int64_t>(c->batch) * c->n_live * t_mid * LEANK_HEAD_DIM * 2;
+  } else {
+    // complete K groups as codes + per-channel (scale, min); the open group bf16;
+    // every middle V row as codes + its (scale, min)
+    const int64_t q = c->quant_bits;
+    const int64_t groups = t_mid / LEANK_QUANT_GROUP;
+    const int64_t stage = t_mid - groups * LEANK_QUANT_GROUP;
+    bytes += static_cast<int64_t>(c->batch) *
+             (groups * LEANK_QUANT_GROUP * kept_sum * q / 8 + groups * kept_sum * 8 + stage * kept_sum * 2);
+    bytes += static_cast<int64_t>(c->batch) * c->n_live * t_mid * (LEANK_HEAD_DIM * q / 8 + 8);
+  }
   *bytes_out = bytes;
   return LEANK_OK;
 }

@@ -39,12 +39,13 @@
 extern "C" {
 #endif
 
-#define LEANK_ABI_VERSION 3
+#define LEANK_ABI_VERSION 4
 #define LEANK_HEAD_DIM 128      /* the only head_dim the kernels implement   */
 #define LEANK_MAX_KV_HEADS 64   /* per-layer KV heads a cache plan can hold  */
 #define LEANK_MAX_GROUP 8       /* query heads per KV head the kernels take  */
 #define LEANK_CHANNEL_QUANTUM 8 /* kept counts must be multiples of this     */
 #define LEANK_V_BLOCK 8         /* V rows per transposed storage block        */
+#define LEANK_QUANT_GROUP 64    /* middle rows per K quantization group       */
 
 typedef enum {
   LEANK_OK = 0,
@@ -123,6 +124,34 @@ int leank_build_mask(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
  * Live heads are grouped by kept count (descending, then head id): their
  * segments follow `group_order`, so heads of one width form one contiguous
  * region (LeanK page, section 3.1 item 1).
+ *
+ * Low-bit middle streams (leank_plan_layer_q, quant_bits 4 or 8; LeanK page
+ * section 4.2 and its deployment notes: quantize after prune and
+ * reorganise; white paper section 5.2.1: INT8/INT4 codes, KIVI's per-channel
+ * K and per-token V).  The middle of a live head is then held in five
+ * buffers instead of k_prun / v_mid (k_prun_bytes = v_mid_bytes = 0):
+ *
+ *   k_q      per live head at byte offset k_q_off[h]: codes of the complete
+ *            K groups, row-major [batch][G64][kept_count[h]] (G64 =
+ *            ceil(mid_capacity / 64) * 64 rows); 4-bit codes two per byte,
+ *            channel 2i in the low nibble of byte i.
+ *   k_qp     per live head at float offset k_qp_off[h]: float32
+ *            [batch][G64 / 64][kept_count[h]][2] = (scale, minimum) of each
+ *            channel over each group of 64 middle rows.
+ *   k_stage  per live head at element offset k_stage_off[h]: bf16
+ *            [batch][64][kept_count[h]], the rows of the group that is not
+ *            complete yet (middle row r in stage row r % 64).
+ *   v_q      per live head at byte offset v_q_off[h]: V codes in 8-row blocks
+ *            [batch][ceil(mid_capacity / 8)][128][8 codes]: 8-bit, byte
+ *            ((r / 8) * 128 + c) * 8 + r % 8; 4-bit, 4 bytes per (block,
+ *            channel), byte k holding row 2k (low nibble) and 2k + 1.
+ *   v_qp     per live head at float offset v_qp_off[h]: float32
+ *            [batch][mid_capacity][2] = (scale, minimum) of each middle row.
+ *
+ * A value is code * scale + minimum.  Codes: minimum and scale = (max -
+ * min) / (2^bits - 1) of the group, code = round-half-even((x - min) /
+ * scale) clamped to [0, 2^bits - 1] (0 when scale is 0), decided in IEEE
+ * float32.  K and V must be finite.  Sink and window rows stay bf16.
  */
 typedef struct leank_layer_cache {
   int32_t batch;
@@ -149,6 +178,25 @@ typedef struct leank_layer_cache {
   void* v_sl;
   void* k_prun;
   void* v_mid;
+  /* low-bit middle streams (filled by leank_plan_layer_q; zero otherwise) */
+  int32_t quant_bits;                        /* 0 (bf16 middle), 4 or 8 */
+  int32_t quant_group;                       /* LEANK_QUANT_GROUP, or 0 */
+  int64_t k_q_off[LEANK_MAX_KV_HEADS];       /* bytes; -1 for dead heads */
+  int64_t k_qp_off[LEANK_MAX_KV_HEADS];      /* floats; -1 for dead heads */
+  int64_t k_stage_off[LEANK_MAX_KV_HEADS];   /* elements; -1 for dead heads */
+  int64_t v_q_off[LEANK_MAX_KV_HEADS];       /* bytes; -1 for dead heads */
+  int64_t v_qp_off[LEANK_MAX_KV_HEADS];      /* floats; -1 for dead heads */
+  uint64_t k_q_bytes;
+  uint64_t k_qp_bytes;
+  uint64_t k_stage_bytes;
+  uint64_t v_q_bytes;
+  uint64_t v_qp_bytes;
+  /* set by the caller (16-byte aligned) when quant_bits != 0: */
+  void* k_q;
+  void* k_qp;
+  void* k_stage;
+  void* v_q;
+  void* v_qp;
 } leank_layer_cache;
 
 /*
@@ -165,6 +213,20 @@ int leank_plan_layer(const int32_t* kept_count_host, int32_t batch,
                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                      int32_t n_sink, int32_t window, int64_t max_ctx,
                      leank_layer_cache* cache_out);
+
+/*
+ * leank_plan_layer_q -- leank_plan_layer for a cache whose middle is held
+ * in low-bit streams (quant_bits 4 or 8; 0 gives the bf16 plan).  Same
+ * requirements; the caller allocates k_sl, v_sl and the five low-bit
+ * buffers.  On such a cache leank_pack_k takes a bulk prefill into an
+ * empty cache (pos0 == 0) or one token per call (n_new == 1);
+ * leank_decode_attn and leank_decode_step read the low-bit streams.  The
+ * ragged (_rows) entry points return LEANK_EUNSUPPORTED for it.
+ */
+int leank_plan_layer_q(const int32_t* kept_count_host, int32_t batch,
+                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                       int32_t n_sink, int32_t window, int64_t max_ctx,
+                       int32_t quant_bits, leank_layer_cache* cache_out);
 
 /*
  * leank_pack_k -- append n_new tokens at positions [pos0, pos0 + n_new)

@@ -69,7 +69,7 @@ def _unblock_v(flat, rows):
     return blocks.transpose(0, 2, 1).reshape(-1, 128)[:rows]
 
 
-def read_pair(cache, b, h, n_mid=None):
+def read_pair(cache, b, h, n_mid=None, ring_only=False):
     """Host uint16 copies of one (batch row, KV head) pair's cache rows:
     ring K/V [slots, 128], K_prun [n_mid, kept] and V_mid [n_mid, 128] (None
     for a fully pruned head).  Slices on the GPU before copying."""
@@ -83,7 +83,7 @@ def read_pair(cache, b, h, n_mid=None):
     vbase = ((b * d.n_kv_heads) + h) * vs * 128
     ring_v = _unblock_v(bf16_bits(cache.v_sl[vbase: vbase + vs * 128]), slots)
     c = d.kept_count[h]
-    if c == 0:
+    if c == 0 or ring_only:
         return ring_k, ring_v, None, None
     ko = d.k_prun_off[h] + b * mid_cap * c
     k_prun = bf16_bits(cache.k_prun[ko: ko + n_mid * c]).reshape(n_mid, c)
@@ -129,3 +129,69 @@ def oracle_outputs(q, k, v, mask, n_sink, window, pairs=None):
     """Oracle decode for torch bf16 tensors (host copies of the same bits)."""
     return oracle.decode(bf16_bits(q), bf16_bits(k), bf16_bits(v), mask, n_sink, window,
                          pairs=pairs)
+
+
+def _unpack_nibbles(b):
+    """uint8 bytes -> codes, low nibble first."""
+    b = np.asarray(b, dtype=np.uint8)
+    out = np.empty(b.size * 2, dtype=np.uint8)
+    out[0::2] = b & 0xF
+    out[1::2] = b >> 4
+    return out
+
+
+def read_pair_q(cache, b, h, t_mid):
+    """Host copies of one (batch row, live KV head) pair's low-bit middle
+    for t_mid middle rows: a dict shaped like oracle.quantize_middle."""
+    d = cache.desc
+    bits, c = d.quant_bits, d.kept_count[h]
+    g_rows = -(-d.mid_capacity // 64) * 64
+    n_full = t_mid // 64
+    q = {name: t.cpu().numpy() for name, t in cache.quant.items()}
+    k0 = d.k_q_off[h] + b * g_rows * c * bits // 8
+    raw = q["k_q"][k0: k0 + n_full * 64 * c * bits // 8]
+    k_codes = (raw if bits == 8 else _unpack_nibbles(raw)).reshape(n_full * 64, c)
+    kp = q["k_qp"].view(np.float32)
+    p0 = d.k_qp_off[h] + b * (g_rows // 64) * c * 2
+    kpar = kp[p0: p0 + n_full * c * 2].reshape(n_full, c, 2)
+    st = q["k_stage"].view(np.uint16)
+    s0 = d.k_stage_off[h] + b * 64 * c
+    k_stage = st[s0: s0 + (t_mid - n_full * 64) * c].reshape(-1, c)
+    vrows = _v_rows(d.mid_capacity)
+    blk_bytes = 128 * 8 * bits // 8
+    v0 = d.v_q_off[h] + b * (vrows // 8) * blk_bytes
+    nb = -(-t_mid // 8)
+    vraw = q["v_q"][v0: v0 + nb * blk_bytes]
+    codes = vraw if bits == 8 else _unpack_nibbles(vraw)
+    v_codes = codes.reshape(nb, 128, 8).transpose(0, 2, 1).reshape(-1, 128)[:t_mid]
+    vp = q["v_qp"].view(np.float32)
+    q0 = d.v_qp_off[h] + b * d.mid_capacity * 2
+    vpar = vp[q0: q0 + t_mid * 2].reshape(t_mid, 2)
+    return {"k_codes": k_codes, "k_scale": kpar[..., 0], "k_lo": kpar[..., 1], "k_stage": k_stage,
+            "v_codes": v_codes, "v_scale": vpar[:, 0], "v_lo": vpar[:, 1]}
+
+
+def assert_quant_cache_matches(cache, k_bits, v_bits, mask, pairs=None):
+    """Bit-exact comparison of a low-bit cache (ring and middle streams) with
+    the oracle's packing of the full context k_bits/v_bits [B, H, T, d]."""
+    d = cache.desc
+    kept_count, kept_idx = kept_from_mask(mask)
+    if pairs is None:
+        pairs = [(b, h) for b in range(d.batch) for h in range(d.n_kv_heads)]
+    ref = oracle.pack_reference_q(k_bits, v_bits, kept_count, kept_idx, d.n_sink, d.window,
+                                  d.quant_bits)
+    for (b, h) in pairs:
+        ring_k, ring_v, _, _ = read_pair(cache, b, h, ring_only=True)
+        for slot, pos in enumerate(ref["slot_pos"]):
+            if pos < 0:
+                continue
+            assert np.array_equal(ring_k[slot], ref["ring_k"][b, h, slot]), (b, h, slot)
+            assert np.array_equal(ring_v[slot], ref["ring_v"][b, h, slot]), (b, h, slot)
+        if kept_count[h] == 0:
+            continue
+        want = ref["mid_q"][h][b]
+        got = read_pair_q(cache, b, h, want["v_codes"].shape[0])
+        for key in ("k_codes", "k_stage", "v_codes"):
+            assert np.array_equal(got[key], want[key]), (b, h, key)
+        for key in ("k_scale", "k_lo", "v_scale", "v_lo"):
+            assert np.array_equal(got[key].view(np.uint32), want[key].view(np.uint32)), (b, h, key)

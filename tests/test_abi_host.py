@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert "leank_build_mask" in names and "leank_pack_k" in names and "leank_decode_attn" in names
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.leank_abi_version() == 3
+    assert lib.leank_abi_version() == 4
     assert lib.leank_layer_cache_size() == ctypes.sizeof(_lib.LayerCacheDesc)
 
 
@@ -206,3 +206,48 @@ def test_build_mask_rejected_before_launch():
     assert L.leank_build_mask(p, 1, 2, 128, 50, 48, p, p, p, None) == _lib.EINVAL
     assert L.leank_build_mask(p, 1, 2, 128, 50, 0, p, p, p, None) == _lib.EINVAL
     assert L.leank_build_mask(p, 0, 2, 128, 50, 32, p, p, p, None) == _lib.EINVAL
+
+
+def test_plan_layer_q_layout():
+    kept = [32, 0, 64, 8]
+    batch, max_ctx, n_sink, window = 3, 1000, 4, 61
+    for bits in (4, 8):
+        d = dac.leank_plan_layer_q(kept, batch, 8, 4, 128, n_sink, window, max_ctx, bits)
+        mid_cap = max_ctx - n_sink - window
+        g_rows = -(-mid_cap // 64) * 64
+        v_rows = -(-mid_cap // 8) * 8
+        assert d.quant_bits == bits and d.quant_group == 64
+        assert d.k_prun_bytes == 0 and d.v_mid_bytes == 0
+        off = dict(kq=0, kqp=0, ks=0, vq=0, vqp=0)
+        for h in [d.group_order[n] for n in range(4)]:
+            c = kept[h]
+            if c == 0:
+                assert d.k_q_off[h] == d.v_q_off[h] == d.k_stage_off[h] == -1
+                continue
+            assert (d.k_q_off[h], d.k_qp_off[h], d.k_stage_off[h], d.v_q_off[h], d.v_qp_off[h]) == \
+                (off["kq"], off["kqp"], off["ks"], off["vq"], off["vqp"])
+            off["kq"] += batch * g_rows * c * bits // 8
+            off["kqp"] += batch * (g_rows // 64) * c * 2
+            off["ks"] += batch * 64 * c
+            off["vq"] += batch * v_rows * 128 * bits // 8
+            off["vqp"] += batch * mid_cap * 2
+        assert d.k_q_bytes == off["kq"] and d.k_qp_bytes == 4 * off["kqp"]
+        assert d.k_stage_bytes == 2 * off["ks"] and d.v_q_bytes == off["vq"]
+        assert d.v_qp_bytes == 4 * off["vqp"]
+
+
+def test_plan_layer_q_rejects_other_widths():
+    for bits in (1, 2, 3, 16):
+        with pytest.raises(dac.LeankError) as err:
+            dac.leank_plan_layer_q([32], 1, 1, 1, 128, 4, 8, 100, bits)
+        assert err.value.status == _lib.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_decode_bytes_q_match_oracle(bits):
+    kept = [32, 0, 64, 128]
+    n_sink, window, max_ctx = 4, 16, 700
+    d = dac.leank_plan_layer_q(kept, 2, 8, 4, 128, n_sink, window, max_ctx, bits)
+    for ctx in (1, 4, 20, 21, 83, 84, 85, 148, 700):
+        assert dac.leank_decode_bytes(d, ctx) == oracle.decode_traffic_bytes_q(
+            2, 8, 4, 128, ctx, n_sink, window, kept, bits), ctx
