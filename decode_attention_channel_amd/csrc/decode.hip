@@ -5,19 +5,51 @@
 // decode_g8.hip.
 
 #include "decode_kernels.h"
+#include "quant.h"
 
 namespace leank {
 
-extern template int launch_decode<1>(const DecodeParams&, int64_t, int64_t, hipStream_t);
-extern template int launch_decode<2>(const DecodeParams&, int64_t, int64_t, hipStream_t);
-extern template int launch_decode<3>(const DecodeParams&, int64_t, int64_t, hipStream_t);
-extern template int launch_decode<4>(const DecodeParams&, int64_t, int64_t, hipStream_t);
-extern template int launch_decode<5>(const DecodeParams&, int64_t, int64_t, hipStream_t);
-extern template int launch_decode<6>(const DecodeParams&, int64_t, int64_t, hipStream_t);
-extern template int launch_decode<7>(const DecodeParams&, int64_t, int64_t, hipStream_t);
-extern template int launch_decode<8>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+#define LEANK_EXTERN_DECODE(G)                                                              \
+  extern template int launch_decode<G, 0>(const DecodeParams&, int64_t, int64_t, hipStream_t); \
+  extern template int launch_decode<G, 4>(const DecodeParams&, int64_t, int64_t, hipStream_t); \
+  extern template int launch_decode<G, 8>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+LEANK_EXTERN_DECODE(1)
+LEANK_EXTERN_DECODE(2)
+LEANK_EXTERN_DECODE(3)
+LEANK_EXTERN_DECODE(4)
+LEANK_EXTERN_DECODE(5)
+LEANK_EXTERN_DECODE(6)
+LEANK_EXTERN_DECODE(7)
+LEANK_EXTERN_DECODE(8)
+#undef LEANK_EXTERN_DECODE
 
 namespace {
+
+// The low-bit segments must follow the canonical layout of
+// leank_plan_layer_q (the kernels derive them from the kept-channel prefix
+// and the live rank of each head).
+bool canonical_quant_layout(const leank_layer_cache* c, int64_t* c_prefix, int64_t* rank) {
+  const int64_t batch = c->batch, bits = c->quant_bits;
+  const int64_t groups = (c->mid_capacity + LEANK_QUANT_GROUP - 1) / LEANK_QUANT_GROUP;
+  const int64_t g_rows = groups * LEANK_QUANT_GROUP;
+  int64_t pre = 0, n = 0;
+  for (int i = 0; i < c->n_kv_heads; ++i) {
+    const int h = c->group_order[i];
+    const int64_t kept = c->kept_count[h];
+    if (h < 0 || h >= c->n_kv_heads) return false;
+    if (kept <= 0) continue;
+    if (c->k_q_off[h] != batch * g_rows * pre * bits / 8 || c->k_qp_off[h] != batch * groups * pre * 2 ||
+        c->k_stage_off[h] != batch * LEANK_QUANT_GROUP * pre ||
+        c->v_q_off[h] != n * batch * v_rows(c->mid_capacity) * LEANK_HEAD_DIM * bits / 8 ||
+        c->v_qp_off[h] != n * batch * c->mid_capacity * 2)
+      return false;
+    c_prefix[h] = pre;
+    rank[h] = n;
+    pre += kept;
+    ++n;
+  }
+  return true;
+}
 
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, int64_t n_words) {
   for (int64_t k = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; k < n_words;
@@ -59,7 +91,12 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
                 float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
   int st = validate_cache(c, true);
   if (st != LEANK_OK) return st;
-  if (c->quant_bits != 0) return LEANK_EUNSUPPORTED;  // low-bit middle streams: not read here yet
+  const bool quant = c->quant_bits != 0;
+  int64_t q_prefix[LEANK_MAX_KV_HEADS] = {0}, q_rank[LEANK_MAX_KV_HEADS] = {0};
+  if (quant) {
+    if (x.ctx_lens || x.row_pos) return LEANK_EUNSUPPORTED;  // ragged calls: bf16 caches only
+    if (!canonical_quant_layout(c, q_prefix, q_rank)) return LEANK_EINVAL;
+  }
   if (!q || !out || !aligned16(q) || !aligned16(out)) return LEANK_EINVAL;
   if (x.step) {
     if (!x.k_new || !x.v_new || !aligned16(x.k_new) || !aligned16(x.v_new)) return LEANK_EINVAL;
@@ -70,8 +107,22 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
     if (plan_len > c->max_ctx) return LEANK_ECAPACITY;
   }
   if (!(scale > 0.0f) || !isfinite(scale)) return LEANK_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool step = x.step;
+  if (quant && step) {
+    // low-bit middle: the append runs first (one kernel), then the attention
+    // over pos + 1 tokens -- the leaving token is read back as it is stored
+    WorkPlan wq;
+    make_work_plan(c, plan_len + 1, 0, &wq);
+    if (!workspace || !aligned16(workspace) || workspace_bytes < wq.workspace_bytes)
+      return LEANK_EWORKSPACE;
+    st = quant_append_one(c, x.k_new, x.v_new, plan_len, s);
+    if (st != LEANK_OK) return st;
+    step = false;
+    plan_len += 1;
+  }
   WorkPlan w;
-  make_work_plan(c, plan_len, x.step ? 1 : 0, &w);
+  make_work_plan(c, plan_len, step ? 1 : 0, &w);
   if (!workspace || !aligned16(workspace) || workspace_bytes < w.workspace_bytes)
     return LEANK_EWORKSPACE;
   if (w.n_items > INT32_MAX) return LEANK_EUNSUPPORTED;
@@ -113,27 +164,42 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
     max_items = std::max(max_items, w.n_sl_items + w.n_mid[h]);
   p.combine_slices = max_items > 256 ? 8 : max_items > 64 ? 4 : max_items > 16 ? 2 : 1;
   p.qk_scale = scale * kLog2e;
+  p.n_batch = c->batch;
+  if (quant) {
+    p.k_q = static_cast<const uint8_t*>(c->k_q);
+    p.k_qp = static_cast<const float*>(c->k_qp);
+    p.k_stage = static_cast<const uint16_t*>(c->k_stage);
+    p.v_q = static_cast<const uint8_t*>(c->v_q);
+    p.v_qp = static_cast<const float*>(c->v_qp);
+    p.q_groups = (c->mid_capacity + LEANK_QUANT_GROUP - 1) / LEANK_QUANT_GROUP;
+  }
   for (int h = 0; h < c->n_kv_heads; ++h) {
-    p.heads[h].k_off = c->k_prun_off[h];
-    p.heads[h].v_off = c->v_mid_off[h];
+    p.heads[h].k_off = quant ? q_prefix[h] : c->k_prun_off[h];
+    p.heads[h].v_off = quant ? q_rank[h] : c->v_mid_off[h];
     p.heads[h].kept = c->kept_count[h];
     p.heads[h].n_mid = w.n_mid[h];
     p.heads[h].mid_rows = w.mid_rows[h];
     p.heads[h].base = w.head_base[h];
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t n_pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
+  const int qb = c->quant_bits;
+#define LEANK_DISPATCH(G)                                                  \
+  case G:                                                                  \
+    return qb == 8   ? launch_decode<G, 8>(p, w.n_items, n_pairs, s)      \
+           : qb == 4 ? launch_decode<G, 4>(p, w.n_items, n_pairs, s)      \
+                     : launch_decode<G, 0>(p, w.n_items, n_pairs, s);
   switch (w.group) {
-    case 1: return launch_decode<1>(p, w.n_items, n_pairs, s);
-    case 2: return launch_decode<2>(p, w.n_items, n_pairs, s);
-    case 3: return launch_decode<3>(p, w.n_items, n_pairs, s);
-    case 4: return launch_decode<4>(p, w.n_items, n_pairs, s);
-    case 5: return launch_decode<5>(p, w.n_items, n_pairs, s);
-    case 6: return launch_decode<6>(p, w.n_items, n_pairs, s);
-    case 7: return launch_decode<7>(p, w.n_items, n_pairs, s);
-    case 8: return launch_decode<8>(p, w.n_items, n_pairs, s);
+    LEANK_DISPATCH(1)
+    LEANK_DISPATCH(2)
+    LEANK_DISPATCH(3)
+    LEANK_DISPATCH(4)
+    LEANK_DISPATCH(5)
+    LEANK_DISPATCH(6)
+    LEANK_DISPATCH(7)
+    LEANK_DISPATCH(8)
     default: return LEANK_EUNSUPPORTED;
   }
+#undef LEANK_DISPATCH
 }
 
 }  // namespace

@@ -2,4 +2,9 @@
 // translation unit per group size keeps builds parallel).
 #include "decode_kernels.h"
 
-template int leank::launch_decode<6>(const leank::DecodeParams&, int64_t, int64_t, hipStream_t);
+template int leank::launch_decode<6, 0>(const leank::DecodeParams&, int64_t, int64_t,
+                                             hipStream_t);
+template int leank::launch_decode<6, 4>(const leank::DecodeParams&, int64_t, int64_t,
+                                             hipStream_t);
+template int leank::launch_decode<6, 8>(const leank::DecodeParams&, int64_t, int64_t,
+                                             hipStream_t);

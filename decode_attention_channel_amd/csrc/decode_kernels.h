@@ -53,8 +53,15 @@
 #ifndef LEANK_WAVES_PER_EU
 #define LEANK_WAVES_PER_EU 3
 #endif
+#ifndef LEANK_Q_WAVES_PER_EU
+#define LEANK_Q_WAVES_PER_EU 2
+#endif
+// register budget: LEANK_WAVES_PER_EU for bf16 caches, LEANK_Q_WAVES_PER_EU
+// for low-bit middle streams (dequantization needs more live registers)
 #if LEANK_WAVES_PER_EU
-#define LEANK_SPLIT_ATTRS __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(LEANK_WAVES_PER_EU)))
+#define LEANK_SPLIT_ATTRS                  \
+  __launch_bounds__(kThreads) __attribute__( \
+      (amdgpu_waves_per_eu(QB ? LEANK_Q_WAVES_PER_EU : LEANK_WAVES_PER_EU)))
 #else
 #define LEANK_SPLIT_ATTRS __launch_bounds__(kThreads)
 #endif
@@ -72,8 +79,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;
 
 struct DecodeHead {
-  int64_t k_off;   // elements of K_prun, -1 for a dead head
-  int64_t v_off;   // elements of V_mid, -1 for a dead head
+  int64_t k_off;   // elements of K_prun, -1 for a dead head (low-bit: kept channels of the live heads before it)
+  int64_t v_off;   // elements of V_mid, -1 for a dead head (low-bit: its rank among the live heads)
   int32_t kept;
   int32_t n_mid;     // middle items of this head per batch row
   int32_t mid_rows;  // rows per middle item
@@ -114,6 +121,15 @@ struct DecodeParams {
   int32_t partial_stride;
   int32_t combine_slices;  // channel slices per (pair, query head) in the combine
   float qk_scale;          // softmax scale * log2(e)
+  // low-bit middle streams (segments in the canonical layout of leank_plan_layer_q)
+  const uint8_t* k_q;
+  const float* k_qp;
+  const uint16_t* k_stage;
+  const uint8_t* v_q;
+  const float* v_qp;
+  int64_t q_groups;  // K groups per (batch row, head): ceil(mid_cap / 64)
+  int32_t n_batch;
+  int32_t pad_q;
   DecodeHead heads[LEANK_MAX_KV_HEADS];
 };
 
@@ -320,6 +336,291 @@ __device__ __forceinline__ void attend_range(const uint16_t* kb, int kstride, co
 #endif
 }
 
+// ---------------------------------------------------------------- low-bit middle
+//
+// A middle item of a cache with low-bit streams reads, per 32-row tile:
+//   K  codes of a complete 64-row group, dequantized per element with the
+//      group's per-channel (scale, min) into the bf16 B operand; or, in the
+//      group that is not complete yet, the bf16 staging rows as they are;
+//   V  codes of the 8-row blocks, turned into exact bf16 integers (4-bit:
+//      128 + code through a byte permute) for the B operand of the PV
+//      product.  The per-token scale multiplies the weight (p' = p * scale)
+//      and sum_t p_t * min'_t is added to every channel of the head at the
+//      end (min' = min, or min - 128 * scale for 4-bit codes).
+
+// Pointers of one (batch row, live head) pair's low-bit middle.
+struct QSegment {
+  const uint8_t* k_codes;  // row 0 of the pair's K codes
+  const float* k_par;      // group 0 of the pair's (scale, min) pairs
+  const uint16_t* k_stage; // the pair's staging rows
+  const uint8_t* v_codes;  // block 0 of the pair's V codes
+  const float* v_par;      // row 0 of the pair's (scale, min) pairs
+  int full_rows;           // rows in complete groups for this call
+};
+
+template <int QB>
+__device__ __forceinline__ QSegment q_segment(const DecodeParams& p, const DecodeHead& hd, int b,
+                                              int t_mid) {
+  const int64_t c = hd.kept;
+  const int64_t batch_rows = p.n_batch;
+  const int64_t g_rows = p.q_groups * LEANK_QUANT_GROUP;
+  const int64_t v_blocks = p.v_mid_rows / LEANK_V_BLOCK;
+  QSegment q;
+  q.k_codes = p.k_q + (batch_rows * g_rows * hd.k_off + static_cast<int64_t>(b) * g_rows * c) * QB / 8;
+  q.k_par = p.k_qp + (batch_rows * p.q_groups * hd.k_off + static_cast<int64_t>(b) * p.q_groups * c) * 2;
+  q.k_stage = p.k_stage + batch_rows * LEANK_QUANT_GROUP * hd.k_off +
+              static_cast<int64_t>(b) * LEANK_QUANT_GROUP * c;
+  q.v_codes = p.v_q + (hd.v_off * batch_rows * v_blocks + static_cast<int64_t>(b) * v_blocks) *
+                          (LEANK_HEAD_DIM * LEANK_V_BLOCK * QB / 8);
+  q.v_par = p.v_qp + (hd.v_off * batch_rows * p.mid_cap + static_cast<int64_t>(b) * p.mid_cap) * 2;
+  q.full_rows = t_mid / LEANK_QUANT_GROUP * LEANK_QUANT_GROUP;
+  return q;
+}
+
+// Raw operands of one low-bit tile.  kStaged: the tile lies in the K group
+// that is not complete yet, whose rows are read as staged (bf16).
+template <int KB, int QB, bool kStaged>
+struct QTileRegs {
+  u32x4_t kf[kStaged ? 2 : 1][kStaged ? KB : 1];     // staged K rows (bf16)
+  uint32_t kc[2][kStaged ? 1 : KB][QB == 8 ? 2 : 1];  // K codes, 8 channels
+  u32x4_t kpar;                                      // 16 bytes of the group's (scale, min) pairs
+  uint32_t vc[8][QB == 8 ? 2 : 1];                   // V codes, 8 rows of one channel
+  float vs[2], vm[2];                                // (scale, min) of rows 16 j + col
+};
+
+template <int KB, int QB, bool kStaged>
+__device__ __forceinline__ void load_tile_q(const QSegment& q, int c, int t0, int nvalid,
+                                            QTileRegs<KB, QB, kStaged>& tr) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int row = t0 + 16 * j + col;
+      const int ch = 32 * kk + 8 * grp;
+      const bool ok = ch < c && 16 * j + col < nvalid;
+      if constexpr (kStaged) {
+        tr.kf[j][kk] = ok ? load_stream16(q.k_stage + static_cast<int64_t>(row - q.full_rows) * c + ch)
+                          : u32x4_t{0u, 0u, 0u, 0u};
+      } else {
+        const uint8_t* src = q.k_codes + (static_cast<int64_t>(row) * c + ch) * QB / 8;
+        if constexpr (QB == 8) {
+          const uint2 w = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
+          tr.kc[j][kk][0] = w.x;
+          tr.kc[j][kk][QB == 8 ? 1 : 0] = w.y;
+        } else {
+          tr.kc[j][kk][0] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+        }
+      }
+    }
+  }
+  if constexpr (!kStaged) {
+    // the group's (scale, min) pairs: c * 8 bytes, 16 per lane
+    const int g = t0 / LEANK_QUANT_GROUP;
+    tr.kpar = 4 * lane < 2 * c
+                  ? *reinterpret_cast<const u32x4_t*>(q.k_par + (static_cast<int64_t>(g) * c) * 2 + 4 * lane)
+                  : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  const bool v_ok = 8 * grp < nvalid;
+  const uint8_t* vt = q.v_codes + (static_cast<int64_t>(t0 / 8 + grp) * LEANK_HEAD_DIM + col) *
+                                      (LEANK_V_BLOCK * QB / 8);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const uint8_t* src = vt + n * 16 * (LEANK_V_BLOCK * QB / 8);
+    if constexpr (QB == 8) {
+      const uint2 w = v_ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
+      tr.vc[n][0] = w.x;
+      tr.vc[n][QB == 8 ? 1 : 0] = w.y;
+    } else {
+      tr.vc[n][0] = v_ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bool ok = 16 * j + col < nvalid;
+    const float2 pr = ok ? *reinterpret_cast<const float2*>(q.v_par + static_cast<int64_t>(t0 + 16 * j + col) * 2)
+                         : make_float2(0.0f, 0.0f);
+    tr.vs[j] = pr.x;
+    tr.vm[j] = pr.y;
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+}
+
+// code e (0..7) of 8 packed codes
+template <int QB>
+__device__ __forceinline__ float code_f32(const uint32_t (&w)[QB == 8 ? 2 : 1], int e) {
+  if (QB == 8) return static_cast<float>((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
+  return static_cast<float>((w[0] >> (4 * e)) & 0xfu);
+}
+
+// B operand (8 rows of one channel) from 8 V codes as exact bf16 integers
+// (8-bit: the code; 4-bit: 128 + code).
+template <int QB>
+__device__ __forceinline__ u32x4_t v_codes_bf16(const uint32_t (&w)[QB == 8 ? 2 : 1]) {
+  u32x4_t r;
+  if (QB == 8) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = pack_bf16x2(code_f32<QB>(w, 2 * k), code_f32<QB>(w, 2 * k + 1));
+  } else {
+    const uint32_t even = w[0] & 0x0f0f0f0fu;         // rows 0, 2, 4, 6 in bytes 0..3
+    const uint32_t odd = (w[0] >> 4) & 0x0f0f0f0fu;   // rows 1, 3, 5, 7
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // bytes [even byte k, 0, odd byte k, 0], then the exponent of 128
+      const uint32_t sel = static_cast<uint32_t>(k) | (0x0cu << 8) | ((4u + k) << 16) | (0x0cu << 24);
+      r[k] = __builtin_amdgcn_perm(odd, even, sel) | 0x43004300u;
+    }
+  }
+  return r;
+}
+
+template <int G, int KB, int QB, bool kStaged, bool kTail>
+__device__ __forceinline__ void compute_tile_q(QTileRegs<KB, QB, kStaged>& tr, int nvalid,
+                                               const u32x4_t (&qa)[KB], float qk_scale,
+                                               uint16_t* __restrict__ p_lds,
+                                               float* __restrict__ par_lds, WaveState& st,
+                                               float (&vmin)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  f32x4_t s[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+  if constexpr (kStaged) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) s[j] = mfma_bf16(qa[kk], tr.kf[j][kk], s[j]);
+    }
+  } else {
+    // dequantize K (float32 code * scale + min), fed as bf16 hi + lo parts
+    // so that the product keeps about 16 bits of every value; the group's
+    // parameters go through this wavefront's LDS
+    reinterpret_cast<u32x4_t*>(par_lds)[lane] = tr.kpar;
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int ch = 32 * kk + 8 * grp;
+      float sc[8], mn[8];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(par_lds + 2 * (ch + e));
+        sc[e] = pr[0];
+        mn[e] = pr[1];
+        sc[e + 1] = pr[2];
+        mn[e + 1] = pr[3];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        u32x4_t hi, lo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float a = fmaf(code_f32<QB>(tr.kc[j][kk], 2 * w), sc[2 * w], mn[2 * w]);
+          const float b = fmaf(code_f32<QB>(tr.kc[j][kk], 2 * w + 1), sc[2 * w + 1], mn[2 * w + 1]);
+          const __bf16 ah = static_cast<__bf16>(a), bh = static_cast<__bf16>(b);
+          hi[w] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ah)) |
+                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, bh)) << 16);
+          lo[w] = pack_bf16x2(a - static_cast<float>(ah), b - static_cast<float>(bh));
+        }
+        s[j] = mfma_bf16(qa[kk], hi, s[j]);
+        s[j] = mfma_bf16(qa[kk], lo, s[j]);
+      }
+    }
+  }
+
+  float mx[4];
+  bool grow = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float v = s[j][i] * qk_scale;
+      if (kTail && 16 * j + col >= nvalid) v = -INFINITY;
+      s[j][i] = v;
+    }
+    mx[i] = row_max16(fmaxf(s[0][i], s[1][i]));
+    grow |= mx[i] > st.m[i] + kRescaleSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float corr = 1.0f;
+      if (mx[i] > st.m[i] + kRescaleSlack) {
+        corr = st.m[i] == -INFINITY ? 0.0f : fast_exp2(st.m[i] - mx[i]);
+        st.m[i] = mx[i];
+      }
+      st.l[i] *= corr;
+      vmin[i] *= corr;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) st.o[n][i] *= corr;
+    }
+  }
+
+  // per-token V scale folded into the weights; the minimum summed apart
+  float vmin_row[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) vmin_row[j] = QB == 4 ? fmaf(-128.0f, tr.vs[j], tr.vm[j]) : tr.vm[j];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float m_use = st.m[i] == -INFINITY ? 0.0f : st.m[i];
+    const int head = 4 * grp + i;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float pw = fast_exp2(s[j][i] - m_use);  // 0 for a dropped row
+      st.l[i] += pw;
+      const bool valid = !kTail || 16 * j + col < nvalid;
+      vmin[i] = valid ? fmaf(pw, vmin_row[j], vmin[i]) : vmin[i];
+      const float pv = valid ? pw * tr.vs[j] : 0.0f;
+      if (head < G) {
+        const __bf16 hi = static_cast<__bf16>(pv);
+        const __bf16 lo = static_cast<__bf16>(pv - static_cast<float>(hi));
+        p_lds[head * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, hi);
+        p_lds[(16 + head) * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, lo);
+      }
+    }
+  }
+  const u32x4_t pa_hi = *reinterpret_cast<const u32x4_t*>(p_lds + col * kTileRows + 8 * grp);
+  const u32x4_t pa_lo = *reinterpret_cast<const u32x4_t*>(p_lds + (16 + col) * kTileRows + 8 * grp);
+
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const u32x4_t vb = v_codes_bf16<QB>(tr.vc[n]);
+    st.o[n] = mfma_bf16(pa_hi, vb, st.o[n]);
+    st.o[n] = mfma_bf16(pa_lo, vb, st.o[n]);
+  }
+}
+
+// Middle rows [r0, r1) of a low-bit stream.
+template <int G, int KB, int QB>
+__device__ __forceinline__ void attend_range_q(const QSegment& q, int r0, int r1, int c,
+                                               const u32x4_t (&qa)[KB], float qk_scale,
+                                               uint16_t* p_lds, float* par_lds, WaveState& st,
+                                               float (&vmin)[4]) {
+  const int wave = threadIdx.x >> 6;
+  for (int t0 = r0 + wave * kTileRows; t0 < r1; t0 += kWaves * kTileRows) {
+    const int nvalid = r1 - t0;
+    if (t0 >= q.full_rows) {  // tiles never straddle a group boundary
+      QTileRegs<KB, QB, true> cur;
+      load_tile_q<KB, QB, true>(q, c, t0, nvalid, cur);
+      if (nvalid >= kTileRows)
+        compute_tile_q<G, KB, QB, true, false>(cur, kTileRows, qa, qk_scale, p_lds, par_lds, st, vmin);
+      else
+        compute_tile_q<G, KB, QB, true, true>(cur, nvalid, qa, qk_scale, p_lds, par_lds, st, vmin);
+    } else {
+      QTileRegs<KB, QB, false> cur;
+      load_tile_q<KB, QB, false>(q, c, t0, nvalid, cur);
+      if (nvalid >= kTileRows)
+        compute_tile_q<G, KB, QB, false, false>(cur, kTileRows, qa, qk_scale, p_lds, par_lds, st, vmin);
+      else
+        compute_tile_q<G, KB, QB, false, true>(cur, nvalid, qa, qk_scale, p_lds, par_lds, st, vmin);
+    }
+  }
+}
+
 // A operand of the score product for this lane: query head col of the
 // group, kept channels 32 kk + 8 grp .. +7 (zero past c or for col >= G).
 template <int G, int KB>
@@ -402,7 +703,7 @@ __device__ __forceinline__ uint32_t compact_from_lds(const uint16_t* row, const 
          (static_cast<uint32_t>(row[s_idx[j0 + 1] & (LEANK_HEAD_DIM - 1)]) << 16);
 }
 
-template <int G>
+template <int G, int QB>
 __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ float s_acc[kWaves][G][LEANK_HEAD_DIM];
   __shared__ float s_m[kWaves][G];
@@ -418,6 +719,8 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t s_tok_v[LEANK_HEAD_DIM];
   __shared__ __attribute__((aligned(16))) uint16_t s_vblk[2][LEANK_HEAD_DIM * LEANK_V_BLOCK];
   __shared__ float s_tok_s[2][G];
+  // low-bit middle: each wavefront's copy of a K group's (scale, min) pairs
+  __shared__ __attribute__((aligned(16))) float s_par[kWaves][QB ? 2 * LEANK_HEAD_DIM : 4];
 
   const int item = blockIdx.x;
   const int b = item / p.items_per_b;
@@ -483,10 +786,12 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __syncthreads();
 
   WaveState st;
+  float vmin[4];  // low-bit middle: sum of weight * V row minimum, per head
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     st.m[i] = -INFINITY;
     st.l[i] = 0.0f;
+    vmin[i] = 0.0f;
   }
 #pragma unroll
   for (int n = 0; n < 8; ++n) st.o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -523,32 +828,62 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     const int r0 = chunk_id * hd.mid_rows;
     const int r1 = min(t_mid, r0 + hd.mid_rows);
     const int c = hd.kept;
-    const uint16_t* kb = p.k_prun + hd.k_off + static_cast<int64_t>(b) * p.mid_cap * c;
-    const uint16_t* vb = p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM;
-    switch ((c + 31) / 32) {
-      case 1: {
-        u32x4_t qa[1];
-        gather_q<G, 1>(s_q, s_idx, false, c, qa);
-        attend_range<G, 1>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
-        break;
+    if constexpr (QB != 0) {
+      const QSegment q = q_segment<QB>(p, hd, b, t_mid);
+      switch ((c + 31) / 32) {
+        case 1: {
+          u32x4_t qa[1];
+          gather_q<G, 1>(s_q, s_idx, false, c, qa);
+          attend_range_q<G, 1, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+          break;
+        }
+        case 2: {
+          u32x4_t qa[2];
+          gather_q<G, 2>(s_q, s_idx, false, c, qa);
+          attend_range_q<G, 2, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+          break;
+        }
+        case 3: {
+          u32x4_t qa[3];
+          gather_q<G, 3>(s_q, s_idx, false, c, qa);
+          attend_range_q<G, 3, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+          break;
+        }
+        default: {
+          u32x4_t qa[4];
+          gather_q<G, 4>(s_q, s_idx, false, c, qa);
+          attend_range_q<G, 4, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+          break;
+        }
       }
-      case 2: {
-        u32x4_t qa[2];
-        gather_q<G, 2>(s_q, s_idx, false, c, qa);
-        attend_range<G, 2>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
-        break;
-      }
-      case 3: {
-        u32x4_t qa[3];
-        gather_q<G, 3>(s_q, s_idx, false, c, qa);
-        attend_range<G, 3>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
-        break;
-      }
-      default: {
-        u32x4_t qa[4];
-        gather_q<G, 4>(s_q, s_idx, false, c, qa);
-        attend_range<G, 4>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
-        break;
+    } else {
+      const uint16_t* kb = p.k_prun + hd.k_off + static_cast<int64_t>(b) * p.mid_cap * c;
+      const uint16_t* vb = p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM;
+      switch ((c + 31) / 32) {
+        case 1: {
+          u32x4_t qa[1];
+          gather_q<G, 1>(s_q, s_idx, false, c, qa);
+          attend_range<G, 1>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
+          break;
+        }
+        case 2: {
+          u32x4_t qa[2];
+          gather_q<G, 2>(s_q, s_idx, false, c, qa);
+          attend_range<G, 2>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
+          break;
+        }
+        case 3: {
+          u32x4_t qa[3];
+          gather_q<G, 3>(s_q, s_idx, false, c, qa);
+          attend_range<G, 3>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
+          break;
+        }
+        default: {
+          u32x4_t qa[4];
+          gather_q<G, 4>(s_q, s_idx, false, c, qa);
+          attend_range<G, 4>(kb, c, vb, r0, r1, -1, c, qa, p.qk_scale, p_lds, st);
+          break;
+        }
       }
     }
   }
@@ -581,10 +916,12 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float l = row_sum16(st.l[i]);
+    // low-bit middle: every channel of the head gets sum_t p_t * min'_t
+    const float vm = QB != 0 ? row_sum16(vmin[i]) : 0.0f;
     const int head = 4 * grp + i;
     if (head < G) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) s_acc[wave][head][16 * n + col] = st.o[n][i];
+      for (int n = 0; n < 8; ++n) s_acc[wave][head][16 * n + col] = QB != 0 ? st.o[n][i] + vm : st.o[n][i];
       if (col == 0) {
         s_m[wave][head] = st.m[i];
         s_l[wave][head] = l;
@@ -776,10 +1113,10 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodePa
 }
 
 // Launches the split and combine kernels for G query heads per KV head.
-template <int G>
+template <int G, int QB>
 int launch_decode(const DecodeParams& p, int64_t n_items, int64_t n_pairs, hipStream_t s) {
-  hipLaunchKernelGGL(decode_split_kernel<G>, dim3(static_cast<unsigned>(n_items)), dim3(kThreads),
-                     0, s, p);
+  hipLaunchKernelGGL((decode_split_kernel<G, QB>), dim3(static_cast<unsigned>(n_items)),
+                     dim3(kThreads), 0, s, p);
   LEANK_HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(decode_combine_kernel<G>,
                      dim3(static_cast<unsigned>(n_pairs * G * p.combine_slices)), dim3(kThreads),

@@ -96,3 +96,123 @@ def test_quant_pack_rejections():
         dac.leank_pack_k_rows(cache, k[:, :, :1].contiguous(), k[:, :, :1].contiguous(),
                               torch.zeros(1, dtype=torch.int64, device=DEV))
     assert err.value.status == dac._lib.EUNSUPPORTED
+
+
+# ---------------------------------------------------------------- attention over low-bit streams
+
+def _oracle_q(q, k, v, mask, n_sink, window, bits, pairs=None):
+    return oracle.decode_q(bf16_bits(q), bf16_bits(k), bf16_bits(v), mask, n_sink, window, bits,
+                           pairs=pairs)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("group", [1, 4, 7])
+@pytest.mark.parametrize("ctx", [3, 20, 20 + 64, 20 + 64 + 37, 20 + 5 * 64 + 1, 1000])
+def test_decode_matches_oracle(bits, group, ctx):
+    n_sink, window, batch = 4, 16, 2
+    mask = mask_with_counts(np.random.default_rng(ctx + group), [32, 0, 64, 128, 8, 40])
+    n_kv = mask.shape[0]
+    cache = make_qcache(mask, batch, n_kv * group, n_sink, window, 1024, bits)
+    gen = torch.Generator(device=DEV).manual_seed(ctx * 3 + bits)
+    k = random_bf16((batch, n_kv, ctx, 128), gen, scale=2.0)
+    v = random_bf16((batch, n_kv, ctx, 128), gen)
+    q = random_bf16((batch, n_kv * group, 128), gen)
+    case("quant decode", bits, group, ctx)
+    dac.leank_pack_k(cache, k, v)
+    out = dac.leank_decode_attn(cache, q)
+    again = dac.leank_decode_attn(cache, q)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+    assert_close(out.cpu().numpy(), _oracle_q(q, k, v, mask, n_sink, window, bits),
+                 f"bits {bits} G {group} ctx {ctx}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_decode_large_values(bits):
+    """Wide value ranges: codes and the folded minimum over large magnitudes."""
+    n_sink, window, batch, ctx = 4, 16, 1, 400
+    mask = mask_with_counts(np.random.default_rng(3), [32, 64])
+    cache = make_qcache(mask, batch, 8, n_sink, window, ctx, bits)
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    k = random_bf16((batch, 2, ctx, 128), gen, scale=6.0)
+    v = (random_bf16((batch, 2, ctx, 128), gen, scale=30.0).float() + 100.0).to(torch.bfloat16)
+    q = random_bf16((batch, 8, 128), gen, scale=0.5)
+    case("quant decode large", bits)
+    dac.leank_pack_k(cache, k, v)
+    out = dac.leank_decode_attn(cache, q)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), _oracle_q(q, k, v, mask, n_sink, window, bits), "large")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("n_sink,window", [(4, 16), (6, 0)])
+def test_step_on_quant_cache(bits, n_sink, window):
+    """leank_decode_step on a low-bit cache across group completions."""
+    batch, group, t0, steps = 2, 4, n_sink + window + 60, 70
+    mask = mask_with_counts(np.random.default_rng(window + bits), COUNTS)
+    n_kv = mask.shape[0]
+    cache = make_qcache(mask, batch, n_kv * group, n_sink, window, t0 + steps, bits)
+    gen = torch.Generator(device=DEV).manual_seed(window * 5 + bits)
+    k = random_bf16((batch, n_kv, t0 + steps, 128), gen, scale=2.0)
+    v = random_bf16((batch, n_kv, t0 + steps, 128), gen)
+    q = random_bf16((steps, batch, n_kv * group, 128), gen)
+    case("quant step", bits, n_sink, window)
+    dac.leank_pack_k(cache, k[:, :, :t0].contiguous(), v[:, :, :t0].contiguous())
+    outs = []
+    for s in range(steps):
+        outs.append(dac.leank_decode_step(cache, q[s], k[:, :, t0 + s].contiguous(),
+                                          v[:, :, t0 + s].contiguous()))
+    torch.cuda.synchronize()
+    kh, vh = bf16_bits(k), bf16_bits(v)
+    assert_quant_cache_matches(cache, kh, vh, mask)
+    for s in (0, 3, 4, 5, steps - 1):
+        ref = oracle.decode_q(bf16_bits(q[s]), kh[:, :, :t0 + s + 1], vh[:, :, :t0 + s + 1], mask,
+                              n_sink, window, bits)
+        assert_close(outs[s].cpu().numpy(), ref, f"step {s}")
+
+
+def test_ragged_calls_rejected_on_quant_cache():
+    mask = mask_with_counts(np.random.default_rng(4), [32, 0])
+    cache = make_qcache(mask, 2, 4, 4, 8, 100, 8)
+    gen = torch.Generator(device=DEV).manual_seed(4)
+    k = random_bf16((2, 2, 30, 128), gen)
+    q = random_bf16((2, 4, 128), gen)
+    case("quant ragged rejections")
+    dac.leank_pack_k(cache, k, k)
+    with pytest.raises(dac.LeankError) as err:
+        dac.leank_decode_attn_rows(cache, q, torch.full((2,), 30, dtype=torch.int32, device=DEV),
+                                   max_ctx_len=30)
+    assert err.value.status == dac._lib.EUNSUPPORTED
+    with pytest.raises(dac.LeankError) as err:
+        dac.leank_decode_step_rows(cache, q, k[:, :, 0].contiguous(), k[:, :, 0].contiguous(),
+                                   torch.full((2,), 30, dtype=torch.int64, device=DEV),
+                                   max_ctx_len=31)
+    assert err.value.status == dac._lib.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_full_workload_quant_sampled(bits):
+    from synthetic import alpha_for, get_config, make_kv, make_q
+
+    cfg = get_config("llama_b64_4k")
+    om, okc, oki = oracle.build_mask(alpha_for(cfg), cfg.prune_pct, cfg.align)
+    case("quant full workload", bits)
+    cache = dac.LayerCache(okc[0].tolist(), torch.from_numpy(oki[0]).to(DEV), cfg.batch,
+                           cfg.n_q_heads, cfg.n_kv_heads, cfg.n_sink, cfg.window, cfg.ctx,
+                           quant_bits=bits)
+    k, v = make_kv(cfg, 0, device=DEV)
+    t0 = cfg.ctx - 2
+    dac.leank_pack_k(cache, k[:, :, :t0].contiguous(), v[:, :, :t0].contiguous())
+    rng = np.random.default_rng(bits)
+    pairs = sorted({(int(rng.integers(cfg.batch)), int(rng.integers(cfg.n_q_heads)))
+                    for _ in range(16)} | {(0, 0), (cfg.batch - 1, cfg.n_q_heads - 1)})
+    kh, vh = bf16_bits(k), bf16_bits(v)
+    for s in range(2):
+        q = make_q(cfg, 0, step=s + 1, device=DEV)
+        out = dac.leank_decode_step(cache, q, k[:, :, t0 + s].contiguous(),
+                                    v[:, :, t0 + s].contiguous())
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        ref = oracle.decode_q(bf16_bits(q), kh[:, :, :t0 + s + 1], vh[:, :, :t0 + s + 1], om[0],
+                              cfg.n_sink, cfg.window, bits, pairs=pairs)
+        assert_close(np.stack([got[b, j] for b, j in pairs]), ref, f"bits {bits} step {s}")
