@@ -15,9 +15,10 @@ the 256 MB Infinity Cache many times over).
 
 Reported on one JSON line: microseconds per step (value), the step's
 roofline figures from HIP events on the launch stream, the same step as two
-calls (leank_pack_k, then leank_decode_attn), the same kernels at 0%
-pruning, the Qwen2.5-7B-shaped cache, and the CPU oracle's time for the
-same step (a baseline, not a target).
+calls (leank_pack_k, then leank_decode_attn), the same step with the middle
+held in 8-bit and 4-bit streams, the same kernels at 0% pruning, the
+Qwen2.5-7B-shaped cache, and the CPU oracle's time for the same step (a
+baseline, not a target).
 """
 
 import argparse
@@ -50,14 +51,15 @@ def parse_args():
     return ap.parse_args()
 
 
-def setup_caches(cfg, mask_counts, kept_idx_dev, k, v, copies, max_ctx):
+def setup_caches(cfg, mask_counts, kept_idx_dev, k, v, copies, max_ctx, quant_bits=0):
     """`copies` caches holding the first ctx-1 tokens of k, v."""
     import decode_attention_channel_amd as dac
 
     caches = []
     for _ in range(copies):
         cache = dac.LayerCache(mask_counts, kept_idx_dev, cfg.batch, cfg.n_q_heads,
-                               cfg.n_kv_heads, cfg.n_sink, cfg.window, max_ctx)
+                               cfg.n_kv_heads, cfg.n_sink, cfg.window, max_ctx,
+                               quant_bits=quant_bits)
         dac.leank_pack_k(cache, k[:, :, : cfg.ctx - 1].contiguous(),
                          v[:, :, : cfg.ctx - 1].contiguous())
         cache.workspace()
@@ -167,8 +169,9 @@ def summarize(t):
     }
 
 
-def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20, fused=True):
-    """Prepare one workload and time it.  prune_override=0 keeps every channel."""
+def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20, fused=True, quant_bits=0):
+    """Prepare one workload and time it.  prune_override=0 keeps every channel;
+    quant_bits 4 or 8 holds the middle in low-bit streams."""
     import numpy as np
     import torch
 
@@ -187,7 +190,8 @@ def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20, fused=Tru
     new_k = torch.stack([a for a, _ in new])
     new_v = torch.stack([b for _, b in new])
     max_ctx = cfg.ctx + (2 * steps + warmup) // copies + 2
-    caches = setup_caches(cfg, counts, kept_idx[0].contiguous(), k, v, copies, max_ctx)
+    caches = setup_caches(cfg, counts, kept_idx[0].contiguous(), k, v, copies, max_ctx,
+                          quant_bits)
     torch.cuda.synchronize()
     timings = run_steps(cfg, caches, q, new_k, new_v, steps, warmup, fused=fused)
     res = summarize(timings)
@@ -330,8 +334,12 @@ def main():
         qwen = workload(qwen_cfg, copies=args.copies, steps=args.steps, warmup=args.warmup)
         qwen_dense = workload(qwen_cfg, prune_override=0, copies=max(2, args.copies // 2),
                               steps=args.steps, warmup=args.warmup)
+        q8 = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup, quant_bits=8)
+        q4 = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup, quant_bits=4)
         extras = {
             "unfused_pack_then_decode": unfused,
+            "lowbit_middle_8bit": q8,
+            "lowbit_middle_4bit": q4,
             "dense_0pct": dense,
             "speedup_vs_0pct_step": dense["us_per_step"] / main_res["us_per_step"],
             "speedup_fused_vs_unfused_step": unfused["us_per_step"] / main_res["us_per_step"],
