@@ -10,9 +10,9 @@
 namespace leank {
 
 #define LEANK_EXTERN_DECODE(G)                                                              \
-  extern template int launch_decode<G, 0>(const DecodeParams&, int64_t, int64_t, hipStream_t); \
-  extern template int launch_decode<G, 4>(const DecodeParams&, int64_t, int64_t, hipStream_t); \
-  extern template int launch_decode<G, 8>(const DecodeParams&, int64_t, int64_t, hipStream_t);
+  extern template int launch_decode<G, 0>(const DecodeParams&, int64_t, int64_t, int, hipStream_t); \
+  extern template int launch_decode<G, 4>(const DecodeParams&, int64_t, int64_t, int, hipStream_t); \
+  extern template int launch_decode<G, 8>(const DecodeParams&, int64_t, int64_t, int, hipStream_t);
 LEANK_EXTERN_DECODE(1)
 LEANK_EXTERN_DECODE(2)
 LEANK_EXTERN_DECODE(3)
@@ -183,11 +183,13 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   }
   const int64_t n_pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
   const int qb = c->quant_bits;
+  int kb_max = 1;
+  for (int h = 0; h < c->n_kv_heads; ++h) kb_max = std::max(kb_max, (c->kept_count[h] + 31) / 32);
 #define LEANK_DISPATCH(G)                                                  \
   case G:                                                                  \
-    return qb == 8   ? launch_decode<G, 8>(p, w.n_items, n_pairs, s)      \
-           : qb == 4 ? launch_decode<G, 4>(p, w.n_items, n_pairs, s)      \
-                     : launch_decode<G, 0>(p, w.n_items, n_pairs, s);
+    return qb == 8   ? launch_decode<G, 8>(p, w.n_items, n_pairs, kb_max, s)  \
+           : qb == 4 ? launch_decode<G, 4>(p, w.n_items, n_pairs, kb_max, s)  \
+                     : launch_decode<G, 0>(p, w.n_items, n_pairs, kb_max, s);
   switch (w.group) {
     LEANK_DISPATCH(1)
     LEANK_DISPATCH(2)

@@ -3,8 +3,8 @@
 #include "decode_kernels.h"
 
 template int leank::launch_decode<6, 0>(const leank::DecodeParams&, int64_t, int64_t,
-                                             hipStream_t);
+                                             int, hipStream_t);
 template int leank::launch_decode<6, 4>(const leank::DecodeParams&, int64_t, int64_t,
-                                             hipStream_t);
+                                             int, hipStream_t);
 template int leank::launch_decode<6, 8>(const leank::DecodeParams&, int64_t, int64_t,
-                                             hipStream_t);
+                                             int, hipStream_t);

@@ -3,8 +3,8 @@
 #include "decode_kernels.h"
 
 template int leank::launch_decode<8, 0>(const leank::DecodeParams&, int64_t, int64_t,
-                                             hipStream_t);
+                                             int, hipStream_t);
 template int leank::launch_decode<8, 4>(const leank::DecodeParams&, int64_t, int64_t,
-                                             hipStream_t);
+                                             int, hipStream_t);
 template int leank::launch_decode<8, 8>(const leank::DecodeParams&, int64_t, int64_t,
-                                             hipStream_t);
+                                             int, hipStream_t);

@@ -56,12 +56,14 @@
 #ifndef LEANK_Q_WAVES_PER_EU
 #define LEANK_Q_WAVES_PER_EU 2
 #endif
-// register budget: LEANK_WAVES_PER_EU for bf16 caches, LEANK_Q_WAVES_PER_EU
-// for low-bit middle streams (dequantization needs more live registers)
+// register budget: LEANK_WAVES_PER_EU for bf16 caches and for low-bit
+// middle streams whose live heads keep at most 32 channels;
+// LEANK_Q_WAVES_PER_EU for wider low-bit heads (dequantizing more channel
+// blocks keeps more registers live)
 #if LEANK_WAVES_PER_EU
 #define LEANK_SPLIT_ATTRS                  \
   __launch_bounds__(kThreads) __attribute__( \
-      (amdgpu_waves_per_eu(QB ? LEANK_Q_WAVES_PER_EU : LEANK_WAVES_PER_EU)))
+      (amdgpu_waves_per_eu(QB && KBMAX > 1 ? LEANK_Q_WAVES_PER_EU : LEANK_WAVES_PER_EU)))
 #else
 #define LEANK_SPLIT_ATTRS __launch_bounds__(kThreads)
 #endif
@@ -703,7 +705,9 @@ __device__ __forceinline__ uint32_t compact_from_lds(const uint16_t* row, const 
          (static_cast<uint32_t>(row[s_idx[j0 + 1] & (LEANK_HEAD_DIM - 1)]) << 16);
 }
 
-template <int G, int QB>
+// KBMAX: 32-channel blocks of the widest live head (low-bit streams only;
+// 4 for bf16 caches).
+template <int G, int QB, int KBMAX>
 __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ float s_acc[kWaves][G][LEANK_HEAD_DIM];
   __shared__ float s_m[kWaves][G];
@@ -830,30 +834,26 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     const int c = hd.kept;
     if constexpr (QB != 0) {
       const QSegment q = q_segment<QB>(p, hd, b, t_mid);
-      switch ((c + 31) / 32) {
-        case 1: {
-          u32x4_t qa[1];
-          gather_q<G, 1>(s_q, s_idx, false, c, qa);
-          attend_range_q<G, 1, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
-          break;
-        }
-        case 2: {
+      const int kb = (c + 31) / 32;
+      if (KBMAX == 1 || kb == 1) {
+        u32x4_t qa[1];
+        gather_q<G, 1>(s_q, s_idx, false, c, qa);
+        attend_range_q<G, 1, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+      } else if constexpr (KBMAX >= 2) {
+        if (KBMAX == 2 || kb == 2) {
           u32x4_t qa[2];
           gather_q<G, 2>(s_q, s_idx, false, c, qa);
           attend_range_q<G, 2, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
-          break;
-        }
-        case 3: {
-          u32x4_t qa[3];
-          gather_q<G, 3>(s_q, s_idx, false, c, qa);
-          attend_range_q<G, 3, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
-          break;
-        }
-        default: {
-          u32x4_t qa[4];
-          gather_q<G, 4>(s_q, s_idx, false, c, qa);
-          attend_range_q<G, 4, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
-          break;
+        } else if constexpr (KBMAX >= 3) {
+          if (kb == 3) {
+            u32x4_t qa[3];
+            gather_q<G, 3>(s_q, s_idx, false, c, qa);
+            attend_range_q<G, 3, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+          } else {
+            u32x4_t qa[4];
+            gather_q<G, 4>(s_q, s_idx, false, c, qa);
+            attend_range_q<G, 4, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+          }
         }
       }
     } else {
@@ -1113,10 +1113,21 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodePa
 }
 
 // Launches the split and combine kernels for G query heads per KV head.
+// kb_max: 32-channel blocks of the widest live head.
 template <int G, int QB>
-int launch_decode(const DecodeParams& p, int64_t n_items, int64_t n_pairs, hipStream_t s) {
-  hipLaunchKernelGGL((decode_split_kernel<G, QB>), dim3(static_cast<unsigned>(n_items)),
-                     dim3(kThreads), 0, s, p);
+int launch_decode(const DecodeParams& p, int64_t n_items, int64_t n_pairs, int kb_max,
+                  hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(n_items));
+  if constexpr (QB == 0) {
+    (void)kb_max;
+    hipLaunchKernelGGL((decode_split_kernel<G, 0, 4>), grid, dim3(kThreads), 0, s, p);
+  } else if (kb_max > 2) {
+    hipLaunchKernelGGL((decode_split_kernel<G, QB, 4>), grid, dim3(kThreads), 0, s, p);
+  } else if (kb_max == 2) {
+    hipLaunchKernelGGL((decode_split_kernel<G, QB, 2>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((decode_split_kernel<G, QB, 1>), grid, dim3(kThreads), 0, s, p);
+  }
   LEANK_HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(decode_combine_kernel<G>,
                      dim3(static_cast<unsigned>(n_pairs * G * p.combine_slices)), dim3(kThreads),
