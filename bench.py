@@ -16,7 +16,8 @@ the 256 MB Infinity Cache many times over).
 Reported on one JSON line: microseconds per step (value), the step's
 roofline figures from HIP events on the launch stream, the same step as two
 calls (leank_pack_k, then leank_decode_attn), the same step with the middle
-held in 8-bit and 4-bit streams, the same kernels at 0% pruning, the
+held in 8-bit and 4-bit streams and in 64-row pages through a shuffled block
+table, the same kernels at 0% pruning, the
 Qwen2.5-7B-shaped cache, and the CPU oracle's time for the same step (a
 baseline, not a target).
 """
@@ -51,15 +52,26 @@ def parse_args():
     return ap.parse_args()
 
 
-def setup_caches(cfg, mask_counts, kept_idx_dev, k, v, copies, max_ctx, quant_bits=0):
-    """`copies` caches holding the first ctx-1 tokens of k, v."""
+def setup_caches(cfg, mask_counts, kept_idx_dev, k, v, copies, max_ctx, quant_bits=0,
+                 paged=False):
+    """`copies` caches holding the first ctx-1 tokens of k, v.  paged: the
+    middle in 64-row pages, mapped through a seeded random block table."""
+    import numpy as np
+    import torch
+
     import decode_attention_channel_amd as dac
 
     caches = []
-    for _ in range(copies):
+    for n in range(copies):
+        extra = {}
+        if paged:
+            ppr = -(-max(0, max_ctx - cfg.n_sink - cfg.window) // 64)
+            order = np.random.default_rng(77 + n).permutation(cfg.batch * ppr).astype(np.int32)
+            extra = dict(n_pages=cfg.batch * ppr,
+                         block_table=torch.from_numpy(order.reshape(cfg.batch, ppr)).to(k.device))
         cache = dac.LayerCache(mask_counts, kept_idx_dev, cfg.batch, cfg.n_q_heads,
                                cfg.n_kv_heads, cfg.n_sink, cfg.window, max_ctx,
-                               quant_bits=quant_bits)
+                               quant_bits=quant_bits, **extra)
         dac.leank_pack_k(cache, k[:, :, : cfg.ctx - 1].contiguous(),
                          v[:, :, : cfg.ctx - 1].contiguous())
         cache.workspace()
@@ -169,9 +181,11 @@ def summarize(t):
     }
 
 
-def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20, fused=True, quant_bits=0):
+def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20, fused=True, quant_bits=0,
+             paged=False):
     """Prepare one workload and time it.  prune_override=0 keeps every channel;
-    quant_bits 4 or 8 holds the middle in low-bit streams."""
+    quant_bits 4 or 8 holds the middle in low-bit streams; paged holds it in
+    64-row pages through a block table."""
     import numpy as np
     import torch
 
@@ -191,7 +205,7 @@ def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20, fused=Tru
     new_v = torch.stack([b for _, b in new])
     max_ctx = cfg.ctx + (2 * steps + warmup) // copies + 2
     caches = setup_caches(cfg, counts, kept_idx[0].contiguous(), k, v, copies, max_ctx,
-                          quant_bits)
+                          quant_bits, paged)
     torch.cuda.synchronize()
     timings = run_steps(cfg, caches, q, new_k, new_v, steps, warmup, fused=fused)
     res = summarize(timings)
@@ -336,10 +350,12 @@ def main():
                               steps=args.steps, warmup=args.warmup)
         q8 = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup, quant_bits=8)
         q4 = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup, quant_bits=4)
+        paged = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup, paged=True)
         extras = {
             "unfused_pack_then_decode": unfused,
             "lowbit_middle_8bit": q8,
             "lowbit_middle_4bit": q4,
+            "paged_middle_64row_pages": paged,
             "dense_0pct": dense,
             "speedup_vs_0pct_step": dense["us_per_step"] / main_res["us_per_step"],
             "speedup_fused_vs_unfused_step": unfused["us_per_step"] / main_res["us_per_step"],

@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     HEAD_DIM,
     MAX_GROUP,
     MAX_KV_HEADS,
+    PAGE_ROWS,
     QUANT_GROUP,
     LayerCacheDesc,
     LeankError,
@@ -41,6 +42,7 @@ __all__ = [
     "leank_build_mask",
     "leank_plan_layer",
     "leank_plan_layer_q",
+    "leank_plan_layer_paged",
     "leank_pack_k",
     "leank_workspace_bytes",
     "leank_workspace_init",
@@ -99,6 +101,20 @@ def leank_plan_layer(kept_count, batch, n_q_heads, n_kv_heads, head_dim, n_sink,
                               max_ctx, 0)
 
 
+def leank_plan_layer_paged(kept_count, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window,
+                           max_ctx, n_pages):
+    """Host plan with the middle in pages of 64 rows from a pool of n_pages."""
+    counts = [int(c) for c in kept_count]
+    if len(counts) != n_kv_heads:
+        raise ValueError("kept_count must hold one count per KV head")
+    arr = (ctypes.c_int32 * max(1, len(counts)))(*counts)
+    desc = LayerCacheDesc()
+    check(lib().leank_plan_layer_paged(arr, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window,
+                                       int(max_ctx), int(n_pages), ctypes.byref(desc)),
+          "leank_plan_layer_paged")
+    return desc
+
+
 def leank_plan_layer_q(kept_count, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window,
                        max_ctx, quant_bits):
     """Host plan with low-bit middle streams (quant_bits 4 or 8; 0 = bf16)."""
@@ -127,10 +143,21 @@ class LayerCache:
     """
 
     def __init__(self, kept_count, kept_idx, batch, n_q_heads, n_kv_heads, n_sink, window,
-                 max_ctx, head_dim=HEAD_DIM, device=None, quant_bits=0):
+                 max_ctx, head_dim=HEAD_DIM, device=None, quant_bits=0, n_pages=0,
+                 block_table=None):
+        """quant_bits 4 or 8: low-bit middle streams.  n_pages > 0: the
+        middle in pages of 64 rows from a pool of n_pages pages, mapped by
+        block_table (int32 [batch, pages_per_row] on the device; default:
+        batch row b's pages contiguous from page b * pages_per_row)."""
         device = _normalize_device(device if device is not None else kept_idx.device)
-        self.desc = leank_plan_layer_q(kept_count, batch, n_q_heads, n_kv_heads, head_dim,
-                                       n_sink, window, max_ctx, quant_bits)
+        if n_pages and quant_bits:
+            raise ValueError("low-bit middle streams are not paged")
+        if n_pages:
+            self.desc = leank_plan_layer_paged(kept_count, batch, n_q_heads, n_kv_heads, head_dim,
+                                               n_sink, window, max_ctx, n_pages)
+        else:
+            self.desc = leank_plan_layer_q(kept_count, batch, n_q_heads, n_kv_heads, head_dim,
+                                           n_sink, window, max_ctx, quant_bits)
         _require(kept_idx, torch.int16, "kept_idx", ndim=2, device=device)
         if tuple(kept_idx.shape) != (n_kv_heads, head_dim):
             raise ValueError("kept_idx must be [n_kv_heads, head_dim]")
@@ -156,6 +183,21 @@ class LayerCache:
                 t = torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
                 self.quant[name] = t
                 setattr(self.desc, name, t.data_ptr())
+        self.pool = None
+        self.block_table = None
+        if n_pages:
+            self.pool = torch.empty(max(8, self.desc.pool_bytes // 2), dtype=torch.bfloat16,
+                                    device=device)
+            ppr = self.desc.pages_per_row
+            if block_table is None:
+                block_table = torch.arange(batch * ppr, dtype=torch.int32,
+                                           device=device).reshape(batch, ppr)
+            _require(block_table, torch.int32, "block_table", ndim=2, device=device)
+            if tuple(block_table.shape) != (batch, ppr):
+                raise ValueError(f"block_table must be [batch, {ppr}]")
+            self.block_table = block_table
+            self.desc.pool = self.pool.data_ptr()
+            self.desc.block_table = block_table.data_ptr() if block_table.numel() else 0
         self.length = 0
         self._workspace = None
 
@@ -194,7 +236,7 @@ class LayerCache:
     def nbytes(self):
         d = self.desc
         return (d.k_sl_bytes + d.v_sl_bytes + d.k_prun_bytes + d.v_mid_bytes + d.k_q_bytes
-                + d.k_qp_bytes + d.k_stage_bytes + d.v_q_bytes + d.v_qp_bytes)
+                + d.k_qp_bytes + d.k_stage_bytes + d.v_q_bytes + d.v_qp_bytes + d.pool_bytes)
 
 
 def _desc(cache):

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libleank.so")
 
 HEAD_DIM = 128
 QUANT_GROUP = 64
+PAGE_ROWS = 64
 MAX_KV_HEADS = 64
 MAX_GROUP = 8
 CHANNEL_QUANTUM = 8
@@ -73,6 +74,13 @@ class LayerCacheDesc(ctypes.Structure):
         ("k_stage", ctypes.c_void_p),
         ("v_q", ctypes.c_void_p),
         ("v_qp", ctypes.c_void_p),
+        ("page_rows", ctypes.c_int32),
+        ("pages_per_row", ctypes.c_int32),
+        ("n_pages", ctypes.c_int64),
+        ("page_bytes", ctypes.c_uint64),
+        ("pool_bytes", ctypes.c_uint64),
+        ("pool", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
     ]
 
 
@@ -94,6 +102,10 @@ _SIGNATURES = {
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                           ctypes.c_int32, ctypes.POINTER(LayerCacheDesc)]),
+    "leank_plan_layer_paged": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                              ctypes.c_int64, ctypes.POINTER(LayerCacheDesc)]),
     "leank_pack_k": (ctypes.c_int, [ctypes.POINTER(LayerCacheDesc), ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_void_p]),

@@ -165,6 +165,11 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   p.combine_slices = max_items > 256 ? 8 : max_items > 64 ? 4 : max_items > 16 ? 2 : 1;
   p.qk_scale = scale * kLog2e;
   p.n_batch = c->batch;
+  p.paged = c->page_rows != 0;
+  p.pool = static_cast<const uint16_t*>(c->pool);
+  p.block_table = c->block_table;
+  p.page_elems = static_cast<int64_t>(c->page_bytes / 2);
+  p.pages_per_row = c->pages_per_row;
   if (quant) {
     p.k_q = static_cast<const uint8_t*>(c->k_q);
     p.k_qp = static_cast<const float*>(c->k_qp);

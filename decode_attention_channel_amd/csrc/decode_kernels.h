@@ -131,7 +131,14 @@ struct DecodeParams {
   const float* v_qp;
   int64_t q_groups;  // K groups per (batch row, head): ceil(mid_cap / 64)
   int32_t n_batch;
-  int32_t pad_q;
+  int32_t paged;     // middle rows in pages of LEANK_PAGE_ROWS through block_table
+  // paged middle: page p of the pool starts at pool + p * page_elems; head
+  // h's K rows at k_off, its V blocks at v_off within the page
+  const uint16_t* pool;
+  const int32_t* block_table;  // [batch][pages_per_row]
+  int64_t page_elems;
+  int32_t pages_per_row;
+  int32_t pad_p;
   DecodeHead heads[LEANK_MAX_KV_HEADS];
 };
 
@@ -336,6 +343,30 @@ __device__ __forceinline__ void attend_range(const uint16_t* kb, int kstride, co
     }
   }
 #endif
+}
+
+// Middle rows [r0, r1) of a paged stream: r0 is a multiple of the page
+// size and s_pages holds the physical pages of rows r0, r0 + 64, ...
+// (tiles never straddle a page: both are 32-row aligned).
+template <int G, int KB>
+__device__ __forceinline__ void attend_range_paged(const uint16_t* pool, int64_t page_elems,
+                                                   const int32_t* s_pages, int64_t k_off,
+                                                   int64_t v_off, int r0, int r1, int c,
+                                                   const u32x4_t (&qa)[KB], float qk_scale,
+                                                   uint16_t* p_lds, WaveState& st) {
+  const int wave = threadIdx.x >> 6;
+  for (int t0 = r0 + wave * kTileRows; t0 < r1; t0 += kWaves * kTileRows) {
+    const int nvalid = r1 - t0;
+    const uint16_t* page = pool + static_cast<int64_t>(s_pages[(t0 - r0) / LEANK_PAGE_ROWS]) * page_elems;
+    const int t_in = t0 % LEANK_PAGE_ROWS;
+    TileRegs<KB> cur;
+    load_tile<KB>(page + k_off, c, page + v_off, t_in, nvalid, c, cur);
+    if (nvalid >= kTileRows) {
+      compute_tile<G, KB, false>(cur, kTileRows, -1, qa, qk_scale, p_lds, st);
+    } else {
+      compute_tile<G, KB, true>(cur, nvalid, -1, qa, qk_scale, p_lds, st);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- low-bit middle
@@ -695,6 +726,24 @@ __device__ __forceinline__ StepTokens step_tokens(const DecodeParams& p, int b, 
   return st;
 }
 
+// Element offsets of middle row r of head hd in batch row b: its K row and
+// the V block that holds it (bf16 middle, paged or not).
+__device__ __forceinline__ void middle_row_at(const DecodeParams& p, const DecodeHead& hd, int b,
+                                              int64_t r, const uint16_t** k_row,
+                                              const uint16_t** v_block) {
+  if (p.paged) {
+    const int64_t page = p.block_table[static_cast<int64_t>(b) * p.pages_per_row + r / LEANK_PAGE_ROWS];
+    const uint16_t* base = p.pool + page * p.page_elems;
+    const int64_t in = r % LEANK_PAGE_ROWS;
+    *k_row = base + hd.k_off + in * hd.kept;
+    *v_block = base + hd.v_off + (in / LEANK_V_BLOCK) * (LEANK_HEAD_DIM * LEANK_V_BLOCK);
+  } else {
+    *k_row = p.k_prun + hd.k_off + (static_cast<int64_t>(b) * p.mid_cap + r) * hd.kept;
+    *v_block = p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM +
+               (r / LEANK_V_BLOCK) * (LEANK_HEAD_DIM * LEANK_V_BLOCK);
+  }
+}
+
 // Word `lane` of a token's compacted K row (kept channels 2 lane, 2 lane + 1
 // of the head) from its full row in LDS.
 __device__ __forceinline__ uint32_t compact_from_lds(const uint16_t* row, const int16_t* s_idx,
@@ -725,6 +774,8 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ float s_tok_s[2][G];
   // low-bit middle: each wavefront's copy of a K group's (scale, min) pairs
   __shared__ __attribute__((aligned(16))) float s_par[kWaves][QB ? 2 * LEANK_HEAD_DIM : 4];
+  // paged middle: the physical pages of the item's rows
+  __shared__ int32_t s_pages[QB ? 1 : 64];
 
   const int item = blockIdx.x;
   const int b = item / p.items_per_b;
@@ -743,6 +794,14 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   const uint16_t* qh = p.q + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM;
   if (t < G * 16)
     *reinterpret_cast<u32x4_t*>(s_q + t * 8) = *reinterpret_cast<const u32x4_t*>(qh + t * 8);
+  if (QB == 0 && p.paged && middle && t >= 192) {
+    // the item's pages (items span at most 64 pages: their rows are capped
+    // by the plan's largest item size)
+    const int first = (local - p.n_sl_items) * hd.mid_rows / LEANK_PAGE_ROWS;
+    const int i = t - 192;
+    if (i < hd.mid_rows / LEANK_PAGE_ROWS && first + i < p.pages_per_row)
+      s_pages[i] = p.block_table[static_cast<int64_t>(b) * p.pages_per_row + first + i];
+  }
   if ((middle || carries_step) && t >= 128 && t < 144)
     *reinterpret_cast<u32x4_t*>(s_idx + (t - 128) * 8) =
         *reinterpret_cast<const u32x4_t*>(p.kept_idx + h * LEANK_HEAD_DIM + (t - 128) * 8);
@@ -766,8 +825,8 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
       const int c = t - 128;
       u32x4_t x = zero4;
       if (tok.mid_row >= 0) {
-        const uint16_t* blk = p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM +
-                              static_cast<int64_t>(tok.mid_row / LEANK_V_BLOCK) * (LEANK_HEAD_DIM * LEANK_V_BLOCK);
+        const uint16_t *k_row, *blk;
+        middle_row_at(p, hd, b, tok.mid_row, &k_row, &blk);
         x = *reinterpret_cast<const u32x4_t*>(blk + c * 8);
       }
       *reinterpret_cast<u32x4_t*>(s_vblk[1] + c * 8) = x;
@@ -854,6 +913,37 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
             gather_q<G, 4>(s_q, s_idx, false, c, qa);
             attend_range_q<G, 4, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
           }
+        }
+      }
+    } else if (p.paged) {
+      switch ((c + 31) / 32) {
+        case 1: {
+          u32x4_t qa[1];
+          gather_q<G, 1>(s_q, s_idx, false, c, qa);
+          attend_range_paged<G, 1>(p.pool, p.page_elems, s_pages, hd.k_off, hd.v_off, r0, r1, c, qa,
+                                   p.qk_scale, p_lds, st);
+          break;
+        }
+        case 2: {
+          u32x4_t qa[2];
+          gather_q<G, 2>(s_q, s_idx, false, c, qa);
+          attend_range_paged<G, 2>(p.pool, p.page_elems, s_pages, hd.k_off, hd.v_off, r0, r1, c, qa,
+                                   p.qk_scale, p_lds, st);
+          break;
+        }
+        case 3: {
+          u32x4_t qa[3];
+          gather_q<G, 3>(s_q, s_idx, false, c, qa);
+          attend_range_paged<G, 3>(p.pool, p.page_elems, s_pages, hd.k_off, hd.v_off, r0, r1, c, qa,
+                                   p.qk_scale, p_lds, st);
+          break;
+        }
+        default: {
+          u32x4_t qa[4];
+          gather_q<G, 4>(s_q, s_idx, false, c, qa);
+          attend_range_paged<G, 4>(p.pool, p.page_elems, s_pages, hd.k_off, hd.v_off, r0, r1, c, qa,
+                                   p.qk_scale, p_lds, st);
+          break;
         }
       }
     } else {
@@ -980,10 +1070,10 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     if (tok.mid_row >= 0) {
       // middle row: kept K channels (compacted) and V
       const int which = tok.leave_in ? 1 : 0;
-      uint32_t* k_prun = reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(p.k_prun));
-      const int64_t row = static_cast<int64_t>(b) * p.mid_cap + tok.mid_row;
+      const uint16_t *k_row_c, *blk_c;
+      middle_row_at(p, hd, b, tok.mid_row, &k_row_c, &blk_c);
       if (2 * lane < hd.kept)
-        k_prun[(hd.k_off + row * hd.kept) / 2 + lane] =
+        reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(k_row_c))[lane] =
             compact_from_lds(s_tok_k[which], s_idx, hd.kept, lane);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -991,9 +1081,7 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
         s_vblk[1][ch * LEANK_V_BLOCK + e_mid] =
             tok.leave_in ? s_vblk[0][ch * LEANK_V_BLOCK + e_ring] : s_tok_v[ch];
       }
-      uint16_t* blk = const_cast<uint16_t*>(p.v_mid) + hd.v_off +
-                      static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM +
-                      static_cast<int64_t>(tok.mid_row / LEANK_V_BLOCK) * (LEANK_HEAD_DIM * LEANK_V_BLOCK);
+      uint16_t* blk = const_cast<uint16_t*>(blk_c);
       reinterpret_cast<u32x4_t*>(blk)[2 * lane] = reinterpret_cast<const u32x4_t*>(s_vblk[1])[2 * lane];
       reinterpret_cast<u32x4_t*>(blk)[2 * lane + 1] =
           reinterpret_cast<const u32x4_t*>(s_vblk[1])[2 * lane + 1];

@@ -35,7 +35,11 @@ struct PackParams {
   uint16_t* v_mid;
   const int16_t* kept_idx;
   int32_t ring_only;   // low-bit cache: middle rows are written by the quantizing kernels
-  int32_t pad0;
+  int32_t paged;       // middle rows in pages through block_table (heads' k_off / v_off are in-page)
+  uint16_t* pool;
+  const int32_t* block_table;
+  int64_t page_elems;
+  int64_t pages_per_row;
   int64_t t_old;       // tokens in the cache before the append
   int64_t t_new;       // tokens after it
   int64_t n_new;
@@ -70,6 +74,14 @@ __device__ __forceinline__ void write_middle(const PackParams& p, int b, int h, 
   const int c0 = j0 < hd.kept ? (p.kept_idx[h * LEANK_HEAD_DIM + j0] & (LEANK_HEAD_DIM - 1)) : 0;
   const int c1 = j0 < hd.kept ? (p.kept_idx[h * LEANK_HEAD_DIM + j0 + 1] & (LEANK_HEAD_DIM - 1)) : 0;
   const uint32_t kc = compact_k_word(kw, c0, c1);
+  if (p.paged) {
+    const int64_t page = p.block_table[static_cast<int64_t>(b) * p.pages_per_row + r / LEANK_PAGE_ROWS];
+    uint16_t* base = p.pool + page * p.page_elems;
+    const int64_t in = r % LEANK_PAGE_ROWS;
+    if (j0 < hd.kept) reinterpret_cast<uint32_t*>(base + hd.k_off + in * hd.kept)[lane] = kc;
+    store_v_row_word(base + hd.v_off, in, lane, vw);
+    return;
+  }
   const int64_t row = static_cast<int64_t>(b) * p.mid_cap + r;
   if (j0 < hd.kept) p.k_prun[(hd.k_off + row * hd.kept) / 2 + lane] = kc;
   store_v_row_word(p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM, r,
@@ -171,6 +183,11 @@ int fill_params(const leank_layer_cache* c, const void* k_new, const void* v_new
   p->n_sink = c->n_sink;
   p->window = c->window;
   p->slots = c->n_sink + c->window;
+  p->paged = c->page_rows != 0;
+  p->pool = static_cast<uint16_t*>(c->pool);
+  p->block_table = c->block_table;
+  p->page_elems = static_cast<int64_t>(c->page_bytes / 2);
+  p->pages_per_row = c->pages_per_row;
   for (int h = 0; h < c->n_kv_heads; ++h) {
     p->heads[h].k_off = c->k_prun_off[h];
     p->heads[h].v_off = c->v_mid_off[h];

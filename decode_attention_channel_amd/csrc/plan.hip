@@ -78,6 +78,30 @@ int validate_cache(const leank_layer_cache* c, bool need_buffers) {
   const bool quant = c->quant_bits != 0;
   if (quant && c->quant_bits != 4 && c->quant_bits != 8) return LEANK_EINVAL;
   if (quant && c->quant_group != LEANK_QUANT_GROUP) return LEANK_EINVAL;
+  const bool paged = c->page_rows != 0;
+  if (paged) {
+    // canonical page layout: K of the live heads in group order, then their V blocks
+    if (quant || c->page_rows != LEANK_PAGE_ROWS || c->n_pages < 1) return LEANK_EINVAL;
+    if (c->pages_per_row != (c->mid_capacity + LEANK_PAGE_ROWS - 1) / LEANK_PAGE_ROWS) return LEANK_EINVAL;
+    int64_t kept_sum = 0, n_live = 0;
+    for (int h = 0; h < c->n_kv_heads; ++h)
+      if (c->kept_count[h] > 0) kept_sum += c->kept_count[h], ++n_live;
+    int64_t k_pre = 0, rank = 0;
+    for (int i = 0; i < c->n_kv_heads; ++i) {
+      const int h = c->group_order[i];
+      if (h < 0 || h >= c->n_kv_heads) return LEANK_EINVAL;
+      if (c->kept_count[h] <= 0) continue;
+      if (c->k_prun_off[h] != LEANK_PAGE_ROWS * k_pre ||
+          c->v_mid_off[h] != LEANK_PAGE_ROWS * (kept_sum + rank * LEANK_HEAD_DIM))
+        return LEANK_EINVAL;
+      k_pre += c->kept_count[h];
+      ++rank;
+    }
+    const int64_t page_bytes = LEANK_PAGE_ROWS * (2 * kept_sum + 2 * LEANK_HEAD_DIM * n_live);
+    if (static_cast<int64_t>(c->page_bytes) != page_bytes ||
+        c->pool_bytes != c->page_bytes * static_cast<uint64_t>(c->n_pages))
+      return LEANK_EINVAL;
+  }
   int live = 0;
   for (int h = 0; h < c->n_kv_heads; ++h) {
     int k = c->kept_count[h];
@@ -87,7 +111,9 @@ int validate_cache(const leank_layer_cache* c, bool need_buffers) {
       ++live;
       if (!quant) {
         if (c->k_prun_off[h] < 0 || c->v_mid_off[h] < 0) return LEANK_EINVAL;
-        if (c->k_prun_off[h] % LEANK_CHANNEL_QUANTUM || c->v_mid_off[h] % (LEANK_HEAD_DIM * LEANK_V_BLOCK))
+        // (paged caches: offsets within a page, checked against the canonical layout above)
+        if (!paged && (c->k_prun_off[h] % LEANK_CHANNEL_QUANTUM ||
+                       c->v_mid_off[h] % (LEANK_HEAD_DIM * LEANK_V_BLOCK)))
           return LEANK_EINVAL;
       } else {
         if (c->k_q_off[h] < 0 || c->k_qp_off[h] < 0 || c->k_stage_off[h] < 0 ||
@@ -104,7 +130,10 @@ int validate_cache(const leank_layer_cache* c, bool need_buffers) {
   if (need_buffers) {
     if (!c->k_sl || !c->v_sl || !c->kept_idx) return LEANK_EINVAL;
     if (!aligned16(c->k_sl) || !aligned16(c->v_sl)) return LEANK_EINVAL;
-    if (!quant) {
+    if (paged) {
+      if (c->pool_bytes && (!c->pool || !aligned16(c->pool))) return LEANK_EINVAL;
+      if (c->pages_per_row > 0 && !c->block_table) return LEANK_EINVAL;
+    } else if (!quant) {
       if (c->k_prun_bytes && (!c->k_prun || !aligned16(c->k_prun))) return LEANK_EINVAL;
       if (c->v_mid_bytes && (!c->v_mid || !aligned16(c->v_mid))) return LEANK_EINVAL;
     } else {
@@ -151,7 +180,10 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPl
       const int64_t row_bytes = middle_row_bytes(c, kept);
       split_rows(w->t_mid, row_target(row_bytes, kItemBytesMin), &n32, &rows32, &b);
       bound_per_b += b;
-      split_rows(w->t_mid, row_target(row_bytes, target), &w->n_mid[h], &w->mid_rows[h], &unused_n);
+      int64_t rows = row_target(row_bytes, target);
+      // a paged item reads its page list from LDS: at most 64 pages
+      if (c->page_rows) rows = std::min<int64_t>(rows, 64 * LEANK_PAGE_ROWS);
+      split_rows(w->t_mid, rows, &w->n_mid[h], &w->mid_rows[h], &unused_n);
     }
     base += w->n_sl_items + w->n_mid[h];
   }
@@ -280,6 +312,39 @@ extern "C" int leank_plan_layer_q(const int32_t* kept_count_host, int32_t batch,
   c.k_stage_bytes = static_cast<uint64_t>(ks) * 2;
   c.v_q_bytes = static_cast<uint64_t>(vq);
   c.v_qp_bytes = static_cast<uint64_t>(vqp) * 4;
+  st = validate_cache(&c, false);
+  if (st != LEANK_OK) return st;
+  *out = c;
+  return LEANK_OK;
+}
+
+extern "C" int leank_plan_layer_paged(const int32_t* kept_count_host, int32_t batch,
+                                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                      int32_t n_sink, int32_t window, int64_t max_ctx,
+                                      int64_t n_pages, leank_layer_cache* out) {
+  if (!out || n_pages < 1) return LEANK_EINVAL;
+  leank_layer_cache c;
+  int st = leank_plan_layer(kept_count_host, batch, n_q_heads, n_kv_heads, head_dim, n_sink,
+                            window, max_ctx, &c);
+  if (st != LEANK_OK) return st;
+  int64_t kept_sum = 0;
+  for (int h = 0; h < n_kv_heads; ++h) kept_sum += std::max(0, c.kept_count[h]);
+  int64_t k_pre = 0, rank = 0;
+  for (int h = 0; h < n_kv_heads; ++h) c.k_prun_off[h] = c.v_mid_off[h] = -1;
+  for (int i = 0; i < n_kv_heads; ++i) {
+    const int h = c.group_order[i];
+    if (c.kept_count[h] <= 0) continue;
+    c.k_prun_off[h] = LEANK_PAGE_ROWS * k_pre;
+    c.v_mid_off[h] = LEANK_PAGE_ROWS * (kept_sum + rank * LEANK_HEAD_DIM);
+    k_pre += c.kept_count[h];
+    ++rank;
+  }
+  c.k_prun_bytes = c.v_mid_bytes = 0;
+  c.page_rows = LEANK_PAGE_ROWS;
+  c.pages_per_row = static_cast<int32_t>((c.mid_capacity + LEANK_PAGE_ROWS - 1) / LEANK_PAGE_ROWS);
+  c.n_pages = n_pages;
+  c.page_bytes = static_cast<uint64_t>(LEANK_PAGE_ROWS) * (2 * kept_sum + 2 * LEANK_HEAD_DIM * rank);
+  c.pool_bytes = c.page_bytes * static_cast<uint64_t>(n_pages);
   st = validate_cache(&c, false);
   if (st != LEANK_OK) return st;
   *out = c;

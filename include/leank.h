@@ -39,13 +39,14 @@
 extern "C" {
 #endif
 
-#define LEANK_ABI_VERSION 4
+#define LEANK_ABI_VERSION 5
 #define LEANK_HEAD_DIM 128      /* the only head_dim the kernels implement   */
 #define LEANK_MAX_KV_HEADS 64   /* per-layer KV heads a cache plan can hold  */
 #define LEANK_MAX_GROUP 8       /* query heads per KV head the kernels take  */
 #define LEANK_CHANNEL_QUANTUM 8 /* kept counts must be multiples of this     */
 #define LEANK_V_BLOCK 8         /* V rows per transposed storage block        */
 #define LEANK_QUANT_GROUP 64    /* middle rows per K quantization group       */
+#define LEANK_PAGE_ROWS 64      /* middle rows per page of a paged cache      */
 
 typedef enum {
   LEANK_OK = 0,
@@ -152,6 +153,21 @@ int leank_build_mask(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
  * min) / (2^bits - 1) of the group, code = round-half-even((x - min) /
  * scale) clamped to [0, 2^bits - 1] (0 when scale is 0), decided in IEEE
  * float32.  K and V must be finite.  Sink and window rows stay bf16.
+ *
+ * Paged middle (leank_plan_layer_paged; white paper section 3, block-level
+ * granularity: the cache of a serving system such as vLLM's PagedAttention
+ * is organised in fixed-size blocks; its worked example block holds 64
+ * tokens).  The middle rows of batch row b are held in pages of
+ * LEANK_PAGE_ROWS rows taken from a caller-owned pool: middle row r lives
+ * in physical page block_table[b * pages_per_row + r / 64], row r % 64 of
+ * it.  One page holds those 64 rows for every live head: first, head by
+ * head in group order, K as [64][kept_count[h]] at element offset
+ * k_prun_off[h]; then, head by head, V as 8 V blocks [8][128][8] at element
+ * offset v_mid_off[h] (element offsets within the page; bf16).  k_prun and
+ * v_mid are unused (k_prun_bytes = v_mid_bytes = 0).  The caller maps a
+ * page before rows are appended to it (for one token per step: whenever
+ * r % 64 == 0); the kernels read the table on the device and do not check
+ * it, so every entry that covers written rows must lie in [0, n_pages).
  */
 typedef struct leank_layer_cache {
   int32_t batch;
@@ -197,6 +213,15 @@ typedef struct leank_layer_cache {
   void* k_stage;
   void* v_q;
   void* v_qp;
+  /* paged middle (filled by leank_plan_layer_paged; zero otherwise) */
+  int32_t page_rows;            /* LEANK_PAGE_ROWS, or 0 */
+  int32_t pages_per_row;        /* block table entries per batch row: ceil(mid_capacity / 64) */
+  int64_t n_pages;              /* pages in the pool */
+  uint64_t page_bytes;          /* 64 * sum over live heads of (2 * kept_count + 256) */
+  uint64_t pool_bytes;          /* n_pages * page_bytes */
+  /* set by the caller when page_rows != 0: */
+  void* pool;                   /* device, 16-byte aligned */
+  const int32_t* block_table;   /* device int32 [batch][pages_per_row] */
 } leank_layer_cache;
 
 /*
@@ -227,6 +252,19 @@ int leank_plan_layer_q(const int32_t* kept_count_host, int32_t batch,
                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                        int32_t n_sink, int32_t window, int64_t max_ctx,
                        int32_t quant_bits, leank_layer_cache* cache_out);
+
+/*
+ * leank_plan_layer_paged -- leank_plan_layer for a bf16 cache whose middle
+ * is held in pages of 64 rows from a pool of n_pages pages (n_pages >= 1)
+ * through a block table (layout above).  max_ctx bounds every batch row.
+ * The caller allocates k_sl, v_sl, the pool (pool_bytes) and the block
+ * table (int32 [batch][pages_per_row]).  Every entry point takes such a
+ * cache; the low-bit streams are not paged.
+ */
+int leank_plan_layer_paged(const int32_t* kept_count_host, int32_t batch,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                           int32_t n_sink, int32_t window, int64_t max_ctx,
+                           int64_t n_pages, leank_layer_cache* cache_out);
 
 /*
  * leank_pack_k -- append n_new tokens at positions [pos0, pos0 + n_new)

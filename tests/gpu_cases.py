@@ -85,6 +85,8 @@ def read_pair(cache, b, h, n_mid=None, ring_only=False):
     c = d.kept_count[h]
     if c == 0 or ring_only:
         return ring_k, ring_v, None, None
+    if d.page_rows:
+        return ring_k, ring_v, *_read_paged_middle(cache, b, h, n_mid)
     ko = d.k_prun_off[h] + b * mid_cap * c
     k_prun = bf16_bits(cache.k_prun[ko: ko + n_mid * c]).reshape(n_mid, c)
     vm = _v_rows(mid_cap)
@@ -195,3 +197,30 @@ def assert_quant_cache_matches(cache, k_bits, v_bits, mask, pairs=None):
             assert np.array_equal(got[key], want[key]), (b, h, key)
         for key in ("k_scale", "k_lo", "v_scale", "v_lo"):
             assert np.array_equal(got[key].view(np.uint32), want[key].view(np.uint32)), (b, h, key)
+
+
+def _read_paged_middle(cache, b, h, n_mid):
+    """K_prun [n_mid, kept] and V_mid [n_mid, 128] of a paged cache, gathered
+    page by page through the block table."""
+    d = cache.desc
+    c = d.kept_count[h]
+    pe = d.page_bytes // 2
+    pool = bf16_bits(cache.pool)
+    table = cache.block_table.cpu().numpy()
+    k_rows, v_rows = [], []
+    for p0 in range(0, n_mid, 64):
+        page = int(table[b, p0 // 64])
+        base = page * pe
+        n = min(64, n_mid - p0)
+        k_rows.append(pool[base + d.k_prun_off[h]: base + d.k_prun_off[h] + 64 * c].reshape(64, c)[:n])
+        v_rows.append(_unblock_v(pool[base + d.v_mid_off[h]: base + d.v_mid_off[h] + 64 * 128], 64)[:n])
+    if not k_rows:
+        return np.zeros((0, c), np.uint16), np.zeros((0, 128), np.uint16)
+    return np.concatenate(k_rows), np.concatenate(v_rows)
+
+
+def shuffled_block_table(rng, batch, pages_per_row, n_pages, device="cuda"):
+    """A block table giving every (batch row, page) a distinct pool page in
+    random order."""
+    pick = rng.permutation(n_pages)[:batch * pages_per_row]
+    return torch.from_numpy(pick.astype(np.int32).reshape(batch, pages_per_row)).to(device)

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert "leank_build_mask" in names and "leank_pack_k" in names and "leank_decode_attn" in names
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.leank_abi_version() == 4
+    assert lib.leank_abi_version() == 5
     assert lib.leank_layer_cache_size() == ctypes.sizeof(_lib.LayerCacheDesc)
 
 
@@ -251,3 +251,37 @@ def test_decode_bytes_q_match_oracle(bits):
     for ctx in (1, 4, 20, 21, 83, 84, 85, 148, 700):
         assert dac.leank_decode_bytes(d, ctx) == oracle.decode_traffic_bytes_q(
             2, 8, 4, 128, ctx, n_sink, window, kept, bits), ctx
+
+
+def test_plan_layer_paged_layout():
+    kept = [32, 0, 64, 8]
+    batch, max_ctx, n_sink, window, n_pages = 3, 1000, 4, 61, 50
+    d = dac.leank_plan_layer_paged(kept, batch, 8, 4, 128, n_sink, window, max_ctx, n_pages)
+    mid_cap = max_ctx - n_sink - window
+    assert d.page_rows == 64 and d.pages_per_row == -(-mid_cap // 64) and d.n_pages == n_pages
+    assert d.k_prun_bytes == 0 and d.v_mid_bytes == 0
+    live = [h for h in (d.group_order[n] for n in range(4)) if kept[h] > 0]
+    k_pre = 0
+    for rank, h in enumerate(live):       # K of the live heads, then their V blocks
+        assert d.k_prun_off[h] == 64 * k_pre
+        assert d.v_mid_off[h] == 64 * (sum(kept) + rank * 128)
+        k_pre += kept[h]
+    assert d.k_prun_off[1] == -1 and d.v_mid_off[1] == -1
+    assert d.page_bytes == 64 * (2 * sum(kept) + 256 * len(live))
+    assert d.pool_bytes == n_pages * d.page_bytes
+
+
+def test_paged_plan_and_calls_rejected():
+    with pytest.raises(dac.LeankError):
+        dac.leank_plan_layer_paged([32], 1, 1, 1, 128, 4, 8, 100, 0)   # no pages
+    L = _lib.lib()
+    desc = dac.leank_plan_layer_paged([32, 0], 2, 4, 2, 128, 4, 8, 100, 4)
+    desc.kept_idx = desc.k_sl = desc.v_sl = 0x1000
+    ws = dac.leank_workspace_bytes(desc, 100)
+    # pool and block table missing
+    assert L.leank_decode_attn(ctypes.byref(desc), 0x1000, 100, 0.1, 0x1000, 0x1000, ws, None) == _lib.EINVAL
+    desc.pool = 0x1000
+    assert L.leank_decode_attn(ctypes.byref(desc), 0x1000, 100, 0.1, 0x1000, 0x1000, ws, None) == _lib.EINVAL
+    desc.block_table = 0x1000
+    desc.k_prun_off[0] = 8                 # not the canonical page layout
+    assert L.leank_decode_attn(ctypes.byref(desc), 0x1000, 100, 0.1, 0x1000, 0x1000, ws, None) == _lib.EINVAL
