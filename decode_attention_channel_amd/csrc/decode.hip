@@ -162,7 +162,13 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   int32_t max_items = 0;
   for (int h = 0; h < c->n_kv_heads; ++h)
     max_items = std::max(max_items, w.n_sl_items + w.n_mid[h]);
+#ifndef LEANK_COMBINE_WAVE
+#define LEANK_COMBINE_WAVE 1
+#endif
   p.combine_slices = max_items > 256 ? 8 : max_items > 64 ? 4 : max_items > 16 ? 2 : 1;
+  // few items per pair: one wavefront per (pair, head) merges them without
+  // barriers (measured faster up to 16 items; the workgroup form wins beyond)
+  if (LEANK_COMBINE_WAVE && max_items <= 16) p.combine_slices = 0;
   p.qk_scale = scale * kLog2e;
   p.n_batch = c->batch;
   p.paged = c->page_rows != 0;

@@ -16,13 +16,13 @@ namespace {
 // Items are sized so that one decode call makes about kTargetCUs *
 // LEANK_ITEMS_PER_CU of them, within [LEANK_ITEM_KB_MIN, LEANK_ITEM_KB_MAX].
 #ifndef LEANK_ITEMS_PER_CU
-#define LEANK_ITEMS_PER_CU 8
+#define LEANK_ITEMS_PER_CU 5
 #endif
 #ifndef LEANK_ITEM_KB_MIN
 #define LEANK_ITEM_KB_MIN 64
 #endif
 #ifndef LEANK_ITEM_KB_MAX
-#define LEANK_ITEM_KB_MAX 1024
+#define LEANK_ITEM_KB_MAX 448
 #endif
 
 constexpr int64_t kTargetCUs = 256;  // compute units of an MI355X
