@@ -493,7 +493,9 @@ __device__ __forceinline__ float code_f32(const uint32_t (&w)[QB == 8 ? 2 : 1], 
 }
 
 // B operand (8 rows of one channel) from 8 V codes as exact bf16 integers
-// (8-bit: the code; 4-bit: 128 + code).
+// (8-bit: the code; 4-bit: 128 + code -- byte k of the word holds rows k
+// and k + 4, so each pair of rows is one byte permute against the exponent
+// byte of 128).
 template <int QB>
 __device__ __forceinline__ u32x4_t v_codes_bf16(const uint32_t (&w)[QB == 8 ? 2 : 1]) {
   u32x4_t r;
@@ -501,14 +503,14 @@ __device__ __forceinline__ u32x4_t v_codes_bf16(const uint32_t (&w)[QB == 8 ? 2 
 #pragma unroll
     for (int k = 0; k < 4; ++k) r[k] = pack_bf16x2(code_f32<QB>(w, 2 * k), code_f32<QB>(w, 2 * k + 1));
   } else {
-    const uint32_t even = w[0] & 0x0f0f0f0fu;         // rows 0, 2, 4, 6 in bytes 0..3
-    const uint32_t odd = (w[0] >> 4) & 0x0f0f0f0fu;   // rows 1, 3, 5, 7
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // bytes [even byte k, 0, odd byte k, 0], then the exponent of 128
-      const uint32_t sel = static_cast<uint32_t>(k) | (0x0cu << 8) | ((4u + k) << 16) | (0x0cu << 24);
-      r[k] = __builtin_amdgcn_perm(odd, even, sel) | 0x43004300u;
-    }
+    const uint32_t lo = w[0] & 0x0f0f0f0fu;          // rows 0..3 in bytes 0..3
+    const uint32_t hi = (w[0] >> 4) & 0x0f0f0f0fu;   // rows 4..7
+    const uint32_t exp128 = 0x43434343u;             // high byte of bf16 128
+    // bytes [row a, 0x43, row a + 1, 0x43]: selectors 0-3 pick the codes, 4 the exponent
+    r[0] = __builtin_amdgcn_perm(exp128, lo, 0x04010400u);
+    r[1] = __builtin_amdgcn_perm(exp128, lo, 0x04030402u);
+    r[2] = __builtin_amdgcn_perm(exp128, hi, 0x04010400u);
+    r[3] = __builtin_amdgcn_perm(exp128, hi, 0x04030402u);
   }
   return r;
 }

@@ -87,11 +87,13 @@ __device__ __forceinline__ void quantize_v_row(float x0, float x1, int bits, flo
   }
 }
 
-// Byte offset of (row e of a block, channel ch) within one V code block, and
-// the nibble shift for 4-bit codes.
+// Byte offset of (row e of a block, channel ch) within one V code block
+// (4-bit: byte k of a channel's 4 bytes holds rows k and k + 4), and the
+// nibble of that byte holding row e.
 __device__ __forceinline__ int v_code_byte(int ch, int e, int bits) {
-  return bits == 8 ? ch * 8 + e : ch * 4 + e / 2;
+  return bits == 8 ? ch * 8 + e : ch * 4 + (e & 3);
 }
+__device__ __forceinline__ int v_code_shift(int e) { return 4 * (e >> 2); }
 
 // ---------------------------------------------------------------- bulk prefill
 
@@ -166,12 +168,12 @@ __global__ __launch_bounds__(kQThreads) void quant_v_bulk_kernel(const QuantPara
       s_blk[v_code_byte(2 * lane, e, 8)] = static_cast<uint8_t>(c0);
       s_blk[v_code_byte(2 * lane + 1, e, 8)] = static_cast<uint8_t>(c1);
     } else {
-      // rows 2k and 2k + 1 share a byte and are quantized by different
+      // rows k and k + 4 share a byte and are quantized by different
       // wavefronts: combine the nibbles with LDS atomic ors
       atomicOr(reinterpret_cast<uint32_t*>(s_blk) + v_code_byte(2 * lane, e, 4) / 4,
-               c0 << (8 * (v_code_byte(2 * lane, e, 4) % 4) + 4 * (e & 1)));
+               c0 << (8 * (v_code_byte(2 * lane, e, 4) % 4) + v_code_shift(e)));
       atomicOr(reinterpret_cast<uint32_t*>(s_blk) + v_code_byte(2 * lane + 1, e, 4) / 4,
-               c1 << (8 * (v_code_byte(2 * lane + 1, e, 4) % 4) + 4 * (e & 1)));
+               c1 << (8 * (v_code_byte(2 * lane + 1, e, 4) % 4) + v_code_shift(e)));
     }
   }
   __syncthreads();
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(kQThreads) void quant_append_kernel(const QuantPara
       if (p.bits == 8) {
         s_blk[at] = static_cast<uint8_t>(code);
       } else {
-        const int sh = 4 * (e & 1);
+        const int sh = v_code_shift(e);
         s_blk[at] = static_cast<uint8_t>((s_blk[at] & ~(0xF << sh)) | (code << sh));
       }
     }

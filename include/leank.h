@@ -145,7 +145,7 @@ int leank_build_mask(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
  *   v_q      per live head at byte offset v_q_off[h]: V codes in 8-row blocks
  *            [batch][ceil(mid_capacity / 8)][128][8 codes]: 8-bit, byte
  *            ((r / 8) * 128 + c) * 8 + r % 8; 4-bit, 4 bytes per (block,
- *            channel), byte k holding row 2k (low nibble) and 2k + 1.
+ *            channel), byte k holding row k (low nibble) and k + 4.
  *   v_qp     per live head at float offset v_qp_off[h]: float32
  *            [batch][mid_capacity][2] = (scale, minimum) of each middle row.
  *

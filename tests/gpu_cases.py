@@ -164,8 +164,12 @@ def read_pair_q(cache, b, h, t_mid):
     v0 = d.v_q_off[h] + b * (vrows // 8) * blk_bytes
     nb = -(-t_mid // 8)
     vraw = q["v_q"][v0: v0 + nb * blk_bytes]
-    codes = vraw if bits == 8 else _unpack_nibbles(vraw)
-    v_codes = codes.reshape(nb, 128, 8).transpose(0, 2, 1).reshape(-1, 128)[:t_mid]
+    if bits == 8:
+        codes = vraw.reshape(nb, 128, 8)
+    else:  # byte k of a channel's 4 bytes: row k (low nibble), row k + 4 (high nibble)
+        b4 = vraw.reshape(nb, 128, 4)
+        codes = np.concatenate([b4 & 0xF, b4 >> 4], axis=2)
+    v_codes = codes.transpose(0, 2, 1).reshape(-1, 128)[:t_mid]
     vp = q["v_qp"].view(np.float32)
     q0 = d.v_qp_off[h] + b * d.mid_capacity * 2
     vpar = vp[q0: q0 + t_mid * 2].reshape(t_mid, 2)
