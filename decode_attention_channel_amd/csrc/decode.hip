@@ -110,16 +110,22 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   bool step = x.step;
   if (quant && step) {
-    // low-bit middle: the append runs first (one kernel), then the attention
-    // over pos + 1 tokens -- the leaving token is read back as it is stored
-    WorkPlan wq;
-    make_work_plan(c, plan_len + 1, 0, &wq);
-    if (!workspace || !aligned16(workspace) || workspace_bytes < wq.workspace_bytes)
-      return LEANK_EWORKSPACE;
-    st = quant_append_one(c, x.k_new, x.v_new, plan_len, s);
-    if (st != LEANK_OK) return st;
-    step = false;
-    plan_len += 1;
+    // the middle row this append writes (every live head writes the same
+    // row); when it completes a K group, every row of that group changes to
+    // codes, which the other items of a fused call would still read staged:
+    // such a step runs the append kernel, then the attention over pos + 1
+    const int64_t pos = plan_len;
+    const int64_t r = c->window > 0 ? pos - c->window - c->n_sink : pos - c->n_sink;
+    if (r >= 0 && r % LEANK_QUANT_GROUP == LEANK_QUANT_GROUP - 1) {
+      WorkPlan wq;
+      make_work_plan(c, plan_len + 1, 0, &wq);
+      if (!workspace || !aligned16(workspace) || workspace_bytes < wq.workspace_bytes)
+        return LEANK_EWORKSPACE;
+      st = quant_append_one(c, x.k_new, x.v_new, pos, s);
+      if (st != LEANK_OK) return st;
+      step = false;
+      plan_len += 1;
+    }
   }
   WorkPlan w;
   make_work_plan(c, plan_len, step ? 1 : 0, &w);

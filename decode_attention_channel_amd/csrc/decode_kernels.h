@@ -43,6 +43,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "quant.h"
 
 #ifndef LEANK_NT_LOADS
 #define LEANK_NT_LOADS 1
@@ -778,6 +779,9 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) float s_par[kWaves][QB ? 2 * LEANK_HEAD_DIM : 4];
   // paged middle: the physical pages of the item's rows
   __shared__ int32_t s_pages[QB ? 1 : 64];
+  // low-bit fused step: the middle token's V as the cache will hold it
+  __shared__ float s_midv[QB ? LEANK_HEAD_DIM : 1];
+  __shared__ float s_vpar[2];
 
   const int item = blockIdx.x;
   const int b = item / p.items_per_b;
@@ -827,9 +831,17 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
       const int c = t - 128;
       u32x4_t x = zero4;
       if (tok.mid_row >= 0) {
-        const uint16_t *k_row, *blk;
-        middle_row_at(p, hd, b, tok.mid_row, &k_row, &blk);
-        x = *reinterpret_cast<const u32x4_t*>(blk + c * 8);
+        if constexpr (QB != 0) {
+          // the middle row's V code block (QB * 128 bytes)
+          const QSegment qs = q_segment<QB>(p, hd, b, 0);
+          constexpr int kBlkBytes = LEANK_HEAD_DIM * LEANK_V_BLOCK * QB / 8;
+          if (c * 16 < kBlkBytes)
+            x = *reinterpret_cast<const u32x4_t*>(qs.v_codes + static_cast<int64_t>(tok.mid_row / LEANK_V_BLOCK) * kBlkBytes + c * 16);
+        } else {
+          const uint16_t *k_row, *blk;
+          middle_row_at(p, hd, b, tok.mid_row, &k_row, &blk);
+          x = *reinterpret_cast<const u32x4_t*>(blk + c * 8);
+        }
       }
       *reinterpret_cast<u32x4_t*>(s_vblk[1] + c * 8) = x;
       if (t >= 144 && t < 160) {
@@ -980,6 +992,43 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     }
   }
 
+  if constexpr (QB != 0) {
+    if (carries_step && tok.mid_row >= 0) {  // block-uniform
+      // the token that becomes middle row r, as the low-bit cache will hold
+      // it: V quantized per token; K exact in staging (a step whose row
+      // completes a K group is not fused: the host runs the append first)
+      const int e = tok.mid_row % LEANK_V_BLOCK;
+      if (wave == 0) {
+        const int e_ring = tok.slot % LEANK_V_BLOCK;
+        const float x0 = bf16_to_f32(tok.leave_in ? s_vblk[0][(2 * lane) * LEANK_V_BLOCK + e_ring] : s_tok_v[2 * lane]);
+        const float x1 = bf16_to_f32(tok.leave_in ? s_vblk[0][(2 * lane + 1) * LEANK_V_BLOCK + e_ring]
+                                                  : s_tok_v[2 * lane + 1]);
+        uint32_t c0, c1;
+        float sc, lo;
+        quantize_v_row_regs(x0, x1, QB, &c0, &c1, &sc, &lo);
+        s_midv[2 * lane] = fmaf(static_cast<float>(c0), sc, lo);
+        s_midv[2 * lane + 1] = fmaf(static_cast<float>(c1), sc, lo);
+        uint8_t* cb = reinterpret_cast<uint8_t*>(s_vblk[1]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int at = v_code_byte(2 * lane + u, e, QB);
+          const uint32_t code = u ? c1 : c0;
+          if (QB == 8) {
+            cb[at] = static_cast<uint8_t>(code);
+          } else {
+            const int sh = v_code_shift(e);
+            cb[at] = static_cast<uint8_t>((cb[at] & ~(0xF << sh)) | (code << sh));
+          }
+        }
+        if (lane == 0) {
+          s_vpar[0] = sc;
+          s_vpar[1] = lo;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
   if (carries_step) {
     // scores of the two step tokens: full width for a sink / window row,
     // kept channels for a middle row (the leaving token, or the new one
@@ -1051,8 +1100,14 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
       const float w_leave = fast_exp2(s_leave - m_use);
       const uint32_t v_leave =
           tok.leave_in ? s_vblk[0][ch * LEANK_V_BLOCK + tok.slot % LEANK_V_BLOCK] : 0u;
-      a = fmaf(w_new, __uint_as_float(static_cast<uint32_t>(s_tok_v[ch]) << 16), a);
-      a = fmaf(w_leave, __uint_as_float(v_leave << 16), a);
+      float vn = __uint_as_float(static_cast<uint32_t>(s_tok_v[ch]) << 16);
+      float vl = __uint_as_float(v_leave << 16);
+      if constexpr (QB != 0) {
+        // the middle token's V as the low-bit cache holds it
+        if (tok.mid_row >= 0) (tok.leave_in ? vl : vn) = s_midv[ch];
+      }
+      a = fmaf(w_new, vn, a);
+      a = fmaf(w_leave, vl, a);
       l += w_new + w_leave;
     }
     rec[k] = a;
@@ -1069,7 +1124,26 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     // 16-byte groups of the two V blocks, so no lane reads another's LDS.
     const int e_ring = tok.slot % LEANK_V_BLOCK;
     const int e_mid = tok.mid_row % LEANK_V_BLOCK;
-    if (tok.mid_row >= 0) {
+    if constexpr (QB != 0) {
+      if (tok.mid_row >= 0) {
+        // staged K row, V codes, V parameters
+        const QSegment qs = q_segment<QB>(p, hd, b, 0);
+        const int r = tok.mid_row;
+        const int which = tok.leave_in ? 1 : 0;
+        if (2 * lane < hd.kept)
+          reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(qs.k_stage) +
+                                      static_cast<int64_t>(r % LEANK_QUANT_GROUP) * hd.kept)[lane] =
+              compact_from_lds(s_tok_k[which], s_idx, hd.kept, lane);
+        constexpr int kBlkBytes = LEANK_HEAD_DIM * LEANK_V_BLOCK * QB / 8;
+        if (lane < kBlkBytes / 16)
+          reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(qs.v_codes) +
+                                     static_cast<int64_t>(r / LEANK_V_BLOCK) * kBlkBytes)[lane] =
+              reinterpret_cast<const u32x4_t*>(s_vblk[1])[lane];
+        if (lane == 0)
+          *reinterpret_cast<float2*>(const_cast<float*>(qs.v_par) + static_cast<int64_t>(r) * 2) =
+              make_float2(s_vpar[0], s_vpar[1]);
+      }
+    } else if (tok.mid_row >= 0) {
       // middle row: kept K channels (compacted) and V
       const int which = tok.leave_in ? 1 : 0;
       const uint16_t *k_row_c, *blk_c;

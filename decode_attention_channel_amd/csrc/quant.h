@@ -43,6 +43,106 @@ struct QuantParams {
   QuantHead heads[LEANK_MAX_KV_HEADS];
 };
 
+// ---------------------------------------------------------------- the code decision
+//
+// A group of values x is held as codes of `bits` bits with lo = min x,
+// scale = (max x - lo) / (2^bits - 1), code = rint((x - lo) / scale) clamped
+// to [0, 2^bits - 1] (0 when scale = 0), decided in IEEE float32: one
+// subtraction, one correctly rounded division, round half to even.
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// scale of a group with minimum lo and maximum hi
+__device__ __forceinline__ float quant_scale(float lo, float hi, int bits) {
+  return __fdiv_rn(__fsub_rn(hi, lo), static_cast<float>((1 << bits) - 1));
+}
+
+__device__ __forceinline__ uint32_t quant_code(float x, float lo, float scale, int bits) {
+  if (!(scale > 0.0f)) return 0u;
+  const float r = rintf(__fdiv_rn(__fsub_rn(x, lo), scale));
+  const float top = static_cast<float>((1 << bits) - 1);
+  return static_cast<uint32_t>(fminf(fmaxf(r, 0.0f), top));
+}
+
+// One V row (128 channels, a wavefront's 64 lanes holding channels 2 lane,
+// 2 lane + 1 as floats x0, x1) quantized per token: the two codes, and the
+// row's (scale, lo) in every lane.
+__device__ __forceinline__ void quantize_v_row_regs(float x0, float x1, int bits, uint32_t* c0,
+                                                    uint32_t* c1, float* scale_out, float* lo_out) {
+  float lo = fminf(x0, x1), hi = fmaxf(x0, x1);
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = fminf(lo, __shfl_xor(lo, off));
+    hi = fmaxf(hi, __shfl_xor(hi, off));
+  }
+  const float scale = quant_scale(lo, hi, bits);
+  *c0 = quant_code(x0, lo, scale, bits);
+  *c1 = quant_code(x1, lo, scale, bits);
+  *scale_out = scale;
+  *lo_out = lo;
+}
+
+// The same, writing (scale, lo) to params through lane 0.
+__device__ __forceinline__ void quantize_v_row(float x0, float x1, int bits, float* params,
+                                               uint32_t* c0, uint32_t* c1) {
+  float scale, lo;
+  quantize_v_row_regs(x0, x1, bits, c0, c1, &scale, &lo);
+  if ((threadIdx.x & 63) == 0) {
+    params[0] = scale;
+    params[1] = lo;
+  }
+}
+
+// Byte offset of (row e of a block, channel ch) within one V code block
+// (4-bit: byte k of a channel's 4 bytes holds rows k and k + 4), and the
+// nibble of that byte holding row e.
+__device__ __forceinline__ int v_code_byte(int ch, int e, int bits) {
+  return bits == 8 ? ch * 8 + e : ch * 4 + (e & 3);
+}
+__device__ __forceinline__ int v_code_shift(int e) { return 4 * (e >> 2); }
+
+__device__ __forceinline__ float group_value(float x) { return x; }
+__device__ __forceinline__ float group_value(uint16_t x) { return bf16_to_f32(x); }
+
+// Quantizes one complete K group (64 rows x c kept channels in
+// s_x[row * c + j], floats or bf16 bits) per channel into codes (row-major,
+// bits wide; 4-bit: the even channel in the low nibble) and (scale, lo)
+// pairs [c][2], and leaves each channel's scale and lo in s_scale / s_lo.
+// Every thread of a workgroup of `threads` threads calls it.
+template <typename T>
+__device__ __forceinline__ void quantize_k_group_wg(const T* s_x, int c, int bits, int threads,
+                                                    float* s_scale, float* s_lo, uint8_t* codes,
+                                                    float* params) {
+  const int t = threadIdx.x;
+  if (t < c) {
+    float lo = group_value(s_x[t]), hi = lo;
+    for (int r = 1; r < LEANK_QUANT_GROUP; ++r) {
+      lo = fminf(lo, group_value(s_x[r * c + t]));
+      hi = fmaxf(hi, group_value(s_x[r * c + t]));
+    }
+    const float scale = quant_scale(lo, hi, bits);
+    s_scale[t] = scale;
+    s_lo[t] = lo;
+    params[2 * t] = scale;
+    params[2 * t + 1] = lo;
+  }
+  __syncthreads();
+  if (bits == 8) {
+    for (int i = t; i < LEANK_QUANT_GROUP * c; i += threads) {
+      const int j = i % c;
+      codes[i] = static_cast<uint8_t>(quant_code(group_value(s_x[i]), s_lo[j], s_scale[j], 8));
+    }
+  } else {
+    for (int i = t; i < LEANK_QUANT_GROUP * c / 2; i += threads) {
+      const int j = (2 * i) % c;
+      const uint32_t a = quant_code(group_value(s_x[2 * i]), s_lo[j], s_scale[j], 4);
+      const uint32_t b = quant_code(group_value(s_x[2 * i + 1]), s_lo[j + 1], s_scale[j + 1], 4);
+      codes[i] = static_cast<uint8_t>(a | (b << 4));
+    }
+  }
+}
+
 void fill_quant_params(const leank_layer_cache* c, QuantParams* p);
 // Middle rows of a prefill of n_new tokens into an empty cache (the sink and
 // window rows are written by the ordinary pack kernel).

@@ -1,12 +1,7 @@
 // Low-bit middle streams: packing into a cache planned by
 // leank_plan_layer_q (LeanK page, section 4.2 and its deployment notes --
 // quantization after prune and reorganisation; white paper section 5.2.1 --
-// KIVI's per-channel K and per-token V).
-//
-// A group of values x is held as codes of `bits` bits with lo = min x,
-// scale = (max x - lo) / (2^bits - 1), code = rint((x - lo) / scale) clamped
-// to [0, 2^bits - 1] (0 when scale = 0).  The code is decided in IEEE float32
-// (one subtraction, one correctly rounded division, round half to even).
+// KIVI's per-channel K and per-token V).  The code decision is in quant.h.
 // K: per kept channel over each group of 64 middle rows; the rows of a group
 // that is not complete yet wait in a bf16 staging buffer.  V: per token.
 
@@ -17,83 +12,11 @@ namespace {
 
 constexpr int kQThreads = 256;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
 
-// (scale, lo) of a group with minimum lo and maximum hi
-__device__ __forceinline__ float quant_scale(float lo, float hi, int bits) {
-  return __fdiv_rn(__fsub_rn(hi, lo), static_cast<float>((1 << bits) - 1));
+__device__ __forceinline__ void quantize_k_group(const float* s_x, int c, int bits, float* s_scale,
+                                                 float* s_lo, uint8_t* codes, float* params) {
+  quantize_k_group_wg(s_x, c, bits, kQThreads, s_scale, s_lo, codes, params);
 }
-
-__device__ __forceinline__ uint32_t quant_code(float x, float lo, float scale, int bits) {
-  if (!(scale > 0.0f)) return 0u;
-  const float r = rintf(__fdiv_rn(__fsub_rn(x, lo), scale));
-  const float top = static_cast<float>((1 << bits) - 1);
-  return static_cast<uint32_t>(fminf(fmaxf(r, 0.0f), top));
-}
-
-// Quantizes one complete K group (64 rows x c kept channels held as floats
-// in s_x[row * c + j]) into codes at `codes` (row-major, bits wide) and
-// (scale, lo) pairs at `params` [c][2].  All kQThreads threads call it.
-__device__ void quantize_k_group(const float* s_x, int c, int bits, float* s_scale, float* s_lo,
-                                 uint8_t* codes, float* params) {
-  const int t = threadIdx.x;
-  if (t < c) {
-    float lo = s_x[t], hi = s_x[t];
-    for (int r = 1; r < LEANK_QUANT_GROUP; ++r) {
-      lo = fminf(lo, s_x[r * c + t]);
-      hi = fmaxf(hi, s_x[r * c + t]);
-    }
-    const float scale = quant_scale(lo, hi, bits);
-    s_scale[t] = scale;
-    s_lo[t] = lo;
-    params[2 * t] = scale;
-    params[2 * t + 1] = lo;
-  }
-  __syncthreads();
-  if (bits == 8) {
-    for (int i = t; i < LEANK_QUANT_GROUP * c; i += kQThreads) {
-      const int j = i % c;
-      codes[i] = static_cast<uint8_t>(quant_code(s_x[i], s_lo[j], s_scale[j], 8));
-    }
-  } else {
-    // two channels per byte, the even channel in the low nibble
-    for (int i = t; i < LEANK_QUANT_GROUP * c / 2; i += kQThreads) {
-      const int j = (2 * i) % c;
-      const uint32_t a = quant_code(s_x[2 * i], s_lo[j], s_scale[j], 4);
-      const uint32_t b = quant_code(s_x[2 * i + 1], s_lo[j + 1], s_scale[j + 1], 4);
-      codes[i] = static_cast<uint8_t>(a | (b << 4));
-    }
-  }
-}
-
-// One V row (128 channels, a wavefront's 64 lanes holding channels 2 lane,
-// 2 lane + 1 as floats x0, x1) quantized per token.  Returns the two codes
-// and writes (scale, lo) through lane 0.
-__device__ __forceinline__ void quantize_v_row(float x0, float x1, int bits, float* params,
-                                               uint32_t* c0, uint32_t* c1) {
-  float lo = fminf(x0, x1), hi = fmaxf(x0, x1);
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = fminf(lo, __shfl_xor(lo, off));
-    hi = fmaxf(hi, __shfl_xor(hi, off));
-  }
-  const float scale = quant_scale(lo, hi, bits);
-  *c0 = quant_code(x0, lo, scale, bits);
-  *c1 = quant_code(x1, lo, scale, bits);
-  if ((threadIdx.x & 63) == 0) {
-    params[0] = scale;
-    params[1] = lo;
-  }
-}
-
-// Byte offset of (row e of a block, channel ch) within one V code block
-// (4-bit: byte k of a channel's 4 bytes holds rows k and k + 4), and the
-// nibble of that byte holding row e.
-__device__ __forceinline__ int v_code_byte(int ch, int e, int bits) {
-  return bits == 8 ? ch * 8 + e : ch * 4 + (e & 3);
-}
-__device__ __forceinline__ int v_code_shift(int e) { return 4 * (e >> 2); }
 
 // ---------------------------------------------------------------- bulk prefill
 
