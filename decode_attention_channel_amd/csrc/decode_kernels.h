@@ -277,12 +277,12 @@ __device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, int e
     for (int j = 0; j < 2; ++j) {
       const float p = fast_exp2(s[j][i] - m_use);
       st.l[i] += p;
-      if (head < G) {
-        const __bf16 hi = static_cast<__bf16>(p);
-        const __bf16 lo = static_cast<__bf16>(p - static_cast<float>(hi));
-        p_lds[head * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, hi);
-        p_lds[(16 + head) * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, lo);
-      }
+      // every head's row is written (rows of heads >= G only feed output
+      // rows that are never recorded), so the stores need no branch
+      const __bf16 hi = static_cast<__bf16>(p);
+      const __bf16 lo = static_cast<__bf16>(p - static_cast<float>(hi));
+      p_lds[head * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, hi);
+      p_lds[(16 + head) * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, lo);
     }
   }
   const u32x4_t pa_hi = *reinterpret_cast<const u32x4_t*>(p_lds + col * kTileRows + 8 * grp);
@@ -373,14 +373,22 @@ __device__ __forceinline__ void attend_range_paged(const uint16_t* pool, int64_t
 // ---------------------------------------------------------------- low-bit middle
 //
 // A middle item of a cache with low-bit streams reads, per 32-row tile:
-//   K  codes of a complete 64-row group, dequantized per element with the
-//      group's per-channel (scale, min) into the bf16 B operand; or, in the
-//      group that is not complete yet, the bf16 staging rows as they are;
-//   V  codes of the 8-row blocks, turned into exact bf16 integers (4-bit:
-//      128 + code through a byte permute) for the B operand of the PV
-//      product.  The per-token scale multiplies the weight (p' = p * scale)
-//      and sum_t p_t * min'_t is added to every channel of the head at the
-//      end (min' = min, or min - 128 * scale for 4-bit codes).
+//   K  codes of a complete 64-row group, fed to the score product as exact
+//      bf16 integers (8-bit: the code; 4-bit: 128 + code through a byte
+//      permute).  The group's per-channel scale is folded into the query
+//      instead: with K = code * scale + min per channel,
+//        q . K = sum_c (q_c scale_c) code_c + sum_c q_c min_c,
+//      so each wavefront forms q_c * scale_c (bf16 hi + lo parts) and the
+//      group's offset term once per group, and the per-element work of a
+//      tile is only the code conversion.  In the group that is not complete
+//      yet, the bf16 staging rows are read as they are;
+//   V  codes of the 8-row blocks, turned into exact bf16 integers the same
+//      way for the B operand of the PV product.  The per-token scale
+//      multiplies the weight (p' = p * scale) and sum_t p_t * min'_t is
+//      added to every channel of the head at the end (min' = min, or
+//      min - 128 * scale for 4-bit codes).
+// Each wavefront takes whole 64-row groups (items start on group
+// boundaries), so a group's query operands serve its two tiles.
 
 // Pointers of one (batch row, live head) pair's low-bit middle.
 struct QSegment {
@@ -417,7 +425,6 @@ template <int KB, int QB, bool kStaged>
 struct QTileRegs {
   u32x4_t kf[kStaged ? 2 : 1][kStaged ? KB : 1];     // staged K rows (bf16)
   uint32_t kc[2][kStaged ? 1 : KB][QB == 8 ? 2 : 1];  // K codes, 8 channels
-  u32x4_t kpar;                                      // 16 bytes of the group's (scale, min) pairs
   uint32_t vc[8][QB == 8 ? 2 : 1];                   // V codes, 8 rows of one channel
   float vs[2], vm[2];                                // (scale, min) of rows 16 j + col
 };
@@ -450,13 +457,6 @@ __device__ __forceinline__ void load_tile_q(const QSegment& q, int c, int t0, in
       }
     }
   }
-  if constexpr (!kStaged) {
-    // the group's (scale, min) pairs: c * 8 bytes, 16 per lane
-    const int g = t0 / LEANK_QUANT_GROUP;
-    tr.kpar = 4 * lane < 2 * c
-                  ? *reinterpret_cast<const u32x4_t*>(q.k_par + (static_cast<int64_t>(g) * c) * 2 + 4 * lane)
-                  : u32x4_t{0u, 0u, 0u, 0u};
-  }
   const bool v_ok = 8 * grp < nvalid;
   const uint8_t* vt = q.v_codes + (static_cast<int64_t>(t0 / 8 + grp) * LEANK_HEAD_DIM + col) *
                                       (LEANK_V_BLOCK * QB / 8);
@@ -486,6 +486,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
 }
 
+// (a, b) as bf16 pairs hi + lo with hi = bf16(x) and lo = bf16(x - hi): the
+// sum keeps about 16 significant bits of each value
+__device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const __bf16 ah = static_cast<__bf16>(a), bh = static_cast<__bf16>(b);
+  hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ah)) |
+       (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, bh)) << 16);
+  lo = pack_bf16x2(a - static_cast<float>(ah), b - static_cast<float>(bh));
+}
+
+// two floats that bf16 holds exactly (small integers), packed without
+// rounding: the upper halves of their bit patterns
+__device__ __forceinline__ uint32_t pack_exact_bf16x2(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
 // code e (0..7) of 8 packed codes
 template <int QB>
 __device__ __forceinline__ float code_f32(const uint32_t (&w)[QB == 8 ? 2 : 1], int e) {
@@ -493,21 +508,23 @@ __device__ __forceinline__ float code_f32(const uint32_t (&w)[QB == 8 ? 2 : 1], 
   return static_cast<float>((w[0] >> (4 * e)) & 0xfu);
 }
 
-// B operand (8 rows of one channel) from 8 V codes as exact bf16 integers
-// (8-bit: the code; 4-bit: 128 + code -- byte k of the word holds rows k
-// and k + 4, so each pair of rows is one byte permute against the exponent
-// byte of 128).
+// Operand of 8 packed codes as exact bf16 integers, in the order of the
+// 4-byte word(s) w: 8-bit codes in byte order; 4-bit codes as 128 + code,
+// the low nibbles of bytes 0..3 then their high nibbles (one byte permute
+// per pair against the exponent byte of 128).  A V block word (byte k: rows
+// k and k + 4) thus gives rows 0..7 in order; a K code word (byte k:
+// channels 2k and 2k + 1) gives channels 0, 2, 4, 6, 1, 3, 5, 7.
 template <int QB>
 __device__ __forceinline__ u32x4_t v_codes_bf16(const uint32_t (&w)[QB == 8 ? 2 : 1]) {
   u32x4_t r;
   if (QB == 8) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) r[k] = pack_bf16x2(code_f32<QB>(w, 2 * k), code_f32<QB>(w, 2 * k + 1));
+    for (int k = 0; k < 4; ++k) r[k] = pack_exact_bf16x2(code_f32<QB>(w, 2 * k), code_f32<QB>(w, 2 * k + 1));
   } else {
-    const uint32_t lo = w[0] & 0x0f0f0f0fu;          // rows 0..3 in bytes 0..3
-    const uint32_t hi = (w[0] >> 4) & 0x0f0f0f0fu;   // rows 4..7
+    const uint32_t lo = w[0] & 0x0f0f0f0fu;          // low nibbles of bytes 0..3
+    const uint32_t hi = (w[0] >> 4) & 0x0f0f0f0fu;   // high nibbles
     const uint32_t exp128 = 0x43434343u;             // high byte of bf16 128
-    // bytes [row a, 0x43, row a + 1, 0x43]: selectors 0-3 pick the codes, 4 the exponent
+    // bytes [code a, 0x43, code b, 0x43]: selectors 0-3 pick the codes, 4 the exponent
     r[0] = __builtin_amdgcn_perm(exp128, lo, 0x04010400u);
     r[1] = __builtin_amdgcn_perm(exp128, lo, 0x04030402u);
     r[2] = __builtin_amdgcn_perm(exp128, hi, 0x04010400u);
@@ -516,57 +533,108 @@ __device__ __forceinline__ u32x4_t v_codes_bf16(const uint32_t (&w)[QB == 8 ? 2 
   return r;
 }
 
-template <int G, int KB, int QB, bool kStaged, bool kTail>
-__device__ __forceinline__ void compute_tile_q(QTileRegs<KB, QB, kStaged>& tr, int nvalid,
-                                               const u32x4_t (&qa)[KB], float qk_scale,
-                                               uint16_t* __restrict__ p_lds,
-                                               float* __restrict__ par_lds, WaveState& st,
-                                               float (&vmin)[4]) {
+// Query operands of one complete K group for this lane (query head col,
+// channels 32 kk + 8 grp .. +7): q_c * scale_c as bf16 hi + lo parts in the
+// channel order of the lane's K code operand, and the group's offset term
+// sum_c q_c min'_c of query head 4 grp + i in register i (the same for
+// every row; min' = min - 128 * scale for 4-bit codes fed as 128 + code).
+// Both carry the softmax scale, so the scores come out scaled.
+template <int KB>
+struct QGroupOps {
+  u32x4_t qh[KB], ql[KB];
+  f32x4_t bias;
+};
+
+// (scale, min) pairs of the lane's channels 32 kk + 8 grp .. +7 in group g
+// (kept counts are multiples of 8, so the 8 channels are all kept or all not)
+template <int KB>
+__device__ __forceinline__ void load_group_par(const QSegment& q, int c, int g, f32x4_t (&par)[KB][4]) {
+  const int grp = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int kk = 0; kk < KB; ++kk) {
+    const int ch = 32 * kk + 8 * grp;
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(q.k_par + (static_cast<int64_t>(g) * c + ch) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) par[kk][i] = ch < c ? src[i] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+}
+
+template <int KB, int QB>
+__device__ __forceinline__ void group_ops(const f32x4_t (&par)[KB][4], const u32x4_t (&qa)[KB],
+                                          float qk_scale, QGroupOps<KB>& go) {
+  go.bias = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < KB; ++kk) {
+    float sc[8], mn[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[2 * i] = par[kk][i][0];
+      mn[2 * i] = par[kk][i][1];
+      sc[2 * i + 1] = par[kk][i][2];
+      mn[2 * i + 1] = par[kk][i][3];
+    }
+    // the offset term: B operand = min' of the lane's channels (every row alike)
+    u32x4_t mh, ml;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = QB == 4 ? fmaf(-128.0f, sc[2 * w], mn[2 * w]) : mn[2 * w];
+      const float b = QB == 4 ? fmaf(-128.0f, sc[2 * w + 1], mn[2 * w + 1]) : mn[2 * w + 1];
+      uint32_t hi, lo;
+      split_bf16x2(a, b, hi, lo);
+      mh[w] = hi;
+      ml[w] = lo;
+    }
+    go.bias = mfma_bf16(qa[kk], mh, go.bias);
+    go.bias = mfma_bf16(qa[kk], ml, go.bias);
+    // scaled query in the code operand's channel order
+    float qf[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      qf[2 * w] = __uint_as_float(qa[kk][w] << 16);
+      qf[2 * w + 1] = __uint_as_float(qa[kk][w] & 0xffff0000u);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // 4-bit pairs: (0, 2), (4, 6), (1, 3), (5, 7)
+      const int e0 = QB == 4 ? (w < 2 ? 4 * w : 4 * w - 7) : 2 * w;
+      const int e1 = QB == 4 ? e0 + 2 : 2 * w + 1;
+      uint32_t hi, lo;
+      split_bf16x2(qf[e0] * sc[e0] * qk_scale, qf[e1] * sc[e1] * qk_scale, hi, lo);
+      go.qh[kk][w] = hi;
+      go.ql[kk][w] = lo;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) go.bias[i] *= qk_scale;
+}
+
+// Scores of one tile of a complete group, already times the softmax scale.
+template <int KB, int QB>
+__device__ __forceinline__ void group_scores(const QTileRegs<KB, QB, false>& tr,
+                                             const QGroupOps<KB>& go, f32x4_t (&s)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    s[j] = go.bias;
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const u32x4_t kb = v_codes_bf16<QB>(tr.kc[j][kk]);
+      s[j] = mfma_bf16(go.qh[kk], kb, s[j]);
+      s[j] = mfma_bf16(go.ql[kk], kb, s[j]);
+    }
+  }
+}
+
+// Softmax update and PV product of one low-bit tile from its scores
+// (s[j][i]: head 4 grp + i, row 16 j + col; raw dot products, or already
+// times the softmax scale when kScaled).
+template <int G, int QB, bool kTail, bool kScaled>
+__device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&vc)[8][QB == 8 ? 2 : 1],
+                                             const float (&vs)[2], const float (&vm)[2], int nvalid,
+                                             float qk_scale, uint16_t* __restrict__ p_lds,
+                                             WaveState& st, float (&vmin)[4]) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
-
-  f32x4_t s[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
-  if constexpr (kStaged) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int kk = 0; kk < KB; ++kk) s[j] = mfma_bf16(qa[kk], tr.kf[j][kk], s[j]);
-    }
-  } else {
-    // dequantize K (float32 code * scale + min), fed as bf16 hi + lo parts
-    // so that the product keeps about 16 bits of every value; the group's
-    // parameters go through this wavefront's LDS
-    reinterpret_cast<u32x4_t*>(par_lds)[lane] = tr.kpar;
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-      const int ch = 32 * kk + 8 * grp;
-      float sc[8], mn[8];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const f32x4_t pr = *reinterpret_cast<const f32x4_t*>(par_lds + 2 * (ch + e));
-        sc[e] = pr[0];
-        mn[e] = pr[1];
-        sc[e + 1] = pr[2];
-        mn[e + 1] = pr[3];
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        u32x4_t hi, lo;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float a = fmaf(code_f32<QB>(tr.kc[j][kk], 2 * w), sc[2 * w], mn[2 * w]);
-          const float b = fmaf(code_f32<QB>(tr.kc[j][kk], 2 * w + 1), sc[2 * w + 1], mn[2 * w + 1]);
-          const __bf16 ah = static_cast<__bf16>(a), bh = static_cast<__bf16>(b);
-          hi[w] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ah)) |
-                  (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, bh)) << 16);
-          lo[w] = pack_bf16x2(a - static_cast<float>(ah), b - static_cast<float>(bh));
-        }
-        s[j] = mfma_bf16(qa[kk], hi, s[j]);
-        s[j] = mfma_bf16(qa[kk], lo, s[j]);
-      }
-    }
-  }
 
   float mx[4];
   bool grow = false;
@@ -574,7 +642,7 @@ __device__ __forceinline__ void compute_tile_q(QTileRegs<KB, QB, kStaged>& tr, i
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      float v = s[j][i] * qk_scale;
+      float v = kScaled ? s[j][i] : s[j][i] * qk_scale;
       if (kTail && 16 * j + col >= nvalid) v = -INFINITY;
       s[j][i] = v;
     }
@@ -599,7 +667,7 @@ __device__ __forceinline__ void compute_tile_q(QTileRegs<KB, QB, kStaged>& tr, i
   // per-token V scale folded into the weights; the minimum summed apart
   float vmin_row[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) vmin_row[j] = QB == 4 ? fmaf(-128.0f, tr.vs[j], tr.vm[j]) : tr.vm[j];
+  for (int j = 0; j < 2; ++j) vmin_row[j] = QB == 4 ? fmaf(-128.0f, vs[j], vm[j]) : vm[j];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float m_use = st.m[i] == -INFINITY ? 0.0f : st.m[i];
@@ -610,13 +678,13 @@ __device__ __forceinline__ void compute_tile_q(QTileRegs<KB, QB, kStaged>& tr, i
       st.l[i] += pw;
       const bool valid = !kTail || 16 * j + col < nvalid;
       vmin[i] = valid ? fmaf(pw, vmin_row[j], vmin[i]) : vmin[i];
-      const float pv = valid ? pw * tr.vs[j] : 0.0f;
-      if (head < G) {
-        const __bf16 hi = static_cast<__bf16>(pv);
-        const __bf16 lo = static_cast<__bf16>(pv - static_cast<float>(hi));
-        p_lds[head * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, hi);
-        p_lds[(16 + head) * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, lo);
-      }
+      const float pv = valid ? pw * vs[j] : 0.0f;
+      // every head's row is written (rows of heads >= G only feed output
+      // rows that are never recorded), so the stores need no branch
+      const __bf16 hi = static_cast<__bf16>(pv);
+      const __bf16 lo = static_cast<__bf16>(pv - static_cast<float>(hi));
+      p_lds[head * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, hi);
+      p_lds[(16 + head) * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, lo);
     }
   }
   const u32x4_t pa_hi = *reinterpret_cast<const u32x4_t*>(p_lds + col * kTileRows + 8 * grp);
@@ -624,35 +692,51 @@ __device__ __forceinline__ void compute_tile_q(QTileRegs<KB, QB, kStaged>& tr, i
 
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
-    const u32x4_t vb = v_codes_bf16<QB>(tr.vc[n]);
+    const u32x4_t vb = v_codes_bf16<QB>(vc[n]);
     st.o[n] = mfma_bf16(pa_hi, vb, st.o[n]);
     st.o[n] = mfma_bf16(pa_lo, vb, st.o[n]);
   }
 }
 
-// Middle rows [r0, r1) of a low-bit stream.
+// Middle rows [r0, r1) of a low-bit stream (r0 on a group boundary).
 template <int G, int KB, int QB>
 __device__ __forceinline__ void attend_range_q(const QSegment& q, int r0, int r1, int c,
                                                const u32x4_t (&qa)[KB], float qk_scale,
-                                               uint16_t* p_lds, float* par_lds, WaveState& st,
-                                               float (&vmin)[4]) {
+                                               uint16_t* p_lds, WaveState& st, float (&vmin)[4]) {
   const int wave = threadIdx.x >> 6;
-  for (int t0 = r0 + wave * kTileRows; t0 < r1; t0 += kWaves * kTileRows) {
-    const int nvalid = r1 - t0;
-    if (t0 >= q.full_rows) {  // tiles never straddle a group boundary
-      QTileRegs<KB, QB, true> cur;
-      load_tile_q<KB, QB, true>(q, c, t0, nvalid, cur);
-      if (nvalid >= kTileRows)
-        compute_tile_q<G, KB, QB, true, false>(cur, kTileRows, qa, qk_scale, p_lds, par_lds, st, vmin);
-      else
-        compute_tile_q<G, KB, QB, true, true>(cur, nvalid, qa, qk_scale, p_lds, par_lds, st, vmin);
+  for (int g0 = r0 + wave * LEANK_QUANT_GROUP; g0 < r1; g0 += kWaves * LEANK_QUANT_GROUP) {
+    if (g0 >= q.full_rows) {
+      // the open group: staged bf16 rows, the last tile possibly partial
+      for (int t0 = g0; t0 < r1 && t0 < g0 + LEANK_QUANT_GROUP; t0 += kTileRows) {
+        const int nvalid = r1 - t0;
+        QTileRegs<KB, QB, true> cur;
+        load_tile_q<KB, QB, true>(q, c, t0, nvalid, cur);
+        f32x4_t s[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int kk = 0; kk < KB; ++kk) s[j] = mfma_bf16(qa[kk], cur.kf[j][kk], s[j]);
+        }
+        if (nvalid >= kTileRows)
+          softmax_pv_q<G, QB, false, false>(s, cur.vc, cur.vs, cur.vm, kTileRows, qk_scale, p_lds, st, vmin);
+        else
+          softmax_pv_q<G, QB, true, false>(s, cur.vc, cur.vs, cur.vm, nvalid, qk_scale, p_lds, st, vmin);
+      }
     } else {
-      QTileRegs<KB, QB, false> cur;
-      load_tile_q<KB, QB, false>(q, c, t0, nvalid, cur);
-      if (nvalid >= kTileRows)
-        compute_tile_q<G, KB, QB, false, false>(cur, kTileRows, qa, qk_scale, p_lds, par_lds, st, vmin);
-      else
-        compute_tile_q<G, KB, QB, false, true>(cur, nvalid, qa, qk_scale, p_lds, par_lds, st, vmin);
+      // a complete group (g0 + 64 <= full_rows <= r1): two whole tiles,
+      // their loads and the group's parameters issued together
+      f32x4_t par[KB][4];
+      load_group_par<KB>(q, c, g0 / LEANK_QUANT_GROUP, par);
+      QTileRegs<KB, QB, false> t_a, t_b;
+      load_tile_q<KB, QB, false>(q, c, g0, kTileRows, t_a);
+      load_tile_q<KB, QB, false>(q, c, g0 + kTileRows, kTileRows, t_b);
+      QGroupOps<KB> go;
+      group_ops<KB, QB>(par, qa, qk_scale, go);
+      f32x4_t s[2];
+      group_scores<KB, QB>(t_a, go, s);
+      softmax_pv_q<G, QB, false, true>(s, t_a.vc, t_a.vs, t_a.vm, kTileRows, qk_scale, p_lds, st, vmin);
+      group_scores<KB, QB>(t_b, go, s);
+      softmax_pv_q<G, QB, false, true>(s, t_b.vc, t_b.vs, t_b.vm, kTileRows, qk_scale, p_lds, st, vmin);
     }
   }
 }
@@ -775,8 +859,6 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t s_tok_v[LEANK_HEAD_DIM];
   __shared__ __attribute__((aligned(16))) uint16_t s_vblk[2][LEANK_HEAD_DIM * LEANK_V_BLOCK];
   __shared__ float s_tok_s[2][G];
-  // low-bit middle: each wavefront's copy of a K group's (scale, min) pairs
-  __shared__ __attribute__((aligned(16))) float s_par[kWaves][QB ? 2 * LEANK_HEAD_DIM : 4];
   // paged middle: the physical pages of the item's rows
   __shared__ int32_t s_pages[QB ? 1 : 64];
   // low-bit fused step: the middle token's V as the cache will hold it
@@ -911,21 +993,21 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
       if (KBMAX == 1 || kb == 1) {
         u32x4_t qa[1];
         gather_q<G, 1>(s_q, s_idx, false, c, qa);
-        attend_range_q<G, 1, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+        attend_range_q<G, 1, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, st, vmin);
       } else if constexpr (KBMAX >= 2) {
         if (KBMAX == 2 || kb == 2) {
           u32x4_t qa[2];
           gather_q<G, 2>(s_q, s_idx, false, c, qa);
-          attend_range_q<G, 2, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+          attend_range_q<G, 2, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, st, vmin);
         } else if constexpr (KBMAX >= 3) {
           if (kb == 3) {
             u32x4_t qa[3];
             gather_q<G, 3>(s_q, s_idx, false, c, qa);
-            attend_range_q<G, 3, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+            attend_range_q<G, 3, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, st, vmin);
           } else {
             u32x4_t qa[4];
             gather_q<G, 4>(s_q, s_idx, false, c, qa);
-            attend_range_q<G, 4, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, s_par[wave], st, vmin);
+            attend_range_q<G, 4, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, st, vmin);
           }
         }
       }

@@ -320,12 +320,13 @@ int leank_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
  *                                            middle tokens of a live head,
  *   middle tokens of a fully pruned head take no part;
  *   out_j = sum_t softmax(score)_t V[t].
- * bf16 inputs, float32 accumulation.  The context is split into work items
- * whose partial (max, sum, weighted V) records go to the workspace; a second
- * kernel merges each (batch row, KV head) pair's records in a fixed order,
- * so the output does not depend on scheduling.  Two kernel launches,
- * asynchronous on `stream`.  Calls that share a workspace must not overlap
- * in time.
+ * bf16 inputs, float32 accumulation.  q and the cache must be finite: the
+ * output for a NaN or infinite input is unspecified.  The context is split
+ * into work items whose partial (max, sum, weighted V) records go to the
+ * workspace; a second kernel merges each (batch row, KV head) pair's records
+ * in a fixed order, so the output does not depend on scheduling.  Two kernel
+ * launches, asynchronous on `stream`.  Calls that share a workspace must not
+ * overlap in time.
  */
 int leank_decode_attn(const leank_layer_cache* cache, const void* q,
                       int64_t ctx_len, float scale, float* out,
