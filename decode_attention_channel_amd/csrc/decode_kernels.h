@@ -251,16 +251,19 @@ __device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, int e
       if (kTail && (16 * j + col >= nvalid || 16 * j + col == excl_rel)) v = -INFINITY;
       s[j][i] = v;
     }
-    mx[i] = row_max16(fmaxf(s[0][i], s[1][i]));
+    mx[i] = fmaxf(s[0][i], s[1][i]);  // this lane's rows
     grow |= mx[i] > st.m[i] + kRescaleSlack;
   }
+  // a head's tile maximum passes its reference by more than the slack iff
+  // one of its lanes does, so the row reductions run only then
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const float tile_max = row_max16(mx[i]);
       float corr = 1.0f;
-      if (mx[i] > st.m[i] + kRescaleSlack) {
-        corr = st.m[i] == -INFINITY ? 0.0f : fast_exp2(st.m[i] - mx[i]);
-        st.m[i] = mx[i];
+      if (tile_max > st.m[i] + kRescaleSlack) {
+        corr = st.m[i] == -INFINITY ? 0.0f : fast_exp2(st.m[i] - tile_max);
+        st.m[i] = tile_max;
       }
       st.l[i] *= corr;
 #pragma unroll
@@ -420,13 +423,15 @@ __device__ __forceinline__ QSegment q_segment(const DecodeParams& p, const Decod
 }
 
 // Raw operands of one low-bit tile.  kStaged: the tile lies in the K group
-// that is not complete yet, whose rows are read as staged (bf16).
+// that is not complete yet, whose rows are read as staged (bf16).  The
+// score product's column col of sub-tile j is row 2 col + j of the tile, so
+// a lane holds the weights of two adjacent rows and stages them as one pair.
 template <int KB, int QB, bool kStaged>
 struct QTileRegs {
   u32x4_t kf[kStaged ? 2 : 1][kStaged ? KB : 1];     // staged K rows (bf16)
   uint32_t kc[2][kStaged ? 1 : KB][QB == 8 ? 2 : 1];  // K codes, 8 channels
   uint32_t vc[8][QB == 8 ? 2 : 1];                   // V codes, 8 rows of one channel
-  float vs[2], vm[2];                                // (scale, min) of rows 16 j + col
+  float vs[2], vm[2];                                // (scale, min) of rows 2 col + j
 };
 
 template <int KB, int QB, bool kStaged>
@@ -439,9 +444,9 @@ __device__ __forceinline__ void load_tile_q(const QSegment& q, int c, int t0, in
   for (int j = 0; j < 2; ++j) {
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk) {
-      const int row = t0 + 16 * j + col;
+      const int row = t0 + 2 * col + j;
       const int ch = 32 * kk + 8 * grp;
-      const bool ok = ch < c && 16 * j + col < nvalid;
+      const bool ok = ch < c && 2 * col + j < nvalid;
       if constexpr (kStaged) {
         tr.kf[j][kk] = ok ? load_stream16(q.k_stage + static_cast<int64_t>(row - q.full_rows) * c + ch)
                           : u32x4_t{0u, 0u, 0u, 0u};
@@ -473,26 +478,28 @@ __device__ __forceinline__ void load_tile_q(const QSegment& q, int c, int t0, in
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const bool ok = 16 * j + col < nvalid;
-    const float2 pr = ok ? *reinterpret_cast<const float2*>(q.v_par + static_cast<int64_t>(t0 + 16 * j + col) * 2)
+    const bool ok = 2 * col + j < nvalid;
+    const float2 pr = ok ? *reinterpret_cast<const float2*>(q.v_par + static_cast<int64_t>(t0 + 2 * col + j) * 2)
                          : make_float2(0.0f, 0.0f);
     tr.vs[j] = pr.x;
     tr.vm[j] = pr.y;
   }
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// (a, b) rounded to bf16 (nearest even), a in the low half: one conversion
+// instruction for the pair
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // (a, b) as bf16 pairs hi + lo with hi = bf16(x) and lo = bf16(x - hi): the
 // sum keeps about 16 significant bits of each value
 __device__ __forceinline__ void split_bf16x2(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const __bf16 ah = static_cast<__bf16>(a), bh = static_cast<__bf16>(b);
-  hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, ah)) |
-       (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, bh)) << 16);
-  lo = pack_bf16x2(a - static_cast<float>(ah), b - static_cast<float>(bh));
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 // two floats that bf16 holds exactly (small integers), packed without
@@ -625,7 +632,7 @@ __device__ __forceinline__ void group_scores(const QTileRegs<KB, QB, false>& tr,
 }
 
 // Softmax update and PV product of one low-bit tile from its scores
-// (s[j][i]: head 4 grp + i, row 16 j + col; raw dot products, or already
+// (s[j][i]: head 4 grp + i, row 2 col + j; raw dot products, or already
 // times the softmax scale when kScaled).
 template <int G, int QB, bool kTail, bool kScaled>
 __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&vc)[8][QB == 8 ? 2 : 1],
@@ -643,19 +650,22 @@ __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&v
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       float v = kScaled ? s[j][i] : s[j][i] * qk_scale;
-      if (kTail && 16 * j + col >= nvalid) v = -INFINITY;
+      if (kTail && 2 * col + j >= nvalid) v = -INFINITY;
       s[j][i] = v;
     }
-    mx[i] = row_max16(fmaxf(s[0][i], s[1][i]));
+    mx[i] = fmaxf(s[0][i], s[1][i]);  // this lane's rows
     grow |= mx[i] > st.m[i] + kRescaleSlack;
   }
+  // a head's tile maximum passes its reference by more than the slack iff
+  // one of its lanes does, so the row reductions run only then
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const float tile_max = row_max16(mx[i]);
       float corr = 1.0f;
-      if (mx[i] > st.m[i] + kRescaleSlack) {
-        corr = st.m[i] == -INFINITY ? 0.0f : fast_exp2(st.m[i] - mx[i]);
-        st.m[i] = mx[i];
+      if (tile_max > st.m[i] + kRescaleSlack) {
+        corr = st.m[i] == -INFINITY ? 0.0f : fast_exp2(st.m[i] - tile_max);
+        st.m[i] = tile_max;
       }
       st.l[i] *= corr;
       vmin[i] *= corr;
@@ -672,20 +682,22 @@ __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&v
   for (int i = 0; i < 4; ++i) {
     const float m_use = st.m[i] == -INFINITY ? 0.0f : st.m[i];
     const int head = 4 * grp + i;
+    float pv[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const float pw = fast_exp2(s[j][i] - m_use);  // 0 for a dropped row
       st.l[i] += pw;
-      const bool valid = !kTail || 16 * j + col < nvalid;
+      const bool valid = !kTail || 2 * col + j < nvalid;
       vmin[i] = valid ? fmaf(pw, vmin_row[j], vmin[i]) : vmin[i];
-      const float pv = valid ? pw * vs[j] : 0.0f;
-      // every head's row is written (rows of heads >= G only feed output
-      // rows that are never recorded), so the stores need no branch
-      const __bf16 hi = static_cast<__bf16>(pv);
-      const __bf16 lo = static_cast<__bf16>(pv - static_cast<float>(hi));
-      p_lds[head * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, hi);
-      p_lds[(16 + head) * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, lo);
+      pv[j] = valid ? pw * vs[j] : 0.0f;
     }
+    // rows 2 col, 2 col + 1 as one hi and one lo pair; every head's row is
+    // written (rows of heads >= G only feed output rows that are never
+    // recorded), so the stores need no branch
+    uint32_t hi, lo;
+    split_bf16x2(pv[0], pv[1], hi, lo);
+    reinterpret_cast<uint32_t*>(p_lds)[(head * kTileRows) / 2 + col] = hi;
+    reinterpret_cast<uint32_t*>(p_lds)[((16 + head) * kTileRows) / 2 + col] = lo;
   }
   const u32x4_t pa_hi = *reinterpret_cast<const u32x4_t*>(p_lds + col * kTileRows + 8 * grp);
   const u32x4_t pa_lo = *reinterpret_cast<const u32x4_t*>(p_lds + (16 + col) * kTileRows + 8 * grp);
@@ -724,16 +736,20 @@ __device__ __forceinline__ void attend_range_q(const QSegment& q, int r0, int r1
       }
     } else {
       // a complete group (g0 + 64 <= full_rows <= r1): two whole tiles,
-      // their loads and the group's parameters issued together
+      // whose loads are issued with the group's parameters (for up to 64
+      // kept channels; wider heads load the second tile after the first
+      // one's scores, to stay within the register budget)
+      constexpr bool kBothFirst = KB <= 2;
       f32x4_t par[KB][4];
       load_group_par<KB>(q, c, g0 / LEANK_QUANT_GROUP, par);
       QTileRegs<KB, QB, false> t_a, t_b;
       load_tile_q<KB, QB, false>(q, c, g0, kTileRows, t_a);
-      load_tile_q<KB, QB, false>(q, c, g0 + kTileRows, kTileRows, t_b);
+      if (kBothFirst) load_tile_q<KB, QB, false>(q, c, g0 + kTileRows, kTileRows, t_b);
       QGroupOps<KB> go;
       group_ops<KB, QB>(par, qa, qk_scale, go);
       f32x4_t s[2];
       group_scores<KB, QB>(t_a, go, s);
+      if (!kBothFirst) load_tile_q<KB, QB, false>(q, c, g0 + kTileRows, kTileRows, t_b);
       softmax_pv_q<G, QB, false, true>(s, t_a.vc, t_a.vs, t_a.vm, kTileRows, qk_scale, p_lds, st, vmin);
       group_scores<KB, QB>(t_b, go, s);
       softmax_pv_q<G, QB, false, true>(s, t_b.vc, t_b.vs, t_b.vm, kTileRows, qk_scale, p_lds, st, vmin);
