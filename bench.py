@@ -283,6 +283,11 @@ def copy_calibration():
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_llama_b64_4k_counters.md")
 KERNEL_SOURCES = ["decode_attention_channel_amd/csrc/decode_kernels.h",
+                  "decode_attention_channel_amd/csrc/decode_base.h",
+                  "decode_attention_channel_amd/csrc/tile_bf16.h",
+                  "decode_attention_channel_amd/csrc/tile_lowbit.h",
+                  "decode_attention_channel_amd/csrc/step_tokens.h",
+                  "decode_attention_channel_amd/csrc/quant.h",
                   "decode_attention_channel_amd/csrc/decode_g4.hip",
                   "decode_attention_channel_amd/csrc/decode.hip",
                   "decode_attention_channel_amd/csrc/common.h",

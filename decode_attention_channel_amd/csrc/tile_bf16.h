@@ -1,0 +1,200 @@
+// Tiles of bf16 streams: the full-width sink and window rows and the
+// bf16 middle (contiguous or paged).  A wavefront takes 32-row tiles
+// round-robin; per tile it loads K (16-byte rows) and V (8-row blocks),
+// forms the scores and the weights and accumulates P V with the matrix
+// instructions.
+#pragma once
+
+#include "decode_base.h"
+
+namespace leank {
+
+// K and V operands of one 32-row tile.
+template <int KB>
+struct TileRegs {
+  u32x4_t kf[2][KB];  // K rows t0 + 16 j + col, channels 32 kk + 8 grp .. +7
+  u32x4_t vf[8];      // V block t0 / 8 + grp, channel 16 n + col
+};
+
+// Issues the loads of the tile starting at row t0 (rows >= nvalid are
+// outside the item).  kb: K row 0 (row length kstride = c elements); vb: V
+// block 0 of the stream.
+template <int KB>
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ kb, int kstride,
+                                          const uint16_t* __restrict__ vb, int t0, int nvalid,
+                                          int c, TileRegs<KB>& tr) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const uint16_t* kt = kb + static_cast<int64_t>(t0) * kstride;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int row = 16 * j + col;
+      const int ch = 32 * kk + 8 * grp;
+      const bool ok = ch < c && row < nvalid;
+      tr.kf[j][kk] = ok ? load_stream16(kt + row * kstride + ch) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  const uint16_t* vt = vb + (static_cast<int64_t>(t0 / 8 + grp) * LEANK_HEAD_DIM + col) * 8;
+  const bool v_ok = 8 * grp < nvalid;
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+    tr.vf[n] = v_ok ? load_stream16(vt + n * 16 * 8) : u32x4_t{0u, 0u, 0u, 0u};
+}
+
+// Scores, softmax bookkeeping and weighted V of one loaded tile.  The
+// masked variant (kTail) drops rows >= nvalid and row excl_rel (a ring row
+// that a fused step replaces; any value outside [0, 32) drops nothing).
+template <int G, int KB, bool kTail>
+__device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, int excl_rel,
+                                             const u32x4_t (&qa)[KB],
+                                             float qk_scale, uint16_t* __restrict__ p_lds,
+                                             WaveState& st) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  // scores: s[j][i] = head 4 grp + i, row 16 j + col
+  f32x4_t s[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    s[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) s[j] = mfma_bf16(qa[kk], tr.kf[j][kk], s[j]);
+  }
+
+  float mx[4];
+  bool grow = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      float v = s[j][i] * qk_scale;
+      if (kTail && (16 * j + col >= nvalid || 16 * j + col == excl_rel)) v = -INFINITY;
+      s[j][i] = v;
+    }
+    mx[i] = fmaxf(s[0][i], s[1][i]);  // this lane's rows
+    grow |= mx[i] > st.m[i] + kRescaleSlack;
+  }
+  // a head's tile maximum passes its reference by more than the slack iff
+  // one of its lanes does, so the row reductions run only then
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float tile_max = row_max16(mx[i]);
+      float corr = 1.0f;
+      if (tile_max > st.m[i] + kRescaleSlack) {
+        corr = st.m[i] == -INFINITY ? 0.0f : fast_exp2(st.m[i] - tile_max);
+        st.m[i] = tile_max;
+      }
+      st.l[i] *= corr;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) st.o[n][i] *= corr;
+    }
+  }
+
+  // weights, staged in LDS as bf16 hi/lo parts: p_lds[part][head][row]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float m_use = st.m[i] == -INFINITY ? 0.0f : st.m[i];
+    const int head = 4 * grp + i;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float p = fast_exp2(s[j][i] - m_use);
+      st.l[i] += p;
+      // every head's row is written (rows of heads >= G only feed output
+      // rows that are never recorded), so the stores need no branch
+      const __bf16 hi = static_cast<__bf16>(p);
+      const __bf16 lo = static_cast<__bf16>(p - static_cast<float>(hi));
+      p_lds[head * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, hi);
+      p_lds[(16 + head) * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, lo);
+    }
+  }
+  const u32x4_t pa_hi = *reinterpret_cast<const u32x4_t*>(p_lds + col * kTileRows + 8 * grp);
+  const u32x4_t pa_lo = *reinterpret_cast<const u32x4_t*>(p_lds + (16 + col) * kTileRows + 8 * grp);
+
+  if (kTail) {
+    // zero the V rows of the lane's block that are dropped
+    u32x4_t keep;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int e0 = 8 * grp + 2 * w, e1 = e0 + 1;
+      keep[w] = (e0 < nvalid && e0 != excl_rel ? 0x0000ffffu : 0u) |
+                (e1 < nvalid && e1 != excl_rel ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) tr.vf[n] &= keep;
+  }
+
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    st.o[n] = mfma_bf16(pa_hi, tr.vf[n], st.o[n]);
+    st.o[n] = mfma_bf16(pa_lo, tr.vf[n], st.o[n]);
+  }
+}
+
+// Rows [r0, r1) of one stream, except row excl (-1: none).
+template <int G, int KB>
+__device__ __forceinline__ void attend_range(const uint16_t* kb, int kstride, const uint16_t* vb,
+                                             int r0, int r1, int excl, int c,
+                                             const u32x4_t (&qa)[KB], float qk_scale,
+                                             uint16_t* p_lds, WaveState& st) {
+  const int wave = threadIdx.x >> 6;
+  int t0 = r0 + wave * kTileRows;
+#if LEANK_PREFETCH
+  // the next tile's loads are in flight while this one computes
+  TileRegs<KB> cur;
+  if (t0 < r1) load_tile<KB>(kb, kstride, vb, t0, r1 - t0, c, cur);
+  for (; t0 < r1; t0 += kWaves * kTileRows) {
+    const int tn = t0 + kWaves * kTileRows;
+    TileRegs<KB> nxt;
+    if (tn < r1) load_tile<KB>(kb, kstride, vb, tn, r1 - tn, c, nxt);
+    const int nvalid = r1 - t0;
+    if (nvalid >= kTileRows && static_cast<unsigned>(excl - t0) >= kTileRows) {
+      compute_tile<G, KB, false>(cur, kTileRows, -1, qa, qk_scale, p_lds, st);
+    } else {
+      compute_tile<G, KB, true>(cur, nvalid, excl - t0, qa, qk_scale, p_lds, st);
+    }
+    cur = nxt;
+  }
+#else
+  for (; t0 < r1; t0 += kWaves * kTileRows) {
+    const int nvalid = r1 - t0;
+    TileRegs<KB> cur;
+    load_tile<KB>(kb, kstride, vb, t0, nvalid, c, cur);
+    if (nvalid >= kTileRows && static_cast<unsigned>(excl - t0) >= kTileRows) {
+      compute_tile<G, KB, false>(cur, kTileRows, -1, qa, qk_scale, p_lds, st);
+    } else {
+      compute_tile<G, KB, true>(cur, nvalid, excl - t0, qa, qk_scale, p_lds, st);
+    }
+  }
+#endif
+}
+
+// Middle rows [r0, r1) of a paged stream: r0 is a multiple of the page
+// size and s_pages holds the physical pages of rows r0, r0 + 64, ...
+// (tiles never straddle a page: both are 32-row aligned).
+template <int G, int KB>
+__device__ __forceinline__ void attend_range_paged(const uint16_t* pool, int64_t page_elems,
+                                                   const int32_t* s_pages, int64_t k_off,
+                                                   int64_t v_off, int r0, int r1, int c,
+                                                   const u32x4_t (&qa)[KB], float qk_scale,
+                                                   uint16_t* p_lds, WaveState& st) {
+  const int wave = threadIdx.x >> 6;
+  for (int t0 = r0 + wave * kTileRows; t0 < r1; t0 += kWaves * kTileRows) {
+    const int nvalid = r1 - t0;
+    const uint16_t* page = pool + static_cast<int64_t>(s_pages[(t0 - r0) / LEANK_PAGE_ROWS]) * page_elems;
+    const int t_in = t0 % LEANK_PAGE_ROWS;
+    TileRegs<KB> cur;
+    load_tile<KB>(page + k_off, c, page + v_off, t_in, nvalid, c, cur);
+    if (nvalid >= kTileRows) {
+      compute_tile<G, KB, false>(cur, kTileRows, -1, qa, qk_scale, p_lds, st);
+    } else {
+      compute_tile<G, KB, true>(cur, nvalid, -1, qa, qk_scale, p_lds, st);
+    }
+  }
+}
+
+}  // namespace leank
