@@ -94,6 +94,11 @@ struct DecodeParams {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+// LDS staging is written in 16- or 32-bit pieces and read back as vectors:
+// these types may alias any other, so no access is reordered across them
+typedef uint32_t u32x4_alias_t __attribute__((ext_vector_type(4), may_alias));
+typedef uint32_t u32x2_alias_t __attribute__((ext_vector_type(2), may_alias));
+typedef float f32x4_alias_t __attribute__((ext_vector_type(4), may_alias));
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

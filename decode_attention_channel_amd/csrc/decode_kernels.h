@@ -83,21 +83,21 @@ __device__ __forceinline__ void attend_middle(const DecodeParams& p, const Decod
     if (KBMAX == 1 || kb == 1) {
       u32x4_t qa[1];
       gather_q<G, 1>(s_q, s_idx, false, c, qa);
-      attend_range_q<G, 1, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, st, vmin);
+      attend_range_q<G, 1, QB>(q, r0, r1, c, qa, s_q, s_idx, p.qk_scale, p_lds, st, vmin);
     } else if constexpr (KBMAX >= 2) {
       if (KBMAX == 2 || kb == 2) {
         u32x4_t qa[2];
         gather_q<G, 2>(s_q, s_idx, false, c, qa);
-        attend_range_q<G, 2, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, st, vmin);
+        attend_range_q<G, 2, QB>(q, r0, r1, c, qa, s_q, s_idx, p.qk_scale, p_lds, st, vmin);
       } else if constexpr (KBMAX >= 3) {
         if (kb == 3) {
           u32x4_t qa[3];
           gather_q<G, 3>(s_q, s_idx, false, c, qa);
-          attend_range_q<G, 3, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, st, vmin);
+          attend_range_q<G, 3, QB>(q, r0, r1, c, qa, s_q, s_idx, p.qk_scale, p_lds, st, vmin);
         } else {
           u32x4_t qa[4];
           gather_q<G, 4>(s_q, s_idx, false, c, qa);
-          attend_range_q<G, 4, QB>(q, r0, r1, c, qa, p.qk_scale, p_lds, st, vmin);
+          attend_range_q<G, 4, QB>(q, r0, r1, c, qa, s_q, s_idx, p.qk_scale, p_lds, st, vmin);
         }
       }
     }
@@ -173,7 +173,9 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ float s_l[kWaves][G];
   __shared__ uint16_t s_q[G * LEANK_HEAD_DIM];
   __shared__ int16_t s_idx[LEANK_HEAD_DIM];
-  __shared__ __attribute__((aligned(16))) uint16_t s_p[kWaves][2 * 16 * kTileRows];
+  // per wavefront: the weight staging of a tile (low-bit: of a 64-row group,
+  // and that group's parameter and query tables)
+  __shared__ __attribute__((aligned(16))) uint16_t s_p[kWaves][QB ? group_lds_halves<KBMAX, G>() : 2 * 16 * kTileRows];
   // fused step: K rows of the new token [0] and the leaving token [1], the
   // new token's V, the V blocks (8 rows, as stored) of the ring row [0] and
   // of the middle row [1] the append writes, and the two tokens' scaled
@@ -216,7 +218,7 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   if ((middle || carries_step) && t >= 128 && t < 144)
     *reinterpret_cast<u32x4_t*>(s_idx + (t - 128) * 8) =
         *reinterpret_cast<const u32x4_t*>(p.kept_idx + h * LEANK_HEAD_DIM + (t - 128) * 8);
-  for (int k = lane; k < 2 * 16 * kTileRows / 8; k += 64)
+  for (int k = lane; k < (QB ? group_lds_halves<KBMAX, G>() : 2 * 16 * kTileRows) / 8; k += 64)
     reinterpret_cast<u32x4_t*>(s_p[wave])[k] = u32x4_t{0u, 0u, 0u, 0u};
   const int64_t pair = static_cast<int64_t>(b) * p.n_kv + h;
   StepTokens tok{};

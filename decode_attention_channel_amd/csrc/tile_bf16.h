@@ -112,8 +112,8 @@ __device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, int e
       p_lds[(16 + head) * kTileRows + 16 * j + col] = __builtin_bit_cast(uint16_t, lo);
     }
   }
-  const u32x4_t pa_hi = *reinterpret_cast<const u32x4_t*>(p_lds + col * kTileRows + 8 * grp);
-  const u32x4_t pa_lo = *reinterpret_cast<const u32x4_t*>(p_lds + (16 + col) * kTileRows + 8 * grp);
+  const u32x4_t pa_hi = *reinterpret_cast<const u32x4_alias_t*>(p_lds + col * kTileRows + 8 * grp);
+  const u32x4_t pa_lo = *reinterpret_cast<const u32x4_alias_t*>(p_lds + (16 + col) * kTileRows + 8 * grp);
 
   if (kTail) {
     // zero the V rows of the lane's block that are dropped

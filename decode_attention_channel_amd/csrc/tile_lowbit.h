@@ -8,23 +8,22 @@ namespace leank {
 
 // ---------------------------------------------------------------- low-bit middle
 //
-// A middle item of a cache with low-bit streams reads, per 32-row tile:
-//   K  codes of a complete 64-row group, fed to the score product as exact
-//      bf16 integers (8-bit: the code; 4-bit: 128 + code through a byte
+// A middle item of a cache with low-bit streams reads, per 64-row group
+// (each wavefront takes whole groups; items start on group boundaries):
+//   K  codes of a complete group, fed to the score product as exact bf16
+//      integers (8-bit: the code; 4-bit: 128 + code through a byte
 //      permute).  The group's per-channel scale is folded into the query
 //      instead: with K = code * scale + min per channel,
 //        q . K = sum_c (q_c scale_c) code_c + sum_c q_c min_c,
 //      so each wavefront forms q_c * scale_c (bf16 hi + lo parts) and the
-//      group's offset term once per group, and the per-element work of a
-//      tile is only the code conversion.  In the group that is not complete
-//      yet, the bf16 staging rows are read as they are;
+//      group's offset term once per group, and the per-element work is
+//      only the code conversion.  The rows of the group that is not
+//      complete yet are read from the bf16 staging rows as they are;
 //   V  codes of the 8-row blocks, turned into exact bf16 integers the same
 //      way for the B operand of the PV product.  The per-token scale
 //      multiplies the weight (p' = p * scale) and sum_t p_t * min'_t is
 //      added to every channel of the head at the end (min' = min, or
 //      min - 128 * scale for 4-bit codes).
-// Each wavefront takes whole 64-row groups (items start on group
-// boundaries), so a group's query operands serve its two tiles.
 
 // Pointers of one (batch row, live head) pair's low-bit middle.
 struct QSegment {
@@ -55,21 +54,20 @@ __device__ __forceinline__ QSegment q_segment(const DecodeParams& p, const Decod
   return q;
 }
 
-// Raw operands of one low-bit tile.  kStaged: the tile lies in the K group
-// that is not complete yet, whose rows are read as staged (bf16).  The
-// score product's column col of sub-tile j is row 2 col + j of the tile, so
-// a lane holds the weights of two adjacent rows and stages them as one pair.
-template <int KB, int QB, bool kStaged>
+// Raw operands of one tile of the open K group (the group that is not
+// complete yet, whose K rows are read as staged bf16).  The score
+// product's column col of sub-tile j is row 2 col + j of the tile, so a
+// lane holds the weights of two adjacent rows and stages them as one pair.
+template <int KB, int QB>
 struct QTileRegs {
-  u32x4_t kf[kStaged ? 2 : 1][kStaged ? KB : 1];     // staged K rows (bf16)
-  uint32_t kc[2][kStaged ? 1 : KB][QB == 8 ? 2 : 1];  // K codes, 8 channels
-  uint32_t vc[8][QB == 8 ? 2 : 1];                   // V codes, 8 rows of one channel
-  float vs[2], vm[2];                                // (scale, min) of rows 2 col + j
+  u32x4_t kf[2][KB];                 // staged K rows (bf16)
+  uint32_t vc[8][QB == 8 ? 2 : 1];  // V codes, 8 rows of one channel
+  float vs[2], vm[2];               // (scale, min) of rows 2 col + j
 };
 
-template <int KB, int QB, bool kStaged>
+template <int KB, int QB>
 __device__ __forceinline__ void load_tile_q(const QSegment& q, int c, int t0, int nvalid,
-                                            QTileRegs<KB, QB, kStaged>& tr) {
+                                            QTileRegs<KB, QB>& tr) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -80,19 +78,8 @@ __device__ __forceinline__ void load_tile_q(const QSegment& q, int c, int t0, in
       const int row = t0 + 2 * col + j;
       const int ch = 32 * kk + 8 * grp;
       const bool ok = ch < c && 2 * col + j < nvalid;
-      if constexpr (kStaged) {
-        tr.kf[j][kk] = ok ? load_stream16(q.k_stage + static_cast<int64_t>(row - q.full_rows) * c + ch)
-                          : u32x4_t{0u, 0u, 0u, 0u};
-      } else {
-        const uint8_t* src = q.k_codes + (static_cast<int64_t>(row) * c + ch) * QB / 8;
-        if constexpr (QB == 8) {
-          const uint2 w = ok ? *reinterpret_cast<const uint2*>(src) : make_uint2(0u, 0u);
-          tr.kc[j][kk][0] = w.x;
-          tr.kc[j][kk][QB == 8 ? 1 : 0] = w.y;
-        } else {
-          tr.kc[j][kk][0] = ok ? *reinterpret_cast<const uint32_t*>(src) : 0u;
-        }
-      }
+      tr.kf[j][kk] = ok ? load_stream16(q.k_stage + static_cast<int64_t>(row - q.full_rows) * c + ch)
+                        : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
   const bool v_ok = 8 * grp < nvalid;
@@ -151,101 +138,284 @@ __device__ __forceinline__ u32x4_t v_codes_bf16(const uint32_t (&w)[QB == 8 ? 2 
   return r;
 }
 
-// Query operands of one complete K group for this lane (query head col,
-// channels 32 kk + 8 grp .. +7): q_c * scale_c as bf16 hi + lo parts in the
-// channel order of the lane's K code operand, and the group's offset term
-// sum_c q_c min'_c of query head 4 grp + i in register i (the same for
-// every row; min' = min - 128 * scale for 4-bit codes fed as 128 + code).
-// Both carry the softmax scale, so the scores come out scaled.
-template <int KB>
-struct QGroupOps {
-  u32x4_t qh[KB], ql[KB];
-  f32x4_t bias;
+// ---------------------------------------------------------------- complete groups
+//
+// The 64 rows of a complete K group are scored with v_mfma_f32_4x4x4_16b_bf16
+// (16 blocks of 4 rows; lane l = 4 blk + j): row l of the group is lane l,
+// whose B operand is 4 of its K codes as exact bf16 integers, and the A
+// operand of lane l is 4 channels of q_c * scale_c for query head l % 4 of
+// a quad of heads; register i of lane l comes out as the score of head
+// 4 qd + i and row l.  Each lane thus holds every head's score of one row:
+// the softmax bookkeeping runs once per (row, head) instead of once per
+// (row, head slot of the 16 the 16x16 product has), and needs no
+// reductions unless a reference maximum moves.  The channel order of a K
+// code operand follows v_codes_bf16 (4-bit: the even channels of a 4-byte
+// word, then the odd ones); the scaled query is laid out in the same order.
+// The group's offset term sum_c q_c min'_c starts the accumulators.
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma4_bf16(uint2 a, uint2 b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
+// Per-wavefront LDS of the group path, in 16-bit units: the weight staging
+// [part 2][head 16][row 64] (4 KiB), then the group's (scale, min) pairs
+// (4 c) and the scaled-query table, hi and lo parts [quad][4-channel
+// step][head 4][4] (8 NQ c).  The staging rows of heads the group does not
+// write keep finite values (zeros, or earlier weights).
+constexpr int kGroupStage = 2 * 16 * 64;
+template <int KBMAX, int G>
+constexpr int group_lds_halves() {
+  return kGroupStage + 4 * 32 * KBMAX + 8 * ((G + 3) / 4) * 32 * KBMAX;
+}
+
+// Softmax state of the group path: register i of quad qd is query head
+// 4 qd + i; the reference maximum is uniform over the wavefront, the sums
+// are this lane's (row's) parts.
+template <int NQ>
+struct RowState {
+  float m[NQ][4];
+  float l[NQ][4];
+  float vmin[NQ][4];  // sum of weight * V row minimum'
 };
 
-// (scale, min) pairs of the lane's channels 32 kk + 8 grp .. +7 in group g
-// (kept counts are multiples of 8, so the 8 channels are all kept or all not)
-template <int KB>
-__device__ __forceinline__ void load_group_par(const QSegment& q, int c, int g, f32x4_t (&par)[KB][4]) {
-  const int grp = (threadIdx.x & 63) >> 4;
+// wavefront maximum
+__device__ __forceinline__ float wave_max(float x) {
+  x = row_max16(x);
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+// Raw operands of one complete group for this lane: K codes of row lane
+// (c * QB / 8 bytes), V codes of both 32-row halves, the row's V (scale, min).
+template <int KB, int QB>
+struct GroupRegs {
+  f32x4_t par;           // 16 bytes of the group's (scale, min) pairs (lanes < c / 2)
+  uint32_t kc[KB * QB];  // 4-byte words of the K code row (8 or 4 channels each)
+  uint32_t vc[2][8][QB == 8 ? 2 : 1];
+  float vs, vm;
+};
+
+template <int KB, int QB>
+__device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, GroupRegs<KB, QB>& gr) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  // the group's parameters first: the query tables wait only for them
+  gr.par = 4 * lane < 2 * c
+               ? *reinterpret_cast<const f32x4_t*>(q.k_par + static_cast<int64_t>(g0 / LEANK_QUANT_GROUP) * c * 2 + 4 * lane)
+               : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // the row's codes: c * QB / 8 bytes, a multiple of 4 (8-bit: of 8)
+  const uint8_t* krow = q.k_codes + static_cast<int64_t>(g0 + lane) * c * QB / 8;
+  if constexpr (QB == 8) {
 #pragma unroll
-  for (int kk = 0; kk < KB; ++kk) {
-    const int ch = 32 * kk + 8 * grp;
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(q.k_par + (static_cast<int64_t>(g) * c + ch) * 2);
+    for (int i = 0; i < KB * QB / 2; ++i) {
+      const uint2 w = 8 * i < c ? *reinterpret_cast<const uint2*>(krow + 8 * i) : make_uint2(0u, 0u);
+      gr.kc[2 * i] = w.x;
+      gr.kc[2 * i + 1] = w.y;
+    }
+  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) par[kk][i] = ch < c ? src[i] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < KB * QB; ++i)
+      gr.kc[i] = 8 * i < c ? *reinterpret_cast<const uint32_t*>(krow + 4 * i) : 0u;
+  }
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint8_t* vt = q.v_codes + (static_cast<int64_t>((g0 + 32 * half) / 8 + grp) * LEANK_HEAD_DIM + col) *
+                                        (LEANK_V_BLOCK * QB / 8);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const uint8_t* src = vt + n * 16 * (LEANK_V_BLOCK * QB / 8);
+      if constexpr (QB == 8) {
+        const uint2 w = *reinterpret_cast<const uint2*>(src);
+        gr.vc[half][n][0] = w.x;
+        gr.vc[half][n][QB == 8 ? 1 : 0] = w.y;
+      } else {
+        gr.vc[half][n][0] = *reinterpret_cast<const uint32_t*>(src);
+      }
+    }
+  }
+  const float2 pr = *reinterpret_cast<const float2*>(q.v_par + static_cast<int64_t>(g0 + lane) * 2);
+  gr.vs = pr.x;
+  gr.vm = pr.y;
+}
+
+// Builds the group's query tables in this wavefront's LDS and returns the
+// offset term of quad qd's head i in bias[qd][i] (every lane): q' = q *
+// scale * qk_scale (hi + lo), min' = min (8-bit) or min - 128 scale.
+template <int G, int NQ, int QB>
+__device__ __forceinline__ void build_group_tables(const f32x4_t& par16, int c,
+                                                   const uint16_t* s_q, const int16_t* s_idx,
+                                                   float qk_scale, uint16_t* w_lds,
+                                                   float (&bias)[NQ][4]) {
+  const int lane = threadIdx.x & 63;
+  float* par = reinterpret_cast<float*>(w_lds + kGroupStage);  // [c][2]
+  uint16_t* tab = w_lds + kGroupStage + 4 * c;                // hi [NQ][c/4][4][4], then lo
+  // the (scale, min) pairs, 16 bytes per lane, to LDS
+  if (4 * lane < 2 * c) reinterpret_cast<f32x4_alias_t*>(par)[lane] = par16;
+  // entries (head h, kept channel j); head h of quad h / 4
+  for (int e = lane; e < NQ * 4 * c; e += 64) {
+    const int h = e / c;
+    const int j = e - h * c;
+    const float qv = h < G ? bf16_to_f32(s_q[h * LEANK_HEAD_DIM + (s_idx[j] & (LEANK_HEAD_DIM - 1))]) : 0.0f;
+    const float x = qv * par[2 * j] * qk_scale;
+    const __bf16 hi = static_cast<__bf16>(x);
+    const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
+    // 4-channel step and place of channel j in the code operand order
+    const int step = QB == 4 ? 2 * (j >> 3) + (j & 1) : j >> 2;
+    const int pos = QB == 4 ? (j & 7) >> 1 : j & 3;
+    const int at = (((h >> 2) * (c / 4) + step) * 4 + (h & 3)) * 4 + pos;
+    tab[at] = __builtin_bit_cast(uint16_t, hi);
+    tab[NQ * 4 * c + at] = __builtin_bit_cast(uint16_t, lo);
+  }
+  // offset terms: lanes of a head sum its channels, then one lane each
+  constexpr int kLanes = 64 / (NQ * 4);  // lanes per head (16 or 8)
+  const int h = lane / kLanes;
+  const int part = lane - h * kLanes;
+  float sum = 0.0f;
+  if (h < G) {
+    for (int j = part; j < c; j += kLanes) {
+      const float mn = QB == 4 ? fmaf(-128.0f, par[2 * j], par[2 * j + 1]) : par[2 * j + 1];
+      sum = fmaf(bf16_to_f32(s_q[h * LEANK_HEAD_DIM + (s_idx[j] & (LEANK_HEAD_DIM - 1))]), mn, sum);
+    }
+  }
+  sum += dpp_f32<kDppQuadXor1>(sum);
+  sum += dpp_f32<kDppQuadXor2>(sum);
+  sum += dpp_f32<kDppHalfMirror>(sum);
+  if (kLanes == 16) sum += dpp_f32<kDppRowMirror>(sum);
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      bias[qd][i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), (4 * qd + i) * kLanes)) * qk_scale;
   }
 }
 
-template <int KB, int QB>
-__device__ __forceinline__ void group_ops(const f32x4_t (&par)[KB][4], const u32x4_t (&qa)[KB],
-                                          float qk_scale, QGroupOps<KB>& go) {
-  go.bias = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+// One complete group of 64 rows starting at g0 (group g0 / 64).
+template <int G, int KB, int QB>
+__device__ __forceinline__ void attend_group(const GroupRegs<KB, QB>& gr, int c, const uint16_t* s_q,
+                                             const int16_t* s_idx, float qk_scale,
+                                             uint16_t* w_lds, RowState<(G + 3) / 4>& rs,
+                                             WaveState& st) {
+  constexpr int NQ = (G + 3) / 4;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  float bias[NQ][4];
+  build_group_tables<G, NQ, QB>(gr.par, c, s_q, s_idx, qk_scale, w_lds, bias);
+
+  // scores (already times the softmax scale)
+  f32x4_t s[NQ];
 #pragma unroll
-  for (int kk = 0; kk < KB; ++kk) {
-    float sc[8], mn[8];
+  for (int qd = 0; qd < NQ; ++qd) s[qd] = f32x4_t{bias[qd][0], bias[qd][1], bias[qd][2], bias[qd][3]};
+  const uint16_t* tab = w_lds + kGroupStage + 4 * c;
+#pragma unroll
+  for (int w = 0; w < KB * QB; ++w) {  // 4-byte words of the row's codes
+    if (4 * w >= c * QB / 8) continue;  // past the row (c < 32 KB)
+    // code operands of the word: 4-bit: two 4-channel steps; 8-bit: one
+    uint2 kb[QB == 4 ? 2 : 1];
+    if constexpr (QB == 4) {
+      const uint32_t wv = gr.kc[w];
+      const uint32_t lo = wv & 0x0f0f0f0fu, hi = (wv >> 4) & 0x0f0f0f0fu;
+      kb[0] = make_uint2(__builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u),
+                         __builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u));
+      kb[QB == 4 ? 1 : 0] = make_uint2(__builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u),
+                                       __builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u));
+    } else {
+      const uint32_t wv = gr.kc[w];
+      kb[0] = make_uint2(pack_exact_bf16x2(static_cast<float>(wv & 0xffu), static_cast<float>((wv >> 8) & 0xffu)),
+                         pack_exact_bf16x2(static_cast<float>((wv >> 16) & 0xffu), static_cast<float>(wv >> 24)));
+    }
+#pragma unroll
+    for (int u = 0; u < (QB == 4 ? 2 : 1); ++u) {
+      const int step = (QB == 4 ? 2 : 1) * w + u;
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        const int at = ((qd * (c / 4) + step) * 4 + (lane & 3)) * 4;
+        const u32x2_alias_t ahv = *reinterpret_cast<const u32x2_alias_t*>(tab + at);
+        const u32x2_alias_t alv = *reinterpret_cast<const u32x2_alias_t*>(tab + NQ * 4 * c + at);
+        const uint2 ah = make_uint2(ahv[0], ahv[1]), al = make_uint2(alv[0], alv[1]);
+        s[qd] = mfma4_bf16(ah, kb[u], s[qd]);
+        s[qd] = mfma4_bf16(al, kb[u], s[qd]);
+      }
+    }
+  }
+
+  // the reference maxima move only when a score passes one by the slack
+  bool grow = false;
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) grow |= s[qd][i] > rs.m[qd][i] + kRescaleSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    float corr[NQ][4];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mx = wave_max(s[qd][i]);
+        corr[qd][i] = 1.0f;
+        if (mx > rs.m[qd][i] + kRescaleSlack) {
+          corr[qd][i] = rs.m[qd][i] == -INFINITY ? 0.0f : fast_exp2(rs.m[qd][i] - mx);
+          rs.m[qd][i] = mx;
+        }
+        rs.l[qd][i] *= corr[qd][i];
+        rs.vmin[qd][i] *= corr[qd][i];
+      }
+    }
+    // accumulator rows of head 4 grp + i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sc[2 * i] = par[kk][i][0];
-      mn[2 * i] = par[kk][i][1];
-      sc[2 * i + 1] = par[kk][i][2];
-      mn[2 * i + 1] = par[kk][i][3];
-    }
-    // the offset term: B operand = min' of the lane's channels (every row alike)
-    u32x4_t mh, ml;
+      float f = 1.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float a = QB == 4 ? fmaf(-128.0f, sc[2 * w], mn[2 * w]) : mn[2 * w];
-      const float b = QB == 4 ? fmaf(-128.0f, sc[2 * w + 1], mn[2 * w + 1]) : mn[2 * w + 1];
-      uint32_t hi, lo;
-      split_bf16x2(a, b, hi, lo);
-      mh[w] = hi;
-      ml[w] = lo;
-    }
-    go.bias = mfma_bf16(qa[kk], mh, go.bias);
-    go.bias = mfma_bf16(qa[kk], ml, go.bias);
-    // scaled query in the code operand's channel order
-    float qf[8];
+      for (int qd = 0; qd < NQ; ++qd) f = grp == qd ? corr[qd][i] : f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      qf[2 * w] = __uint_as_float(qa[kk][w] << 16);
-      qf[2 * w + 1] = __uint_as_float(qa[kk][w] & 0xffff0000u);
-    }
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // 4-bit pairs: (0, 2), (4, 6), (1, 3), (5, 7)
-      const int e0 = QB == 4 ? (w < 2 ? 4 * w : 4 * w - 7) : 2 * w;
-      const int e1 = QB == 4 ? e0 + 2 : 2 * w + 1;
-      uint32_t hi, lo;
-      split_bf16x2(qf[e0] * sc[e0] * qk_scale, qf[e1] * sc[e1] * qk_scale, hi, lo);
-      go.qh[kk][w] = hi;
-      go.ql[kk][w] = lo;
+      for (int n = 0; n < 8; ++n) st.o[n][i] *= f;
     }
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) go.bias[i] *= qk_scale;
-}
 
-// Scores of one tile of a complete group, already times the softmax scale.
-template <int KB, int QB>
-__device__ __forceinline__ void group_scores(const QTileRegs<KB, QB, false>& tr,
-                                             const QGroupOps<KB>& go, f32x4_t (&s)[2]) {
+  // weights, staged as bf16 hi / lo: w_lds[part][head][row]
+  const float vmin_row = QB == 4 ? fmaf(-128.0f, gr.vs, gr.vm) : gr.vm;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    s[j] = go.bias;
+  for (int qd = 0; qd < NQ; ++qd) {
 #pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-      const u32x4_t kb = v_codes_bf16<QB>(tr.kc[j][kk]);
-      s[j] = mfma_bf16(go.qh[kk], kb, s[j]);
-      s[j] = mfma_bf16(go.ql[kk], kb, s[j]);
+    for (int i = 0; i < 4; ++i) {
+      const float m_use = rs.m[qd][i] == -INFINITY ? 0.0f : rs.m[qd][i];
+      const float pw = fast_exp2(s[qd][i] - m_use);
+      rs.l[qd][i] += pw;
+      rs.vmin[qd][i] = fmaf(pw, vmin_row, rs.vmin[qd][i]);
+      const int head = 4 * qd + i;
+      if (head < G) {
+        const float pv = pw * gr.vs;
+        const __bf16 hi = static_cast<__bf16>(pv);
+        const __bf16 lo = static_cast<__bf16>(pv - static_cast<float>(hi));
+        w_lds[head * 64 + lane] = __builtin_bit_cast(uint16_t, hi);
+        w_lds[(16 + head) * 64 + lane] = __builtin_bit_cast(uint16_t, lo);
+      }
+    }
+  }
+
+  // P V over the two 32-row halves (A operand: head col, rows 8 grp .. +7)
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const u32x4_t pa_hi = *reinterpret_cast<const u32x4_alias_t*>(w_lds + col * 64 + 32 * half + 8 * grp);
+    const u32x4_t pa_lo = *reinterpret_cast<const u32x4_alias_t*>(w_lds + (16 + col) * 64 + 32 * half + 8 * grp);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const u32x4_t vb = v_codes_bf16<QB>(gr.vc[half][n]);
+      st.o[n] = mfma_bf16(pa_hi, vb, st.o[n]);
+      st.o[n] = mfma_bf16(pa_lo, vb, st.o[n]);
     }
   }
 }
 
-// Softmax update and PV product of one low-bit tile from its scores
-// (s[j][i]: head 4 grp + i, row 2 col + j; raw dot products, or already
-// times the softmax scale when kScaled).
-template <int G, int QB, bool kTail, bool kScaled>
+// Softmax update and PV product of one tile of the open group from its
+// raw scores (s[j][i]: head 4 grp + i, row 2 col + j).
+template <int G, int QB, bool kTail>
 __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&vc)[8][QB == 8 ? 2 : 1],
                                              const float (&vs)[2], const float (&vm)[2], int nvalid,
                                              float qk_scale, uint16_t* __restrict__ p_lds,
@@ -260,7 +430,7 @@ __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&v
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      float v = kScaled ? s[j][i] : s[j][i] * qk_scale;
+      float v = s[j][i] * qk_scale;
       if (kTail && 2 * col + j >= nvalid) v = -INFINITY;
       s[j][i] = v;
     }
@@ -310,8 +480,8 @@ __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&v
     reinterpret_cast<uint32_t*>(p_lds)[(head * kTileRows) / 2 + col] = hi;
     reinterpret_cast<uint32_t*>(p_lds)[((16 + head) * kTileRows) / 2 + col] = lo;
   }
-  const u32x4_t pa_hi = *reinterpret_cast<const u32x4_t*>(p_lds + col * kTileRows + 8 * grp);
-  const u32x4_t pa_lo = *reinterpret_cast<const u32x4_t*>(p_lds + (16 + col) * kTileRows + 8 * grp);
+  const u32x4_t pa_hi = *reinterpret_cast<const u32x4_alias_t*>(p_lds + col * kTileRows + 8 * grp);
+  const u32x4_t pa_lo = *reinterpret_cast<const u32x4_alias_t*>(p_lds + (16 + col) * kTileRows + 8 * grp);
 
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
@@ -321,49 +491,78 @@ __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&v
   }
 }
 
-// Middle rows [r0, r1) of a low-bit stream (r0 on a group boundary).
+// Middle rows [r0, r1) of a low-bit stream (r0 on a group boundary): the
+// wavefront's complete groups through the row-per-lane path, then, if it
+// takes it, the open group (staged rows) in the 16x16 tile layout, whose
+// state the row path's state is first folded into.
 template <int G, int KB, int QB>
 __device__ __forceinline__ void attend_range_q(const QSegment& q, int r0, int r1, int c,
-                                               const u32x4_t (&qa)[KB], float qk_scale,
+                                               const u32x4_t (&qa)[KB], const uint16_t* s_q,
+                                               const int16_t* s_idx, float qk_scale,
                                                uint16_t* p_lds, WaveState& st, float (&vmin)[4]) {
+  constexpr int NQ = (G + 3) / 4;
   const int wave = threadIdx.x >> 6;
-  for (int g0 = r0 + wave * LEANK_QUANT_GROUP; g0 < r1; g0 += kWaves * LEANK_QUANT_GROUP) {
-    if (g0 >= q.full_rows) {
-      // the open group: staged bf16 rows, the last tile possibly partial
-      for (int t0 = g0; t0 < r1 && t0 < g0 + LEANK_QUANT_GROUP; t0 += kTileRows) {
-        const int nvalid = r1 - t0;
-        QTileRegs<KB, QB, true> cur;
-        load_tile_q<KB, QB, true>(q, c, t0, nvalid, cur);
-        f32x4_t s[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+  const int lane = threadIdx.x & 63;
+  int g0 = r0 + wave * LEANK_QUANT_GROUP;
+  const int full_end = min(r1, q.full_rows);
+  if (g0 < full_end) {
+    RowState<NQ> rs;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+    for (int qd = 0; qd < NQ; ++qd) {
 #pragma unroll
-          for (int kk = 0; kk < KB; ++kk) s[j] = mfma_bf16(qa[kk], cur.kf[j][kk], s[j]);
-        }
-        if (nvalid >= kTileRows)
-          softmax_pv_q<G, QB, false, false>(s, cur.vc, cur.vs, cur.vm, kTileRows, qk_scale, p_lds, st, vmin);
-        else
-          softmax_pv_q<G, QB, true, false>(s, cur.vc, cur.vs, cur.vm, nvalid, qk_scale, p_lds, st, vmin);
+      for (int i = 0; i < 4; ++i) {
+        rs.m[qd][i] = -INFINITY;
+        rs.l[qd][i] = 0.0f;
+        rs.vmin[qd][i] = 0.0f;
       }
-    } else {
-      // a complete group (g0 + 64 <= full_rows <= r1): two whole tiles,
-      // whose loads are issued with the group's parameters (for up to 64
-      // kept channels; wider heads load the second tile after the first
-      // one's scores, to stay within the register budget)
-      constexpr bool kBothFirst = KB <= 2;
-      f32x4_t par[KB][4];
-      load_group_par<KB>(q, c, g0 / LEANK_QUANT_GROUP, par);
-      QTileRegs<KB, QB, false> t_a, t_b;
-      load_tile_q<KB, QB, false>(q, c, g0, kTileRows, t_a);
-      if (kBothFirst) load_tile_q<KB, QB, false>(q, c, g0 + kTileRows, kTileRows, t_b);
-      QGroupOps<KB> go;
-      group_ops<KB, QB>(par, qa, qk_scale, go);
-      f32x4_t s[2];
-      group_scores<KB, QB>(t_a, go, s);
-      if (!kBothFirst) load_tile_q<KB, QB, false>(q, c, g0 + kTileRows, kTileRows, t_b);
-      softmax_pv_q<G, QB, false, true>(s, t_a.vc, t_a.vs, t_a.vm, kTileRows, qk_scale, p_lds, st, vmin);
-      group_scores<KB, QB>(t_b, go, s);
-      softmax_pv_q<G, QB, false, true>(s, t_b.vc, t_b.vs, t_b.vm, kTileRows, qk_scale, p_lds, st, vmin);
+    }
+    for (; g0 < full_end; g0 += kWaves * LEANK_QUANT_GROUP) {
+      GroupRegs<KB, QB> gr;
+      load_group<KB, QB>(q, c, g0, gr);
+      attend_group<G, KB, QB>(gr, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+    }
+    // fold into the tile layout: head 4 grp + i of lane (col, grp), whose
+    // 16 lanes' sums the record adds up
+    const int grp = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = -INFINITY, l = 0.0f, vm = 0.0f;
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        // sums over the four rows of lanes: the 16 lanes of a row then
+        // hold the head's total between them
+        float lt = rs.l[qd][i], vt = rs.vmin[qd][i];
+        lt += __shfl_xor(lt, 16);
+        vt += __shfl_xor(vt, 16);
+        lt += __shfl_xor(lt, 32);
+        vt += __shfl_xor(vt, 32);
+        if (grp == qd) {
+          m = rs.m[qd][i];
+          l = lt;
+          vm = vt;
+        }
+      }
+      st.m[i] = m;
+      st.l[i] = l;
+      vmin[i] = vm;
+    }
+  }
+  for (; g0 < r1; g0 += kWaves * LEANK_QUANT_GROUP) {
+    // the open group: staged bf16 rows, the last tile possibly partial
+    for (int t0 = g0; t0 < r1 && t0 < g0 + LEANK_QUANT_GROUP; t0 += kTileRows) {
+      const int nvalid = r1 - t0;
+      QTileRegs<KB, QB> cur;
+      load_tile_q<KB, QB>(q, c, t0, nvalid, cur);
+      f32x4_t s[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) s[j] = mfma_bf16(qa[kk], cur.kf[j][kk], s[j]);
+      }
+      if (nvalid >= kTileRows)
+        softmax_pv_q<G, QB, false>(s, cur.vc, cur.vs, cur.vm, kTileRows, qk_scale, p_lds, st, vmin);
+      else
+        softmax_pv_q<G, QB, true>(s, cur.vc, cur.vs, cur.vm, nvalid, qk_scale, p_lds, st, vmin);
     }
   }
 }
