@@ -106,7 +106,7 @@ def _oracle_q(q, k, v, mask, n_sink, window, bits, pairs=None):
 
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("group", [1, 4, 7])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 7, 8])
 @pytest.mark.parametrize("ctx", [3, 20, 20 + 64, 20 + 64 + 37, 20 + 5 * 64 + 1, 1000])
 def test_decode_matches_oracle(bits, group, ctx):
     n_sink, window, batch = 4, 16, 2
@@ -125,6 +125,29 @@ def test_decode_matches_oracle(bits, group, ctx):
     assert torch.equal(out, again)
     assert_close(out.cpu().numpy(), _oracle_q(q, k, v, mask, n_sink, window, bits),
                  f"bits {bits} G {group} ctx {ctx}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("group", [4, 7])
+def test_decode_channel_scales(bits, group):
+    """K channels whose magnitudes differ by orders of magnitude (log-normal
+    scales): the per-channel group scales folded into the query span as
+    wide a range."""
+    n_sink, window, batch, ctx = 4, 16, 2, 20 + 7 * 64 + 9
+    mask = mask_with_counts(np.random.default_rng(5), [32, 64, 128])
+    cache = make_qcache(mask, batch, 3 * group, n_sink, window, ctx, bits)
+    gen = torch.Generator(device=DEV).manual_seed(17 + bits)
+    rng = np.random.default_rng(23)
+    ch_scale = torch.from_numpy(np.exp(rng.normal(0.0, 1.5, size=128)).astype(np.float32)).to(DEV)
+    k = (random_bf16((batch, 3, ctx, 128), gen).float() * ch_scale).to(torch.bfloat16)
+    v = random_bf16((batch, 3, ctx, 128), gen)
+    q = random_bf16((batch, 3 * group, 128), gen, scale=0.3)
+    case("quant decode channel scales", bits, group)
+    dac.leank_pack_k(cache, k, v)
+    out = dac.leank_decode_attn(cache, q)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), _oracle_q(q, k, v, mask, n_sink, window, bits),
+                 f"channel scales bits {bits} G {group}")
 
 
 @pytest.mark.parametrize("bits", [4, 8])
