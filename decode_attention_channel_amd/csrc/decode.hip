@@ -93,10 +93,7 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   if (st != LEANK_OK) return st;
   const bool quant = c->quant_bits != 0;
   int64_t q_prefix[LEANK_MAX_KV_HEADS] = {0}, q_rank[LEANK_MAX_KV_HEADS] = {0};
-  if (quant) {
-    if (x.ctx_lens || x.row_pos) return LEANK_EUNSUPPORTED;  // ragged calls: bf16 caches only
-    if (!canonical_quant_layout(c, q_prefix, q_rank)) return LEANK_EINVAL;
-  }
+  if (quant && !canonical_quant_layout(c, q_prefix, q_rank)) return LEANK_EINVAL;
   if (!q || !out || !aligned16(q) || !aligned16(out)) return LEANK_EINVAL;
   if (x.step) {
     if (!x.k_new || !x.v_new || !aligned16(x.k_new) || !aligned16(x.v_new)) return LEANK_EINVAL;
@@ -109,21 +106,26 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   if (!(scale > 0.0f) || !isfinite(scale)) return LEANK_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   bool step = x.step;
+  bool lens_from_pos = false;  // attention over row_pos[b] + 1 tokens after a separate append
   if (quant && step) {
     // the middle row this append writes (every live head writes the same
     // row); when it completes a K group, every row of that group changes to
     // codes, which the other items of a fused call would still read staged:
-    // such a step runs the append kernel, then the attention over pos + 1
+    // such a step runs the append kernel, then the attention over pos + 1.
+    // So does every ragged step, whose rows complete groups at different
+    // steps.
     const int64_t pos = plan_len;
     const int64_t r = c->window > 0 ? pos - c->window - c->n_sink : pos - c->n_sink;
-    if (r >= 0 && r % LEANK_QUANT_GROUP == LEANK_QUANT_GROUP - 1) {
+    if (x.row_pos || (r >= 0 && r % LEANK_QUANT_GROUP == LEANK_QUANT_GROUP - 1)) {
       WorkPlan wq;
       make_work_plan(c, plan_len + 1, 0, &wq);
       if (!workspace || !aligned16(workspace) || workspace_bytes < wq.workspace_bytes)
         return LEANK_EWORKSPACE;
-      st = quant_append_one(c, x.k_new, x.v_new, pos, s);
+      st = x.row_pos ? quant_append(c, x.k_new, x.v_new, 0, 1, x.row_pos, nullptr, plan_len + 1, s)
+                     : quant_append(c, x.k_new, x.v_new, pos, 1, nullptr, nullptr, c->max_ctx, s);
       if (st != LEANK_OK) return st;
       step = false;
+      lens_from_pos = x.row_pos != nullptr;
       plan_len += 1;
     }
   }
@@ -148,6 +150,7 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   p.row_pos = x.row_pos;
   p.step_pos = plan_len;
   p.step = w.step;
+  p.lens_from_pos = lens_from_pos ? 1 : 0;
   p.n_sink = c->n_sink;
   p.window = c->window;
   p.max_len = static_cast<int32_t>(plan_len);

@@ -61,6 +61,7 @@ struct DecodeParams {
   int32_t n_q;
   int32_t max_len;  // context length the work plan was made for (rows before the append in a step)
   int32_t step;     // 1 in a fused decode step: full-width item 0 of each pair carries the append
+  int32_t lens_from_pos;  // 1: row b attends over row_pos[b] + 1 tokens (appended before the call's kernels)
   int32_t n_sink;
   int32_t window;
   int32_t slots;

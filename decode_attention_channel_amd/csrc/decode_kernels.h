@@ -297,6 +297,11 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     const int len = min(max(p.ctx_lens[b], 0), p.max_len);
     t_sl = min(len, p.slots);
     t_mid = max(0, len - p.slots);
+  } else if (p.lens_from_pos) {  // ragged step whose appends ran first
+    const int64_t pos = p.row_pos[b];
+    const int len = pos >= 0 && pos < p.max_len ? static_cast<int>(pos) + 1 : 0;
+    t_sl = min(len, p.slots);
+    t_mid = max(0, len - p.slots);
   }
   if (!middle) {
     const int r0 = local * p.sl_rows;

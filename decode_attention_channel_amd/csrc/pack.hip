@@ -215,9 +215,10 @@ extern "C" int leank_pack_k(const leank_layer_cache* c, const void* k_new, const
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   if (c->quant_bits != 0) {
-    // low-bit middle: one token per call, or a prefill into an empty cache
-    if (n_new == 1) return quant_append_one(c, k_new, v_new, pos0, s);
-    if (pos0 != 0) return LEANK_EUNSUPPORTED;
+    // low-bit middle: a prefill into an empty cache in bulk; any other
+    // append token by token (each may complete a K group)
+    if (pos0 != 0 || n_new == 1)
+      return quant_append(c, k_new, v_new, pos0, n_new, nullptr, nullptr, c->max_ctx, s);
     p.ring_only = 1;
     p.mode = n_new <= c->window ? kFused : kPlace;
     st = launch(p, n_new, pairs, s);  // sink and window rows
@@ -254,14 +255,15 @@ extern "C" int leank_pack_k_rows(const leank_layer_cache* c, const void* k_new, 
   if (n_new == 0) return LEANK_OK;
   if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return LEANK_EINVAL;
   if (n_new > c->max_ctx) return LEANK_ECAPACITY;
-  if (c->quant_bits != 0) return LEANK_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c->quant_bits != 0)  // token by token per row
+    return quant_append(c, k_new, v_new, 0, n_new, row_pos, row_count, c->max_ctx, s);
 
   PackParams p;
   fill_params(c, k_new, v_new, n_new, &p);
   p.row_pos = row_pos;
   p.row_count = row_count;
   const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (c->window > 0 && n_new <= c->window) {
     p.mode = kFused;
     return launch(p, n_new, pairs, s);

@@ -33,7 +33,13 @@ struct QuantParams {
   int64_t v_rows_cap;  // V code rows per (b, head): whole blocks
   int64_t v_sl_rows;
   int64_t t_mid;       // bulk: middle rows of the prefill
-  int64_t pos;         // one token: its position
+  int64_t pos;         // appends: position of the first token (every row)
+  // appends in a ragged batch: row b appends row_count[b] (null: n_src)
+  // tokens at row_pos[b]; a row whose tokens would end past pos_end is
+  // left untouched
+  const int64_t* row_pos;
+  const int32_t* row_count;
+  int64_t pos_end;
   int32_t n_kv;
   int32_t n_sink;
   int32_t window;
@@ -148,8 +154,11 @@ void fill_quant_params(const leank_layer_cache* c, QuantParams* p);
 // window rows are written by the ordinary pack kernel).
 int quant_pack_bulk(const leank_layer_cache* c, const void* k_new, const void* v_new,
                     int64_t n_new, hipStream_t s);
-// One token at position pos, ring and middle.
-int quant_append_one(const leank_layer_cache* c, const void* k_new, const void* v_new, int64_t pos,
-                     hipStream_t s);
+// n_new tokens at positions pos0 .. (every row), or, with row_pos set, a
+// ragged append as in leank_pack_k_rows (tokens ending past pos_end leave
+// the row untouched): ring and middle, one token after the other.
+int quant_append(const leank_layer_cache* c, const void* k_new, const void* v_new, int64_t pos0,
+                 int64_t n_new, const int64_t* row_pos, const int32_t* row_count, int64_t pos_end,
+                 hipStream_t s);
 
 }  // namespace leank

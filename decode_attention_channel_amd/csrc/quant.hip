@@ -127,90 +127,102 @@ __global__ __launch_bounds__(kQThreads) void quant_append_kernel(const QuantPara
   const int c = hd.kept;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int64_t pos = p.pos;
   const int S = p.n_sink, W = p.window;
-  const uint16_t* k_new = p.k_src + pair * LEANK_HEAD_DIM;
-  const uint16_t* v_new = p.v_src + pair * LEANK_HEAD_DIM;
   uint16_t* ring_k = p.k_sl + pair * p.slots * LEANK_HEAD_DIM;
   uint16_t* ring_v = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM;
-  const int slot = pos < S ? static_cast<int>(pos) : (W > 0 ? S + static_cast<int>((pos - S) % W) : -1);
-
-  // the token that becomes a middle row, if any
-  int64_t r = -1;
-  if (c > 0) {
-    if (pos >= S && W == 0) r = pos - S;
-    else if (W > 0 && pos - W >= S) r = pos - W - S;
+  int64_t pos0 = p.pos, count = p.n_src;
+  if (p.row_pos) {
+    pos0 = p.row_pos[b];
+    count = p.row_count ? p.row_count[b] : p.n_src;
+    // a row whose tokens fall outside the cache is left untouched
+    if (pos0 < 0 || count < 0 || count > p.n_src || pos0 + count > p.pos_end) return;
   }
-  if (t < LEANK_HEAD_DIM) {
-    s_idx[t] = p.kept_idx[h * LEANK_HEAD_DIM + t] & (LEANK_HEAD_DIM - 1);
-    if (r >= 0) {
-      const bool from_ring = W > 0;
-      s_tok[0][t] = from_ring ? ring_k[slot * LEANK_HEAD_DIM + t] : k_new[t];
-      s_tok[1][t] = from_ring ? ring_v[v_elem(slot, t)] : v_new[t];
+  for (int64_t u = 0; u < count; ++u) {
+    // tokens in order: the previous token's reads and writes (ring row, V
+    // block, staged K row) are done and visible to the whole workgroup
+    if (u > 0) __syncthreads();
+    const int64_t pos = pos0 + u;
+    const uint16_t* k_new = p.k_src + (pair * p.n_src + u) * LEANK_HEAD_DIM;
+    const uint16_t* v_new = p.v_src + (pair * p.n_src + u) * LEANK_HEAD_DIM;
+    const int slot = pos < S ? static_cast<int>(pos) : (W > 0 ? S + static_cast<int>((pos - S) % W) : -1);
+
+    // the token that becomes a middle row, if any
+    int64_t r = -1;
+    if (c > 0) {
+      if (pos >= S && W == 0) r = pos - S;
+      else if (W > 0 && pos - W >= S) r = pos - W - S;
     }
-  }
-  const int blk_bytes = LEANK_HEAD_DIM * LEANK_V_BLOCK * p.bits / 8;
-  uint8_t* vblk = nullptr;
-  if (r >= 0) {
-    vblk = p.v_q + hd.v_q_off +
-           (static_cast<int64_t>(b) * (p.v_rows_cap / LEANK_V_BLOCK) + r / LEANK_V_BLOCK) * blk_bytes;
-    for (int i = t; i < blk_bytes / 16; i += kQThreads)
-      reinterpret_cast<uint4*>(s_blk)[i] = reinterpret_cast<const uint4*>(vblk)[i];
-  }
-  __syncthreads();  // the ring row is read before it is replaced below
-
-  if (slot >= 0 && t < 64) {
-    // the new token to its sink or ring row
-    reinterpret_cast<uint32_t*>(ring_k + slot * LEANK_HEAD_DIM)[t] =
-        reinterpret_cast<const uint32_t*>(k_new)[t];
-    store_v_row_word(ring_v, slot, t, reinterpret_cast<const uint32_t*>(v_new)[t]);
-  }
-  if (r < 0) return;
-
-  const int e = static_cast<int>(r % LEANK_V_BLOCK);
-  const int in_group = static_cast<int>(r % LEANK_QUANT_GROUP);
-  if (t < 64) {
-    // V of the middle row, quantized per token, replaces row e of its block
-    const uint32_t w = reinterpret_cast<const uint32_t*>(s_tok[1])[lane];
-    uint32_t c0, c1;
-    quantize_v_row(bf16_lo(w), bf16_hi(w), p.bits,
-                   p.v_qp + hd.v_qp_off + (static_cast<int64_t>(b) * p.mid_cap + r) * 2, &c0, &c1);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int ch = 2 * lane + u;
-      const uint32_t code = u ? c1 : c0;
-      const int at = v_code_byte(ch, e, p.bits);
-      if (p.bits == 8) {
-        s_blk[at] = static_cast<uint8_t>(code);
-      } else {
-        const int sh = v_code_shift(e);
-        s_blk[at] = static_cast<uint8_t>((s_blk[at] & ~(0xF << sh)) | (code << sh));
+    if (t < LEANK_HEAD_DIM) {
+      s_idx[t] = p.kept_idx[h * LEANK_HEAD_DIM + t] & (LEANK_HEAD_DIM - 1);
+      if (r >= 0) {
+        const bool from_ring = W > 0;
+        s_tok[0][t] = from_ring ? ring_k[slot * LEANK_HEAD_DIM + t] : k_new[t];
+        s_tok[1][t] = from_ring ? ring_v[v_elem(slot, t)] : v_new[t];
       }
     }
-  } else if (t >= 64 && t - 64 < c) {
-    // K kept channels to staging
-    const int j = t - 64;
-    p.k_stage[hd.k_stage_off + (static_cast<int64_t>(b) * LEANK_QUANT_GROUP + in_group) * c + j] =
-        s_tok[0][s_idx[j]];
-  }
-  __syncthreads();
-  for (int i = t; i < blk_bytes / 16; i += kQThreads)
-    reinterpret_cast<uint4*>(vblk)[i] = reinterpret_cast<const uint4*>(s_blk)[i];
+    const int blk_bytes = LEANK_HEAD_DIM * LEANK_V_BLOCK * p.bits / 8;
+    uint8_t* vblk = nullptr;
+    if (r >= 0) {
+      vblk = p.v_q + hd.v_q_off +
+             (static_cast<int64_t>(b) * (p.v_rows_cap / LEANK_V_BLOCK) + r / LEANK_V_BLOCK) * blk_bytes;
+      for (int i = t; i < blk_bytes / 16; i += kQThreads)
+        reinterpret_cast<uint4*>(s_blk)[i] = reinterpret_cast<const uint4*>(vblk)[i];
+    }
+    __syncthreads();  // the ring row is read before it is replaced below
 
-  if (in_group != LEANK_QUANT_GROUP - 1) return;
-  // the row completes its group: quantize the 64 staged rows (this row from LDS)
-  const uint16_t* stage = p.k_stage + hd.k_stage_off + static_cast<int64_t>(b) * LEANK_QUANT_GROUP * c;
-  for (int i = t; i < LEANK_QUANT_GROUP * c; i += kQThreads) {
-    const int row = i / c, j = i - (i / c) * c;
-    s_x[i] = bf16_to_f32(row == LEANK_QUANT_GROUP - 1 ? s_tok[0][s_idx[j]] : stage[i]);
+    if (slot >= 0 && t < 64) {
+      // the new token to its sink or ring row
+      reinterpret_cast<uint32_t*>(ring_k + slot * LEANK_HEAD_DIM)[t] =
+          reinterpret_cast<const uint32_t*>(k_new)[t];
+      store_v_row_word(ring_v, slot, t, reinterpret_cast<const uint32_t*>(v_new)[t]);
+    }
+    if (r < 0) continue;
+
+    const int e = static_cast<int>(r % LEANK_V_BLOCK);
+    const int in_group = static_cast<int>(r % LEANK_QUANT_GROUP);
+    if (t < 64) {
+      // V of the middle row, quantized per token, replaces row e of its block
+      const uint32_t w = reinterpret_cast<const uint32_t*>(s_tok[1])[lane];
+      uint32_t c0, c1;
+      quantize_v_row(bf16_lo(w), bf16_hi(w), p.bits,
+                     p.v_qp + hd.v_qp_off + (static_cast<int64_t>(b) * p.mid_cap + r) * 2, &c0, &c1);
+  #pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ch = 2 * lane + u;
+        const uint32_t code = u ? c1 : c0;
+        const int at = v_code_byte(ch, e, p.bits);
+        if (p.bits == 8) {
+          s_blk[at] = static_cast<uint8_t>(code);
+        } else {
+          const int sh = v_code_shift(e);
+          s_blk[at] = static_cast<uint8_t>((s_blk[at] & ~(0xF << sh)) | (code << sh));
+        }
+      }
+    } else if (t >= 64 && t - 64 < c) {
+      // K kept channels to staging
+      const int j = t - 64;
+      p.k_stage[hd.k_stage_off + (static_cast<int64_t>(b) * LEANK_QUANT_GROUP + in_group) * c + j] =
+          s_tok[0][s_idx[j]];
+    }
+    __syncthreads();
+    for (int i = t; i < blk_bytes / 16; i += kQThreads)
+      reinterpret_cast<uint4*>(vblk)[i] = reinterpret_cast<const uint4*>(s_blk)[i];
+
+    if (in_group != LEANK_QUANT_GROUP - 1) continue;
+    // the row completes its group: quantize the 64 staged rows (this row from LDS)
+    const uint16_t* stage = p.k_stage + hd.k_stage_off + static_cast<int64_t>(b) * LEANK_QUANT_GROUP * c;
+    for (int i = t; i < LEANK_QUANT_GROUP * c; i += kQThreads) {
+      const int row = i / c, j = i - (i / c) * c;
+      s_x[i] = bf16_to_f32(row == LEANK_QUANT_GROUP - 1 ? s_tok[0][s_idx[j]] : stage[i]);
+    }
+    __syncthreads();
+    const int64_t g = r / LEANK_QUANT_GROUP;
+    uint8_t* codes = p.k_q + hd.k_q_off +
+                     ((static_cast<int64_t>(b) * p.g_rows + g * LEANK_QUANT_GROUP) * c) * p.bits / 8;
+    float* params = p.k_qp + hd.k_qp_off +
+                    ((static_cast<int64_t>(b) * (p.g_rows / LEANK_QUANT_GROUP) + g) * c) * 2;
+    quantize_k_group(s_x, c, p.bits, s_scale, s_lo, codes, params);
   }
-  __syncthreads();
-  const int64_t g = r / LEANK_QUANT_GROUP;
-  uint8_t* codes = p.k_q + hd.k_q_off +
-                   ((static_cast<int64_t>(b) * p.g_rows + g * LEANK_QUANT_GROUP) * c) * p.bits / 8;
-  float* params = p.k_qp + hd.k_qp_off +
-                  ((static_cast<int64_t>(b) * (p.g_rows / LEANK_QUANT_GROUP) + g) * c) * 2;
-  quantize_k_group(s_x, c, p.bits, s_scale, s_lo, codes, params);
 }
 
 }  // namespace
@@ -267,14 +279,18 @@ int quant_pack_bulk(const leank_layer_cache* c, const void* k_new, const void* v
   return LEANK_OK;
 }
 
-int quant_append_one(const leank_layer_cache* c, const void* k_new, const void* v_new, int64_t pos,
-                     hipStream_t s) {
+int quant_append(const leank_layer_cache* c, const void* k_new, const void* v_new, int64_t pos0,
+                 int64_t n_new, const int64_t* row_pos, const int32_t* row_count, int64_t pos_end,
+                 hipStream_t s) {
   QuantParams p;
   fill_quant_params(c, &p);
   p.k_src = static_cast<const uint16_t*>(k_new);
   p.v_src = static_cast<const uint16_t*>(v_new);
-  p.n_src = 1;
-  p.pos = pos;
+  p.n_src = n_new;
+  p.pos = pos0;
+  p.row_pos = row_pos;
+  p.row_count = row_count;
+  p.pos_end = pos_end;
   const int64_t pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
   if (pairs > INT32_MAX) return LEANK_EUNSUPPORTED;
   hipLaunchKernelGGL(quant_append_kernel, dim3(static_cast<unsigned>(pairs)), dim3(kQThreads), 0,

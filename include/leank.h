@@ -243,10 +243,16 @@ int leank_plan_layer(const int32_t* kept_count_host, int32_t batch,
  * leank_plan_layer_q -- leank_plan_layer for a cache whose middle is held
  * in low-bit streams (quant_bits 4 or 8; 0 gives the bf16 plan).  Same
  * requirements; the caller allocates k_sl, v_sl and the five low-bit
- * buffers.  On such a cache leank_pack_k takes a bulk prefill into an
- * empty cache (pos0 == 0) or one token per call (n_new == 1);
- * leank_decode_attn and leank_decode_step read the low-bit streams.  The
- * ragged (_rows) entry points return LEANK_EUNSUPPORTED for it.
+ * buffers.  Every entry point works on such a cache.  leank_pack_k packs a
+ * prefill into an empty cache (pos0 == 0) in bulk and takes any other
+ * append, like leank_pack_k_rows, token by token in one kernel (a token
+ * that completes a K group quantizes the group).  leank_decode_step fuses
+ * the append into the attention except when the row it moves to the
+ * middle completes a K group, and leank_decode_step_rows always runs the
+ * append first: both then launch the append kernel before the two decode
+ * kernels.  In the ragged decode calls ctx_lens[b] / row_pos[b] must be
+ * the row's current length, since its open K group is staged for that
+ * length.
  */
 int leank_plan_layer_q(const int32_t* kept_count_host, int32_t batch,
                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,

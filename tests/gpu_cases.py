@@ -177,25 +177,29 @@ def read_pair_q(cache, b, h, t_mid):
             "v_codes": v_codes, "v_scale": vpar[:, 0], "v_lo": vpar[:, 1]}
 
 
-def assert_quant_cache_matches(cache, k_bits, v_bits, mask, pairs=None):
+def assert_quant_cache_matches(cache, k_bits, v_bits, mask, pairs=None, rows=None):
     """Bit-exact comparison of a low-bit cache (ring and middle streams) with
-    the oracle's packing of the full context k_bits/v_bits [B, H, T, d]."""
+    the oracle's packing of the full context k_bits/v_bits [B, H, T, d].
+    rows: the cache rows that k_bits' batch entries belong to (default: the
+    same index), so one row of a ragged batch can be checked on its own."""
     d = cache.desc
     kept_count, kept_idx = kept_from_mask(mask)
+    rows = list(range(k_bits.shape[0])) if rows is None else list(rows)
     if pairs is None:
-        pairs = [(b, h) for b in range(d.batch) for h in range(d.n_kv_heads)]
+        pairs = [(rb, h) for rb in range(len(rows)) for h in range(d.n_kv_heads)]
     ref = oracle.pack_reference_q(k_bits, v_bits, kept_count, kept_idx, d.n_sink, d.window,
                                   d.quant_bits)
-    for (b, h) in pairs:
+    for (rb, h) in pairs:
+        b = rows[rb]
         ring_k, ring_v, _, _ = read_pair(cache, b, h, ring_only=True)
         for slot, pos in enumerate(ref["slot_pos"]):
             if pos < 0:
                 continue
-            assert np.array_equal(ring_k[slot], ref["ring_k"][b, h, slot]), (b, h, slot)
-            assert np.array_equal(ring_v[slot], ref["ring_v"][b, h, slot]), (b, h, slot)
+            assert np.array_equal(ring_k[slot], ref["ring_k"][rb, h, slot]), (b, h, slot)
+            assert np.array_equal(ring_v[slot], ref["ring_v"][rb, h, slot]), (b, h, slot)
         if kept_count[h] == 0:
             continue
-        want = ref["mid_q"][h][b]
+        want = ref["mid_q"][h][rb]
         got = read_pair_q(cache, b, h, want["v_codes"].shape[0])
         for key in ("k_codes", "k_stage", "v_codes"):
             assert np.array_equal(got[key], want[key]), (b, h, key)

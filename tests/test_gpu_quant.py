@@ -82,20 +82,72 @@ def test_appends_from_empty(bits):
     assert_quant_cache_matches(cache, bf16_bits(k), bf16_bits(v), mask)
 
 
-def test_quant_pack_rejections():
-    mask = mask_with_counts(np.random.default_rng(2), [32, 0])
-    cache = make_qcache(mask, 1, 2, 4, 8, 100, 4)
-    gen = torch.Generator(device=DEV).manual_seed(2)
-    k = random_bf16((1, 2, 20, 128), gen)
-    case("quant rejections")
-    dac.leank_pack_k(cache, k, k)
-    with pytest.raises(dac.LeankError) as err:   # chunked append into a non-empty cache
-        dac.leank_pack_k(cache, k[:, :, :2].contiguous(), k[:, :, :2].contiguous())
-    assert err.value.status == dac._lib.EUNSUPPORTED
-    with pytest.raises(dac.LeankError) as err:
-        dac.leank_pack_k_rows(cache, k[:, :, :1].contiguous(), k[:, :, :1].contiguous(),
-                              torch.zeros(1, dtype=torch.int64, device=DEV))
-    assert err.value.status == dac._lib.EUNSUPPORTED
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("n_sink,window", [(4, 16), (6, 0)])
+def test_chunked_appends_match_bulk(bits, n_sink, window):
+    """Appends of several tokens into a non-empty cache (token by token in
+    one kernel, across group completions) leave the cache the bulk packing
+    of the same tokens would."""
+    batch, t0 = 2, n_sink + window + 30
+    chunks = [5, 64, 1, 130, 17]
+    total = t0 + sum(chunks)
+    mask = mask_with_counts(np.random.default_rng(31 + bits), COUNTS)
+    n_kv = mask.shape[0]
+    cache = make_qcache(mask, batch, n_kv * 2, n_sink, window, total, bits)
+    gen = torch.Generator(device=DEV).manual_seed(41 + bits + window)
+    k = random_bf16((batch, n_kv, total, 128), gen, scale=2.0)
+    v = random_bf16((batch, n_kv, total, 128), gen)
+    case("quant chunked appends", bits, n_sink, window)
+    dac.leank_pack_k(cache, k[:, :, :t0].contiguous(), v[:, :, :t0].contiguous())
+    kh, vh = bf16_bits(k), bf16_bits(v)
+    pos = t0
+    for n in chunks:
+        dac.leank_pack_k(cache, k[:, :, pos:pos + n].contiguous(), v[:, :, pos:pos + n].contiguous(),
+                         pos0=pos)
+        pos += n
+        torch.cuda.synchronize()
+        assert_quant_cache_matches(cache, kh[:, :, :pos], vh[:, :, :pos], mask)
+
+
+def _ragged_qcache(bits, lens, n_sink, window, max_ctx, seed, counts=(32, 0, 64, 8), group=2):
+    """A low-bit cache whose rows hold lens[b] tokens, built with ragged
+    appends from empty in two rounds; returns the cache, the mask and the
+    full per-row token streams."""
+    batch = len(lens)
+    mask = mask_with_counts(np.random.default_rng(seed), list(counts))
+    n_kv = mask.shape[0]
+    cache = make_qcache(mask, batch, n_kv * group, n_sink, window, max_ctx, bits)
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    width = max(lens) + 2
+    k = random_bf16((batch, n_kv, width, 128), gen, scale=2.0)
+    v = random_bf16((batch, n_kv, width, 128), gen)
+    first = [min(n, 70 + 13 * b) for b, n in enumerate(lens)]
+    for start, cnt in ((np.zeros(batch, np.int64), first),
+                       (np.array(first, np.int64), [n - f for n, f in zip(lens, first)])):
+        n_new = max(max(cnt), 1)
+        kk = torch.zeros((batch, n_kv, n_new, 128), dtype=torch.bfloat16, device=DEV)
+        vv = torch.zeros_like(kk)
+        for b in range(batch):
+            kk[b, :, :cnt[b]] = k[b, :, start[b]:start[b] + cnt[b]]
+            vv[b, :, :cnt[b]] = v[b, :, start[b]:start[b] + cnt[b]]
+        dac.leank_pack_k_rows(cache, kk, vv, torch.from_numpy(start).to(DEV),
+                              torch.tensor(cnt, dtype=torch.int32, device=DEV))
+    return cache, mask, k, v
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("n_sink,window", [(4, 16), (0, 8), (5, 0)])
+def test_ragged_appends_match_bulk(bits, n_sink, window):
+    """leank_pack_k_rows on a low-bit cache: each row holds what the bulk
+    packing of its own tokens gives."""
+    lens = [0, 1, n_sink + window + 63, n_sink + window + 64, 300]
+    case("quant ragged appends", bits, n_sink, window)
+    cache, mask, k, v = _ragged_qcache(bits, lens, n_sink, window, 320, 53 + bits + window)
+    torch.cuda.synchronize()
+    kh, vh = bf16_bits(k), bf16_bits(v)
+    for b, n in enumerate(lens):
+        if n:
+            assert_quant_cache_matches(cache, kh[b:b + 1, :, :n], vh[b:b + 1, :, :n], mask, rows=[b])
 
 
 # ---------------------------------------------------------------- attention over low-bit streams
@@ -194,23 +246,71 @@ def test_step_on_quant_cache(bits, n_sink, window):
         assert_close(outs[s].cpu().numpy(), ref, f"step {s}")
 
 
-def test_ragged_calls_rejected_on_quant_cache():
-    mask = mask_with_counts(np.random.default_rng(4), [32, 0])
-    cache = make_qcache(mask, 2, 4, 4, 8, 100, 8)
-    gen = torch.Generator(device=DEV).manual_seed(4)
-    k = random_bf16((2, 2, 30, 128), gen)
-    q = random_bf16((2, 4, 128), gen)
-    case("quant ragged rejections")
-    dac.leank_pack_k(cache, k, k)
-    with pytest.raises(dac.LeankError) as err:
-        dac.leank_decode_attn_rows(cache, q, torch.full((2,), 30, dtype=torch.int32, device=DEV),
-                                   max_ctx_len=30)
-    assert err.value.status == dac._lib.EUNSUPPORTED
-    with pytest.raises(dac.LeankError) as err:
-        dac.leank_decode_step_rows(cache, q, k[:, :, 0].contiguous(), k[:, :, 0].contiguous(),
-                                   torch.full((2,), 30, dtype=torch.int64, device=DEV),
-                                   max_ctx_len=31)
-    assert err.value.status == dac._lib.EUNSUPPORTED
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("group", [1, 4])
+def test_ragged_decode_on_quant_cache(bits, group):
+    """leank_decode_attn_rows: each row attends over its own length."""
+    n_sink, window = 4, 16
+    lens = [1, 20, 20 + 64, 20 + 64 + 37, 20 + 5 * 64 + 1]
+    case("quant ragged decode", bits, group)
+    cache, mask, k, v = _ragged_qcache(bits, lens, n_sink, window, 420, 61 + bits, group=group)
+    n_kv = mask.shape[0]
+    gen = torch.Generator(device=DEV).manual_seed(67 + bits)
+    q = random_bf16((len(lens), n_kv * group, 128), gen)
+    out = dac.leank_decode_attn_rows(cache, q, torch.tensor(lens, dtype=torch.int32, device=DEV),
+                                     max_ctx_len=max(lens))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b, n in enumerate(lens):
+        ref = _oracle_q(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], mask, n_sink, window, bits)
+        assert_close(got[b:b + 1], ref, f"ragged decode bits {bits} G {group} row {b}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_ragged_step_on_quant_cache(bits):
+    """leank_decode_step_rows: row b appends at row_pos[b] and attends over
+    row_pos[b] + 1 tokens; rows whose position is out of range are left as
+    they were and get zeros.  Rows cross group completions at different
+    steps."""
+    n_sink, window, group = 4, 16, 2
+    lens = [1, 40, 83, 84, 150, 7]
+    max_ctx_len = 160
+    case("quant ragged step", bits)
+    cache, mask, k, v = _ragged_qcache(bits, lens, n_sink, window, 200, 71 + bits, group=group)
+    n_kv = mask.shape[0]
+    kh, vh = bf16_bits(k), bf16_bits(v)
+    gen = torch.Generator(device=DEV).manual_seed(73 + bits)
+    steps = 70
+    extra_k = random_bf16((steps, len(lens), n_kv, 128), gen, scale=2.0)
+    extra_v = random_bf16((steps, len(lens), n_kv, 128), gen)
+    pos = list(lens)
+    pos[5] = -1  # a row that takes no part
+    hist_k = [kh[b, :, :n] for b, n in enumerate(lens)]
+    hist_v = [vh[b, :, :n] for b, n in enumerate(lens)]
+    for s in range(steps):
+        q = random_bf16((len(lens), n_kv * group, 128), gen)
+        out = dac.leank_decode_step_rows(cache, q, extra_k[s], extra_v[s],
+                                         torch.tensor(pos, dtype=torch.int64, device=DEV),
+                                         max_ctx_len=max_ctx_len)
+        for b in range(len(lens)):
+            if 0 <= pos[b] < max_ctx_len:
+                hist_k[b] = np.concatenate([hist_k[b], bf16_bits(extra_k[s][b])[:, None]], axis=1)
+                hist_v[b] = np.concatenate([hist_v[b], bf16_bits(extra_v[s][b])[:, None]], axis=1)
+        if s in (0, 1, 43, 44, steps - 1):
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            for b in range(len(lens)):
+                if not 0 <= pos[b] < max_ctx_len:
+                    assert not got[b].any(), (s, b)
+                    assert_quant_cache_matches(cache, hist_k[b][None], hist_v[b][None], mask, rows=[b])
+                    continue
+                ref = oracle.decode_q(bf16_bits(q[b:b + 1]), hist_k[b][None], hist_v[b][None], mask,
+                                      n_sink, window, bits)
+                assert_close(got[b:b + 1], ref, f"ragged step bits {bits} step {s} row {b}")
+                assert_quant_cache_matches(cache, hist_k[b][None], hist_v[b][None], mask, rows=[b])
+        for b in range(len(lens)):
+            if 0 <= pos[b] < max_ctx_len:
+                pos[b] += 1
 
 
 @pytest.mark.parametrize("bits", [4, 8])
