@@ -43,6 +43,7 @@ __all__ = [
     "leank_plan_layer",
     "leank_plan_layer_q",
     "leank_plan_layer_paged",
+    "leank_plan_layer_paged_q",
     "leank_pack_k",
     "leank_workspace_bytes",
     "leank_workspace_init",
@@ -115,6 +116,21 @@ def leank_plan_layer_paged(kept_count, batch, n_q_heads, n_kv_heads, head_dim, n
     return desc
 
 
+def leank_plan_layer_paged_q(kept_count, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window,
+                             max_ctx, n_pages, quant_bits):
+    """Host plan with a low-bit middle in pages of 64 rows (one K group each)."""
+    counts = [int(c) for c in kept_count]
+    if len(counts) != n_kv_heads:
+        raise ValueError("kept_count must hold one count per KV head")
+    arr = (ctypes.c_int32 * max(1, len(counts)))(*counts)
+    desc = LayerCacheDesc()
+    check(lib().leank_plan_layer_paged_q(arr, batch, n_q_heads, n_kv_heads, head_dim, n_sink,
+                                         window, int(max_ctx), int(n_pages), int(quant_bits),
+                                         ctypes.byref(desc)),
+          "leank_plan_layer_paged_q")
+    return desc
+
+
 def leank_plan_layer_q(kept_count, batch, n_q_heads, n_kv_heads, head_dim, n_sink, window,
                        max_ctx, quant_bits):
     """Host plan with low-bit middle streams (quant_bits 4 or 8; 0 = bf16)."""
@@ -150,11 +166,9 @@ class LayerCache:
         block_table (int32 [batch, pages_per_row] on the device; default:
         batch row b's pages contiguous from page b * pages_per_row)."""
         device = _normalize_device(device if device is not None else kept_idx.device)
-        if n_pages and quant_bits:
-            raise ValueError("low-bit middle streams are not paged")
         if n_pages:
-            self.desc = leank_plan_layer_paged(kept_count, batch, n_q_heads, n_kv_heads, head_dim,
-                                               n_sink, window, max_ctx, n_pages)
+            self.desc = leank_plan_layer_paged_q(kept_count, batch, n_q_heads, n_kv_heads, head_dim,
+                                                 n_sink, window, max_ctx, n_pages, quant_bits)
         else:
             self.desc = leank_plan_layer_q(kept_count, batch, n_q_heads, n_kv_heads, head_dim,
                                            n_sink, window, max_ctx, quant_bits)

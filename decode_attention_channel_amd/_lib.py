@@ -106,6 +106,11 @@ _SIGNATURES = {
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                               ctypes.c_int64, ctypes.POINTER(LayerCacheDesc)]),
+    "leank_plan_layer_paged_q": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                                ctypes.c_int64, ctypes.c_int32,
+                                                ctypes.POINTER(LayerCacheDesc)]),
     "leank_pack_k": (ctypes.c_int, [ctypes.POINTER(LayerCacheDesc), ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_void_p]),

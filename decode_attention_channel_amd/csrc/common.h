@@ -58,6 +58,30 @@ struct WorkPlan {
 };
 
 int validate_cache(const leank_layer_cache* c, bool need_buffers);
+
+// In-page layout of a paged low-bit middle: a page holds one 64-row K group
+// of every live head -- the K codes of the live heads in group order, then
+// their K (scale, min) pairs, then their V code blocks, then their V row
+// parameters.  A head at kept-channel prefix P and live rank R starts its K
+// codes at byte 64 P bits / 8, its K pairs at kc_bytes + 8 P, its V codes at
+// kc_bytes + kp_bytes + R vc_head and its V parameters at kc_bytes +
+// kp_bytes + n_live vc_head + R vp_head.
+struct QPageLayout {
+  int64_t kc_bytes;  // K codes of all live heads
+  int64_t kp_bytes;  // their K pairs
+  int64_t vc_head;   // V codes of one head: 8 blocks
+  int64_t vp_head;   // V parameters of one head: 64 (scale, min) pairs
+  int64_t page_bytes;
+};
+inline QPageLayout q_page_layout(int64_t kept_sum, int64_t n_live, int bits) {
+  QPageLayout l;
+  l.kc_bytes = LEANK_PAGE_ROWS * kept_sum * bits / 8;
+  l.kp_bytes = 8 * kept_sum;
+  l.vc_head = static_cast<int64_t>(LEANK_PAGE_ROWS) * LEANK_HEAD_DIM * bits / 8;
+  l.vp_head = 8 * LEANK_PAGE_ROWS;
+  l.page_bytes = l.kc_bytes + l.kp_bytes + n_live * (l.vc_head + l.vp_head);
+  return l;
+}
 // HBM bytes one middle row of a live head with `kept` channels streams
 // (bf16 or low-bit layout, K group parameters not counted).
 int64_t middle_row_bytes(const leank_layer_cache* c, int kept);

@@ -32,16 +32,18 @@ bool canonical_quant_layout(const leank_layer_cache* c, int64_t* c_prefix, int64
   const int64_t batch = c->batch, bits = c->quant_bits;
   const int64_t groups = (c->mid_capacity + LEANK_QUANT_GROUP - 1) / LEANK_QUANT_GROUP;
   const int64_t g_rows = groups * LEANK_QUANT_GROUP;
+  const bool paged = c->page_rows != 0;  // in-page offsets, checked by validate_cache
   int64_t pre = 0, n = 0;
   for (int i = 0; i < c->n_kv_heads; ++i) {
     const int h = c->group_order[i];
     const int64_t kept = c->kept_count[h];
     if (h < 0 || h >= c->n_kv_heads) return false;
     if (kept <= 0) continue;
-    if (c->k_q_off[h] != batch * g_rows * pre * bits / 8 || c->k_qp_off[h] != batch * groups * pre * 2 ||
-        c->k_stage_off[h] != batch * LEANK_QUANT_GROUP * pre ||
-        c->v_q_off[h] != n * batch * v_rows(c->mid_capacity) * LEANK_HEAD_DIM * bits / 8 ||
-        c->v_qp_off[h] != n * batch * c->mid_capacity * 2)
+    if (!paged &&
+        (c->k_q_off[h] != batch * g_rows * pre * bits / 8 || c->k_qp_off[h] != batch * groups * pre * 2 ||
+         c->k_stage_off[h] != batch * LEANK_QUANT_GROUP * pre ||
+         c->v_q_off[h] != n * batch * v_rows(c->mid_capacity) * LEANK_HEAD_DIM * bits / 8 ||
+         c->v_qp_off[h] != n * batch * c->mid_capacity * 2))
       return false;
     c_prefix[h] = pre;
     rank[h] = n;
@@ -200,6 +202,12 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
     p.heads[h].n_mid = w.n_mid[h];
     p.heads[h].mid_rows = w.mid_rows[h];
     p.heads[h].base = w.head_base[h];
+    if (quant && p.paged && c->kept_count[h] > 0) {
+      p.heads[h].pq_k_codes = static_cast<int32_t>(c->k_q_off[h]);
+      p.heads[h].pq_k_par = static_cast<int32_t>(4 * c->k_qp_off[h]);
+      p.heads[h].pq_v_codes = static_cast<int32_t>(c->v_q_off[h]);
+      p.heads[h].pq_v_par = static_cast<int32_t>(4 * c->v_qp_off[h]);
+    }
   }
   const int64_t n_pairs = static_cast<int64_t>(c->batch) * c->n_kv_heads;
   const int qb = c->quant_bits;

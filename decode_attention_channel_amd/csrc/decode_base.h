@@ -36,6 +36,9 @@ struct DecodeHead {
   int32_t n_mid;     // middle items of this head per batch row
   int32_t mid_rows;  // rows per middle item
   int32_t base;      // first item of this head within a batch row
+  // paged low-bit middle: byte offsets of the head's K codes, K pairs, V
+  // codes and V parameters within a page
+  int32_t pq_k_codes, pq_k_par, pq_v_codes, pq_v_par;
 };
 
 struct DecodeParams {

@@ -241,9 +241,11 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
         if constexpr (QB != 0) {
           // the middle row's V code block (QB * 128 bytes)
           const QSegment qs = q_segment<QB>(p, hd, b, 0);
+          const QGroup at = q_group<QB>(qs, hd.kept, tok.mid_row / LEANK_QUANT_GROUP);
           constexpr int kBlkBytes = LEANK_HEAD_DIM * LEANK_V_BLOCK * QB / 8;
           if (c * 16 < kBlkBytes)
-            x = *reinterpret_cast<const u32x4_t*>(qs.v_codes + static_cast<int64_t>(tok.mid_row / LEANK_V_BLOCK) * kBlkBytes + c * 16);
+            x = *reinterpret_cast<const u32x4_t*>(
+                at.v_codes + ((tok.mid_row % LEANK_QUANT_GROUP) / LEANK_V_BLOCK) * kBlkBytes + c * 16);
         } else {
           const uint16_t *k_row, *blk;
           middle_row_at(p, hd, b, tok.mid_row, &k_row, &blk);
@@ -460,13 +462,13 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
                                       static_cast<int64_t>(r % LEANK_QUANT_GROUP) * hd.kept)[lane] =
               compact_from_lds(s_tok_k[which], s_idx, hd.kept, lane);
         constexpr int kBlkBytes = LEANK_HEAD_DIM * LEANK_V_BLOCK * QB / 8;
+        const QGroup at = q_group<QB>(qs, hd.kept, r / LEANK_QUANT_GROUP);
+        const int r_in = r % LEANK_QUANT_GROUP;
         if (lane < kBlkBytes / 16)
-          reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(qs.v_codes) +
-                                     static_cast<int64_t>(r / LEANK_V_BLOCK) * kBlkBytes)[lane] =
+          reinterpret_cast<u32x4_t*>(const_cast<uint8_t*>(at.v_codes) + (r_in / LEANK_V_BLOCK) * kBlkBytes)[lane] =
               reinterpret_cast<const u32x4_t*>(s_vblk[1])[lane];
         if (lane == 0)
-          *reinterpret_cast<float2*>(const_cast<float*>(qs.v_par) + static_cast<int64_t>(r) * 2) =
-              make_float2(s_vpar[0], s_vpar[1]);
+          *reinterpret_cast<float2*>(const_cast<float*>(at.v_par) + r_in * 2) = make_float2(s_vpar[0], s_vpar[1]);
       }
     } else if (tok.mid_row >= 0) {
       // middle row: kept K channels (compacted) and V

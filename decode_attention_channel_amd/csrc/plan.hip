@@ -80,24 +80,35 @@ int validate_cache(const leank_layer_cache* c, bool need_buffers) {
   if (quant && c->quant_group != LEANK_QUANT_GROUP) return LEANK_EINVAL;
   const bool paged = c->page_rows != 0;
   if (paged) {
-    // canonical page layout: K of the live heads in group order, then their V blocks
-    if (quant || c->page_rows != LEANK_PAGE_ROWS || c->n_pages < 1) return LEANK_EINVAL;
+    // canonical page layouts: bf16, K of the live heads in group order, then
+    // their V blocks; low-bit, as QPageLayout describes (staging not paged)
+    if (c->page_rows != LEANK_PAGE_ROWS || c->n_pages < 1) return LEANK_EINVAL;
     if (c->pages_per_row != (c->mid_capacity + LEANK_PAGE_ROWS - 1) / LEANK_PAGE_ROWS) return LEANK_EINVAL;
     int64_t kept_sum = 0, n_live = 0;
     for (int h = 0; h < c->n_kv_heads; ++h)
       if (c->kept_count[h] > 0) kept_sum += c->kept_count[h], ++n_live;
+    const QPageLayout ql = q_page_layout(kept_sum, n_live, quant ? c->quant_bits : 8);
     int64_t k_pre = 0, rank = 0;
     for (int i = 0; i < c->n_kv_heads; ++i) {
       const int h = c->group_order[i];
       if (h < 0 || h >= c->n_kv_heads) return LEANK_EINVAL;
       if (c->kept_count[h] <= 0) continue;
-      if (c->k_prun_off[h] != LEANK_PAGE_ROWS * k_pre ||
-          c->v_mid_off[h] != LEANK_PAGE_ROWS * (kept_sum + rank * LEANK_HEAD_DIM))
+      if (!quant) {
+        if (c->k_prun_off[h] != LEANK_PAGE_ROWS * k_pre ||
+            c->v_mid_off[h] != LEANK_PAGE_ROWS * (kept_sum + rank * LEANK_HEAD_DIM))
+          return LEANK_EINVAL;
+      } else if (c->k_q_off[h] != LEANK_PAGE_ROWS * k_pre * c->quant_bits / 8 ||
+                 c->k_qp_off[h] != (ql.kc_bytes + 8 * k_pre) / 4 ||
+                 c->v_q_off[h] != ql.kc_bytes + ql.kp_bytes + rank * ql.vc_head ||
+                 c->v_qp_off[h] != (ql.kc_bytes + ql.kp_bytes + n_live * ql.vc_head + rank * ql.vp_head) / 4 ||
+                 c->k_stage_off[h] != static_cast<int64_t>(c->batch) * LEANK_QUANT_GROUP * k_pre) {
         return LEANK_EINVAL;
+      }
       k_pre += c->kept_count[h];
       ++rank;
     }
-    const int64_t page_bytes = LEANK_PAGE_ROWS * (2 * kept_sum + 2 * LEANK_HEAD_DIM * n_live);
+    const int64_t page_bytes =
+        quant ? ql.page_bytes : LEANK_PAGE_ROWS * (2 * kept_sum + 2 * LEANK_HEAD_DIM * n_live);
     if (static_cast<int64_t>(c->page_bytes) != page_bytes ||
         c->pool_bytes != c->page_bytes * static_cast<uint64_t>(c->n_pages))
       return LEANK_EINVAL;
@@ -133,6 +144,7 @@ int validate_cache(const leank_layer_cache* c, bool need_buffers) {
     if (paged) {
       if (c->pool_bytes && (!c->pool || !aligned16(c->pool))) return LEANK_EINVAL;
       if (c->pages_per_row > 0 && !c->block_table) return LEANK_EINVAL;
+      if (quant && c->k_stage_bytes && (!c->k_stage || !aligned16(c->k_stage))) return LEANK_EINVAL;
     } else if (!quant) {
       if (c->k_prun_bytes && (!c->k_prun || !aligned16(c->k_prun))) return LEANK_EINVAL;
       if (c->v_mid_bytes && (!c->v_mid || !aligned16(c->v_mid))) return LEANK_EINVAL;
@@ -350,6 +362,47 @@ extern "C" int leank_plan_layer_paged(const int32_t* kept_count_host, int32_t ba
   *out = c;
   return LEANK_OK;
 }
+
+extern "C" int leank_plan_layer_paged_q(const int32_t* kept_count_host, int32_t batch,
+                                        int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                        int32_t n_sink, int32_t window, int64_t max_ctx,
+                                        int64_t n_pages, int32_t quant_bits,
+                                        leank_layer_cache* out) {
+  if (quant_bits == 0)
+    return leank_plan_layer_paged(kept_count_host, batch, n_q_heads, n_kv_heads, head_dim, n_sink,
+                                  window, max_ctx, n_pages, out);
+  if (!out || n_pages < 1) return LEANK_EINVAL;
+  leank_layer_cache c;
+  int st = leank_plan_layer_q(kept_count_host, batch, n_q_heads, n_kv_heads, head_dim, n_sink,
+                              window, max_ctx, quant_bits, &c);
+  if (st != LEANK_OK) return st;
+  int64_t kept_sum = 0, n_live = 0;
+  for (int h = 0; h < n_kv_heads; ++h)
+    if (c.kept_count[h] > 0) kept_sum += c.kept_count[h], ++n_live;
+  const QPageLayout ql = q_page_layout(kept_sum, n_live, quant_bits);
+  int64_t k_pre = 0, rank = 0;
+  for (int i = 0; i < n_kv_heads; ++i) {
+    const int h = c.group_order[i];
+    if (c.kept_count[h] <= 0) continue;
+    c.k_q_off[h] = LEANK_PAGE_ROWS * k_pre * quant_bits / 8;
+    c.k_qp_off[h] = (ql.kc_bytes + 8 * k_pre) / 4;
+    c.v_q_off[h] = ql.kc_bytes + ql.kp_bytes + rank * ql.vc_head;
+    c.v_qp_off[h] = (ql.kc_bytes + ql.kp_bytes + n_live * ql.vc_head + rank * ql.vp_head) / 4;
+    k_pre += c.kept_count[h];
+    ++rank;
+  }
+  c.k_q_bytes = c.k_qp_bytes = c.v_q_bytes = c.v_qp_bytes = 0;  // the middle lives in pages
+  c.page_rows = LEANK_PAGE_ROWS;
+  c.pages_per_row = static_cast<int32_t>((c.mid_capacity + LEANK_PAGE_ROWS - 1) / LEANK_PAGE_ROWS);
+  c.n_pages = n_pages;
+  c.page_bytes = static_cast<uint64_t>(ql.page_bytes);
+  c.pool_bytes = c.page_bytes * static_cast<uint64_t>(n_pages);
+  st = validate_cache(&c, false);
+  if (st != LEANK_OK) return st;
+  *out = c;
+  return LEANK_OK;
+}
+
 
 extern "C" int leank_workspace_bytes(const leank_layer_cache* cache, int64_t ctx_len,
                                      size_t* bytes_out) {

@@ -40,6 +40,14 @@ struct QuantParams {
   const int64_t* row_pos;
   const int32_t* row_count;
   int64_t pos_end;
+  // paged middle (one K group per page): group g of batch row b lives in
+  // page block_table[b * pages_per_row + g] of the pool, and the head
+  // offsets above are offsets within a page
+  uint8_t* pool;
+  const int32_t* block_table;
+  int64_t page_bytes;
+  int32_t pages_per_row;
+  int32_t paged;
   int32_t n_kv;
   int32_t n_sink;
   int32_t window;
@@ -48,6 +56,39 @@ struct QuantParams {
   int32_t pad;
   QuantHead heads[LEANK_MAX_KV_HEADS];
 };
+
+// Where group g (64 middle rows) of batch row b and live head hd lives: its
+// K codes, K (scale, min) pairs, first V code block and first V row
+// parameters.
+struct QGroupAt {
+  uint8_t* k_codes;
+  float* k_par;
+  uint8_t* v_codes;
+  float* v_par;
+};
+
+__device__ __forceinline__ QGroupAt q_group_at(const QuantParams& p, const QuantHead& hd, int b,
+                                               int64_t g) {
+  QGroupAt a;
+  const int64_t c = hd.kept;
+  if (p.paged) {
+    uint8_t* base = p.pool + static_cast<int64_t>(p.block_table[static_cast<int64_t>(b) * p.pages_per_row + g]) *
+                                 p.page_bytes;
+    a.k_codes = base + hd.k_q_off;
+    a.k_par = reinterpret_cast<float*>(base) + hd.k_qp_off;
+    a.v_codes = base + hd.v_q_off;
+    a.v_par = reinterpret_cast<float*>(base) + hd.v_qp_off;
+  } else {
+    const int64_t blk_bytes = LEANK_HEAD_DIM * LEANK_V_BLOCK * p.bits / 8;
+    a.k_codes = p.k_q + hd.k_q_off + (static_cast<int64_t>(b) * p.g_rows + g * LEANK_QUANT_GROUP) * c * p.bits / 8;
+    a.k_par = p.k_qp + hd.k_qp_off + (static_cast<int64_t>(b) * (p.g_rows / LEANK_QUANT_GROUP) + g) * c * 2;
+    a.v_codes = p.v_q + hd.v_q_off +
+                (static_cast<int64_t>(b) * (p.v_rows_cap / LEANK_V_BLOCK) + g * (LEANK_QUANT_GROUP / LEANK_V_BLOCK)) *
+                    blk_bytes;
+    a.v_par = p.v_qp + hd.v_qp_off + (static_cast<int64_t>(b) * p.mid_cap + g * LEANK_QUANT_GROUP) * 2;
+  }
+  return a;
+}
 
 // ---------------------------------------------------------------- the code decision
 //

@@ -56,11 +56,8 @@ __global__ __launch_bounds__(kQThreads) void quant_k_bulk_kernel(const QuantPara
     s_x[i] = bf16_to_f32(src[static_cast<int64_t>(r) * LEANK_HEAD_DIM + s_idx[j]]);
   }
   __syncthreads();
-  uint8_t* codes = p.k_q + hd.k_q_off +
-                   ((static_cast<int64_t>(b) * p.g_rows + r0) * c) * p.bits / 8;
-  float* params = p.k_qp + hd.k_qp_off +
-                  ((static_cast<int64_t>(b) * (p.g_rows / LEANK_QUANT_GROUP) + g) * c) * 2;
-  quantize_k_group(s_x, c, p.bits, s_scale, s_lo, codes, params);
+  const QGroupAt at = q_group_at(p, hd, b, g);
+  quantize_k_group(s_x, c, p.bits, s_scale, s_lo, at.k_codes, at.k_par);
 }
 
 // Grid: batch x n_kv x ceil(t_mid / 8).  One 8-row V block per workgroup:
@@ -86,7 +83,7 @@ __global__ __launch_bounds__(kQThreads) void quant_v_bulk_kernel(const QuantPara
         p.v_src + (pair * p.n_src + p.n_sink + r) * LEANK_HEAD_DIM)[lane];
     uint32_t c0, c1;
     quantize_v_row(bf16_lo(w), bf16_hi(w), p.bits,
-                   p.v_qp + hd.v_qp_off + (static_cast<int64_t>(b) * p.mid_cap + r) * 2, &c0, &c1);
+                   q_group_at(p, hd, b, r / LEANK_QUANT_GROUP).v_par + (r % LEANK_QUANT_GROUP) * 2, &c0, &c1);
     if (p.bits == 8) {
       s_blk[v_code_byte(2 * lane, e, 8)] = static_cast<uint8_t>(c0);
       s_blk[v_code_byte(2 * lane + 1, e, 8)] = static_cast<uint8_t>(c1);
@@ -100,8 +97,8 @@ __global__ __launch_bounds__(kQThreads) void quant_v_bulk_kernel(const QuantPara
     }
   }
   __syncthreads();
-  uint8_t* dst = p.v_q + hd.v_q_off +
-                 (static_cast<int64_t>(b) * (p.v_rows_cap / LEANK_V_BLOCK) + blk) * blk_bytes;
+  constexpr int kBlocksPerGroup = LEANK_QUANT_GROUP / LEANK_V_BLOCK;
+  uint8_t* dst = q_group_at(p, hd, b, blk / kBlocksPerGroup).v_codes + (blk % kBlocksPerGroup) * blk_bytes;
   for (int i = t; i < blk_bytes / 16; i += kQThreads)
     reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(s_blk)[i];
 }
@@ -163,8 +160,8 @@ __global__ __launch_bounds__(kQThreads) void quant_append_kernel(const QuantPara
     const int blk_bytes = LEANK_HEAD_DIM * LEANK_V_BLOCK * p.bits / 8;
     uint8_t* vblk = nullptr;
     if (r >= 0) {
-      vblk = p.v_q + hd.v_q_off +
-             (static_cast<int64_t>(b) * (p.v_rows_cap / LEANK_V_BLOCK) + r / LEANK_V_BLOCK) * blk_bytes;
+      vblk = q_group_at(p, hd, b, r / LEANK_QUANT_GROUP).v_codes +
+             ((r % LEANK_QUANT_GROUP) / LEANK_V_BLOCK) * blk_bytes;
       for (int i = t; i < blk_bytes / 16; i += kQThreads)
         reinterpret_cast<uint4*>(s_blk)[i] = reinterpret_cast<const uint4*>(vblk)[i];
     }
@@ -185,7 +182,7 @@ __global__ __launch_bounds__(kQThreads) void quant_append_kernel(const QuantPara
       const uint32_t w = reinterpret_cast<const uint32_t*>(s_tok[1])[lane];
       uint32_t c0, c1;
       quantize_v_row(bf16_lo(w), bf16_hi(w), p.bits,
-                     p.v_qp + hd.v_qp_off + (static_cast<int64_t>(b) * p.mid_cap + r) * 2, &c0, &c1);
+                     q_group_at(p, hd, b, r / LEANK_QUANT_GROUP).v_par + (r % LEANK_QUANT_GROUP) * 2, &c0, &c1);
   #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int ch = 2 * lane + u;
@@ -216,12 +213,8 @@ __global__ __launch_bounds__(kQThreads) void quant_append_kernel(const QuantPara
       s_x[i] = bf16_to_f32(row == LEANK_QUANT_GROUP - 1 ? s_tok[0][s_idx[j]] : stage[i]);
     }
     __syncthreads();
-    const int64_t g = r / LEANK_QUANT_GROUP;
-    uint8_t* codes = p.k_q + hd.k_q_off +
-                     ((static_cast<int64_t>(b) * p.g_rows + g * LEANK_QUANT_GROUP) * c) * p.bits / 8;
-    float* params = p.k_qp + hd.k_qp_off +
-                    ((static_cast<int64_t>(b) * (p.g_rows / LEANK_QUANT_GROUP) + g) * c) * 2;
-    quantize_k_group(s_x, c, p.bits, s_scale, s_lo, codes, params);
+    const QGroupAt at = q_group_at(p, hd, b, r / LEANK_QUANT_GROUP);
+    quantize_k_group(s_x, c, p.bits, s_scale, s_lo, at.k_codes, at.k_par);
   }
 }
 
@@ -246,6 +239,11 @@ void fill_quant_params(const leank_layer_cache* c, QuantParams* p) {
   p->window = c->window;
   p->slots = c->n_sink + c->window;
   p->bits = c->quant_bits;
+  p->paged = c->page_rows != 0;
+  p->pool = static_cast<uint8_t*>(c->pool);
+  p->block_table = c->block_table;
+  p->page_bytes = static_cast<int64_t>(c->page_bytes);
+  p->pages_per_row = c->pages_per_row;
   for (int h = 0; h < c->n_kv_heads; ++h) {
     p->heads[h].kept = c->kept_count[h];
     p->heads[h].k_q_off = c->k_q_off[h];

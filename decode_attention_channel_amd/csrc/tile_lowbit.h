@@ -25,13 +25,18 @@ namespace leank {
 //      added to every channel of the head at the end (min' = min, or
 //      min - 128 * scale for 4-bit codes).
 
-// Pointers of one (batch row, live head) pair's low-bit middle.
+// Pointers of one (batch row, live head) pair's low-bit middle: contiguous
+// streams, or one page per 64-row group through the block table.
 struct QSegment {
-  const uint8_t* k_codes;  // row 0 of the pair's K codes
+  const uint8_t* k_codes;  // row 0 of the pair's K codes (contiguous)
   const float* k_par;      // group 0 of the pair's (scale, min) pairs
   const uint16_t* k_stage; // the pair's staging rows
   const uint8_t* v_codes;  // block 0 of the pair's V codes
   const float* v_par;      // row 0 of the pair's (scale, min) pairs
+  const uint8_t* pool;     // paged: the page pool, or null
+  const int32_t* pages;    // paged: the row's block table entries
+  int64_t page_bytes;
+  int32_t pk_codes, pk_par, pv_codes, pv_par;  // paged: byte offsets within a page
   int full_rows;           // rows in complete groups for this call
 };
 
@@ -43,15 +48,59 @@ __device__ __forceinline__ QSegment q_segment(const DecodeParams& p, const Decod
   const int64_t g_rows = p.q_groups * LEANK_QUANT_GROUP;
   const int64_t v_blocks = p.v_mid_rows / LEANK_V_BLOCK;
   QSegment q;
-  q.k_codes = p.k_q + (batch_rows * g_rows * hd.k_off + static_cast<int64_t>(b) * g_rows * c) * QB / 8;
-  q.k_par = p.k_qp + (batch_rows * p.q_groups * hd.k_off + static_cast<int64_t>(b) * p.q_groups * c) * 2;
   q.k_stage = p.k_stage + batch_rows * LEANK_QUANT_GROUP * hd.k_off +
               static_cast<int64_t>(b) * LEANK_QUANT_GROUP * c;
+  q.full_rows = t_mid / LEANK_QUANT_GROUP * LEANK_QUANT_GROUP;
+  if (p.paged) {
+    q.pool = reinterpret_cast<const uint8_t*>(p.pool);
+    q.pages = p.block_table + static_cast<int64_t>(b) * p.pages_per_row;
+    q.page_bytes = 2 * p.page_elems;
+    q.pk_codes = hd.pq_k_codes;
+    q.pk_par = hd.pq_k_par;
+    q.pv_codes = hd.pq_v_codes;
+    q.pv_par = hd.pq_v_par;
+    q.k_codes = nullptr;
+    q.k_par = nullptr;
+    q.v_codes = nullptr;
+    q.v_par = nullptr;
+    return q;
+  }
+  q.pool = nullptr;
+  q.k_codes = p.k_q + (batch_rows * g_rows * hd.k_off + static_cast<int64_t>(b) * g_rows * c) * QB / 8;
+  q.k_par = p.k_qp + (batch_rows * p.q_groups * hd.k_off + static_cast<int64_t>(b) * p.q_groups * c) * 2;
   q.v_codes = p.v_q + (hd.v_off * batch_rows * v_blocks + static_cast<int64_t>(b) * v_blocks) *
                           (LEANK_HEAD_DIM * LEANK_V_BLOCK * QB / 8);
   q.v_par = p.v_qp + (hd.v_off * batch_rows * p.mid_cap + static_cast<int64_t>(b) * p.mid_cap) * 2;
-  q.full_rows = t_mid / LEANK_QUANT_GROUP * LEANK_QUANT_GROUP;
   return q;
+}
+
+// Where group g (rows 64 g ..) of a pair lives: its K codes (row 0 of the
+// group), K (scale, min) pairs, first V code block and first V row
+// parameters.
+struct QGroup {
+  const uint8_t* k_codes;
+  const float* k_par;
+  const uint8_t* v_codes;
+  const float* v_par;
+};
+
+template <int QB>
+__device__ __forceinline__ QGroup q_group(const QSegment& q, int c, int g) {
+  QGroup a;
+  if (q.pool) {
+    const uint8_t* base = q.pool + static_cast<int64_t>(q.pages[g]) * q.page_bytes;
+    a.k_codes = base + q.pk_codes;
+    a.k_par = reinterpret_cast<const float*>(base + q.pk_par);
+    a.v_codes = base + q.pv_codes;
+    a.v_par = reinterpret_cast<const float*>(base + q.pv_par);
+  } else {
+    a.k_codes = q.k_codes + static_cast<int64_t>(g) * LEANK_QUANT_GROUP * c * QB / 8;
+    a.k_par = q.k_par + static_cast<int64_t>(g) * c * 2;
+    a.v_codes = q.v_codes + static_cast<int64_t>(g) * (LEANK_QUANT_GROUP / LEANK_V_BLOCK) *
+                                (LEANK_HEAD_DIM * LEANK_V_BLOCK * QB / 8);
+    a.v_par = q.v_par + static_cast<int64_t>(g) * LEANK_QUANT_GROUP * 2;
+  }
+  return a;
 }
 
 // Raw operands of one tile of the open K group (the group that is not
@@ -83,8 +132,9 @@ __device__ __forceinline__ void load_tile_q(const QSegment& q, int c, int t0, in
     }
   }
   const bool v_ok = 8 * grp < nvalid;
-  const uint8_t* vt = q.v_codes + (static_cast<int64_t>(t0 / 8 + grp) * LEANK_HEAD_DIM + col) *
-                                      (LEANK_V_BLOCK * QB / 8);
+  const QGroup at = q_group<QB>(q, c, t0 / LEANK_QUANT_GROUP);
+  const int t_in = t0 % LEANK_QUANT_GROUP;  // tiles never straddle a group
+  const uint8_t* vt = at.v_codes + ((t_in / 8 + grp) * LEANK_HEAD_DIM + col) * (LEANK_V_BLOCK * QB / 8);
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const uint8_t* src = vt + n * 16 * (LEANK_V_BLOCK * QB / 8);
@@ -99,7 +149,7 @@ __device__ __forceinline__ void load_tile_q(const QSegment& q, int c, int t0, in
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const bool ok = 2 * col + j < nvalid;
-    const float2 pr = ok ? *reinterpret_cast<const float2*>(q.v_par + static_cast<int64_t>(t0 + 2 * col + j) * 2)
+    const float2 pr = ok ? *reinterpret_cast<const float2*>(at.v_par + (t_in + 2 * col + j) * 2)
                          : make_float2(0.0f, 0.0f);
     tr.vs[j] = pr.x;
     tr.vm[j] = pr.y;
@@ -203,12 +253,12 @@ __device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, Gro
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
+  const QGroup at = q_group<QB>(q, c, g0 / LEANK_QUANT_GROUP);
   // the group's parameters first: the query tables wait only for them
-  gr.par = 4 * lane < 2 * c
-               ? *reinterpret_cast<const f32x4_t*>(q.k_par + static_cast<int64_t>(g0 / LEANK_QUANT_GROUP) * c * 2 + 4 * lane)
-               : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  gr.par = 4 * lane < 2 * c ? *reinterpret_cast<const f32x4_t*>(at.k_par + 4 * lane)
+                            : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // the row's codes: c * QB / 8 bytes, a multiple of 4 (8-bit: of 8)
-  const uint8_t* krow = q.k_codes + static_cast<int64_t>(g0 + lane) * c * QB / 8;
+  const uint8_t* krow = at.k_codes + lane * c * QB / 8;
   if constexpr (QB == 8) {
 #pragma unroll
     for (int i = 0; i < KB * QB / 2; ++i) {
@@ -223,8 +273,7 @@ __device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, Gro
   }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const uint8_t* vt = q.v_codes + (static_cast<int64_t>((g0 + 32 * half) / 8 + grp) * LEANK_HEAD_DIM + col) *
-                                        (LEANK_V_BLOCK * QB / 8);
+    const uint8_t* vt = at.v_codes + ((4 * half + grp) * LEANK_HEAD_DIM + col) * (LEANK_V_BLOCK * QB / 8);
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const uint8_t* src = vt + n * 16 * (LEANK_V_BLOCK * QB / 8);
@@ -237,7 +286,7 @@ __device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, Gro
       }
     }
   }
-  const float2 pr = *reinterpret_cast<const float2*>(q.v_par + static_cast<int64_t>(g0 + lane) * 2);
+  const float2 pr = *reinterpret_cast<const float2*>(at.v_par + lane * 2);
   gr.vs = pr.x;
   gr.vm = pr.y;
 }

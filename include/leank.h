@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define LEANK_ABI_VERSION 5
+#define LEANK_ABI_VERSION 6
 #define LEANK_HEAD_DIM 128      /* the only head_dim the kernels implement   */
 #define LEANK_MAX_KV_HEADS 64   /* per-layer KV heads a cache plan can hold  */
 #define LEANK_MAX_GROUP 8       /* query heads per KV head the kernels take  */
@@ -168,6 +168,15 @@ int leank_build_mask(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
  * page before rows are appended to it (for one token per step: whenever
  * r % 64 == 0); the kernels read the table on the device and do not check
  * it, so every entry that covers written rows must lie in [0, n_pages).
+ *
+ * Paged low-bit middle (leank_plan_layer_paged_q): a page holds one 64-row
+ * K group of every live head.  Within the page, at byte offsets: the K
+ * codes of the live heads in group order, each [64][kept_count[h]] at
+ * k_q_off[h]; then their K (scale, minimum) pairs, float32
+ * [kept_count[h]][2] at float offset k_qp_off[h]; then their V codes, 8
+ * blocks as in v_q at v_q_off[h]; then their V row parameters, float32
+ * [64][2] at float offset v_qp_off[h].  The staging rows of the open group
+ * stay in k_stage; k_q, k_qp, v_q and v_qp are unused (their sizes are 0).
  */
 typedef struct leank_layer_cache {
   int32_t batch;
@@ -265,12 +274,26 @@ int leank_plan_layer_q(const int32_t* kept_count_host, int32_t batch,
  * through a block table (layout above).  max_ctx bounds every batch row.
  * The caller allocates k_sl, v_sl, the pool (pool_bytes) and the block
  * table (int32 [batch][pages_per_row]).  Every entry point takes such a
- * cache; the low-bit streams are not paged.
+ * cache.
  */
 int leank_plan_layer_paged(const int32_t* kept_count_host, int32_t batch,
                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                            int32_t n_sink, int32_t window, int64_t max_ctx,
                            int64_t n_pages, leank_layer_cache* cache_out);
+
+/*
+ * leank_plan_layer_paged_q -- a cache whose middle is both low-bit
+ * (quant_bits 4 or 8, as leank_plan_layer_q) and paged (as
+ * leank_plan_layer_paged; page layout above).  quant_bits 0 gives
+ * leank_plan_layer_paged.  The caller allocates k_sl, v_sl, k_stage, the
+ * pool and the block table.  Every entry point takes such a cache, with the
+ * low-bit rules of leank_plan_layer_q.
+ */
+int leank_plan_layer_paged_q(const int32_t* kept_count_host, int32_t batch,
+                             int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                             int32_t n_sink, int32_t window, int64_t max_ctx,
+                             int64_t n_pages, int32_t quant_bits,
+                             leank_layer_cache* cache_out);
 
 /*
  * leank_pack_k -- append n_new tokens at positions [pos0, pos0 + n_new)

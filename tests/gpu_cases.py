@@ -142,10 +142,50 @@ def _unpack_nibbles(b):
     return out
 
 
+def _read_paged_q(cache, b, h, t_mid):
+    """read_pair_q for a paged low-bit middle: group g of the row in page
+    block_table[b][g]."""
+    d = cache.desc
+    bits, c = d.quant_bits, d.kept_count[h]
+    pool = cache.pool.view(torch.uint8).cpu().numpy()
+    table = cache.block_table.cpu().numpy()
+    n_full = t_mid // 64
+    n_groups = -(-t_mid // 64)
+    blk_bytes = 128 * 8 * bits // 8
+    k_codes, kpar, v_codes, vpar = [], [], [], []
+    for g in range(n_groups):
+        base = int(table[b, g]) * d.page_bytes
+        page = pool[base: base + d.page_bytes]
+        if g < n_full:
+            raw = page[d.k_q_off[h]: d.k_q_off[h] + 64 * c * bits // 8]
+            k_codes.append((raw if bits == 8 else _unpack_nibbles(raw)).reshape(64, c))
+            kp = page[4 * d.k_qp_off[h]: 4 * d.k_qp_off[h] + 8 * c].view(np.float32)
+            kpar.append(kp.reshape(c, 2))
+        vraw = page[d.v_q_off[h]: d.v_q_off[h] + 8 * blk_bytes]
+        if bits == 8:
+            codes = vraw.reshape(8, 128, 8)
+        else:
+            b4 = vraw.reshape(8, 128, 4)
+            codes = np.concatenate([b4 & 0xF, b4 >> 4], axis=2)
+        v_codes.append(codes.transpose(0, 2, 1).reshape(64, 128))
+        vpar.append(page[4 * d.v_qp_off[h]: 4 * d.v_qp_off[h] + 512].view(np.float32).reshape(64, 2))
+    st = cache.quant["k_stage"].cpu().numpy().view(np.uint16)
+    s0 = d.k_stage_off[h] + b * 64 * c
+    k_stage = st[s0: s0 + (t_mid - n_full * 64) * c].reshape(-1, c)
+    k_codes = np.concatenate(k_codes) if k_codes else np.zeros((0, c), np.uint8)
+    kpar = np.stack(kpar) if kpar else np.zeros((0, c, 2), np.float32)
+    v_codes = np.concatenate(v_codes)[:t_mid] if v_codes else np.zeros((0, 128), np.uint8)
+    vpar = np.concatenate(vpar)[:t_mid] if vpar else np.zeros((0, 2), np.float32)
+    return {"k_codes": k_codes, "k_scale": kpar[..., 0], "k_lo": kpar[..., 1], "k_stage": k_stage,
+            "v_codes": v_codes, "v_scale": vpar[:, 0], "v_lo": vpar[:, 1]}
+
+
 def read_pair_q(cache, b, h, t_mid):
     """Host copies of one (batch row, live KV head) pair's low-bit middle
     for t_mid middle rows: a dict shaped like oracle.quantize_middle."""
     d = cache.desc
+    if d.page_rows:
+        return _read_paged_q(cache, b, h, t_mid)
     bits, c = d.quant_bits, d.kept_count[h]
     g_rows = -(-d.mid_capacity // 64) * 64
     n_full = t_mid // 64

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert "leank_build_mask" in names and "leank_pack_k" in names and "leank_decode_attn" in names
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.leank_abi_version() == 5
+    assert lib.leank_abi_version() == 6
     assert lib.leank_layer_cache_size() == ctypes.sizeof(_lib.LayerCacheDesc)
 
 
@@ -269,6 +269,51 @@ def test_plan_layer_paged_layout():
     assert d.k_prun_off[1] == -1 and d.v_mid_off[1] == -1
     assert d.page_bytes == 64 * (2 * sum(kept) + 256 * len(live))
     assert d.pool_bytes == n_pages * d.page_bytes
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_plan_layer_paged_q_layout(bits):
+    """A paged low-bit page: K codes of the live heads in group order, their
+    K (scale, min) pairs, their V code blocks, then their V row parameters;
+    one 64-row K group per page; staging outside the pool."""
+    kept = [32, 0, 64, 8]
+    batch, max_ctx, n_sink, window, n_pages = 3, 1000, 4, 61, 50
+    d = dac.leank_plan_layer_paged_q(kept, batch, 8, 4, 128, n_sink, window, max_ctx, n_pages, bits)
+    mid_cap = max_ctx - n_sink - window
+    assert d.quant_bits == bits and d.page_rows == 64 and d.pages_per_row == -(-mid_cap // 64)
+    assert d.k_q_bytes == d.k_qp_bytes == d.v_q_bytes == d.v_qp_bytes == 0
+    assert d.k_stage_bytes == batch * 64 * sum(kept) * 2
+    live = [h for h in (d.group_order[n] for n in range(4)) if kept[h] > 0]
+    kc = 64 * sum(kept) * bits // 8
+    kp = 8 * sum(kept)
+    vc = 64 * 128 * bits // 8
+    k_pre = 0
+    for rank, h in enumerate(live):
+        assert d.k_q_off[h] == 64 * k_pre * bits // 8
+        assert d.k_qp_off[h] * 4 == kc + 8 * k_pre
+        assert d.v_q_off[h] == kc + kp + rank * vc
+        assert d.v_qp_off[h] * 4 == kc + kp + len(live) * vc + rank * 512
+        assert d.k_stage_off[h] == batch * 64 * k_pre
+        k_pre += kept[h]
+    assert d.page_bytes == kc + kp + len(live) * (vc + 512)
+    assert d.pool_bytes == n_pages * d.page_bytes
+    # every segment 16-byte aligned
+    for h in live:
+        assert d.k_q_off[h] % 16 == 0 and (d.k_qp_off[h] * 4) % 16 == 0
+        assert d.v_q_off[h] % 16 == 0 and (d.v_qp_off[h] * 4) % 16 == 0
+    # quant_bits 0 is the bf16 paged plan
+    d0 = dac.leank_plan_layer_paged_q(kept, batch, 8, 4, 128, n_sink, window, max_ctx, n_pages, 0)
+    d1 = dac.leank_plan_layer_paged(kept, batch, 8, 4, 128, n_sink, window, max_ctx, n_pages)
+    assert bytes(d0) == bytes(d1)
+
+
+def test_paged_q_layout_rejected_when_moved():
+    L = _lib.lib()
+    desc = dac.leank_plan_layer_paged_q([32, 0], 2, 4, 2, 128, 4, 8, 200, 4, 4)
+    desc.kept_idx = desc.k_sl = desc.v_sl = desc.pool = desc.block_table = desc.k_stage = 0x1000
+    ws = dac.leank_workspace_bytes(desc, 100)
+    desc.v_q_off[0] += 16                  # not the canonical page layout (rejected before any launch)
+    assert L.leank_decode_attn(ctypes.byref(desc), 0x1000, 100, 0.1, 0x1000, 0x1000, ws, None) == _lib.EINVAL
 
 
 def test_paged_plan_and_calls_rejected():
