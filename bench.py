@@ -356,11 +356,14 @@ def main():
         q8 = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup, quant_bits=8)
         q4 = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup, quant_bits=4)
         paged = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup, paged=True)
+        paged_q4 = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup,
+                            quant_bits=4, paged=True)
         extras = {
             "unfused_pack_then_decode": unfused,
             "lowbit_middle_8bit": q8,
             "lowbit_middle_4bit": q4,
             "paged_middle_64row_pages": paged,
+            "paged_lowbit_4bit": paged_q4,
             "dense_0pct": dense,
             "speedup_vs_0pct_step": dense["us_per_step"] / main_res["us_per_step"],
             "speedup_fused_vs_unfused_step": unfused["us_per_step"] / main_res["us_per_step"],
