@@ -358,6 +358,8 @@ def main():
         paged = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup, paged=True)
         paged_q4 = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup,
                             quant_bits=4, paged=True)
+        long_cfg = get_config("llama32_b1_128k")
+        long_ctx = workload(long_cfg, copies=args.copies, steps=args.steps, warmup=args.warmup)
         extras = {
             "unfused_pack_then_decode": unfused,
             "lowbit_middle_8bit": q8,
@@ -370,6 +372,7 @@ def main():
             "qwen_b16_32k": qwen,
             "qwen_b16_32k_dense_0pct": qwen_dense,
             "qwen_speedup_vs_0pct_step": qwen_dense["us_per_step"] / qwen["us_per_step"],
+            "llama_b1_128k_layer0": long_ctx,
         }
     if args.copy_calibration:
         extras["copy_calibration"] = copy_calibration()

@@ -176,7 +176,12 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
 #ifndef LEANK_COMBINE_WAVE
 #define LEANK_COMBINE_WAVE 1
 #endif
-  p.combine_slices = max_items > 256 ? 8 : max_items > 64 ? 4 : max_items > 16 ? 2 : 1;
+  // channel slices per (pair, query head): 8 * slices item groups per
+  // workgroup, so that each thread merges about two items (32 slices at most:
+  // one float4 of channels per workgroup)
+  int slices = 1;
+  while (slices < 32 && 16 * slices < max_items) slices *= 2;
+  p.combine_slices = slices;
   // few items per pair: one wavefront per (pair, head) merges them without
   // barriers (measured faster up to 16 items; the workgroup form wins beyond)
   if (LEANK_COMBINE_WAVE && max_items <= 16) p.combine_slices = 0;

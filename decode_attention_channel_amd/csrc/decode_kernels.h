@@ -565,8 +565,9 @@ __global__ __launch_bounds__(kThreads) void decode_combine_wave_kernel(const Dec
 // Merges the records of one (batch row, KV head) pair for one query head g
 // of its group -- or, when the pair has many items, for one of `slices`
 // channel slices of that head -- and writes the output.  Threads form
-// item groups x float4 channel quads; item group j takes items j, j+groups,
-// ...; the groups are summed in a fixed order, so the result does not
+// item groups x float4 channel quads; item group j merges items j,
+// j + groups, ... in one pass with a running maximum, and the groups'
+// (max, sum, acc) are then merged as a fixed tree, so the result does not
 // depend on timing.  Grid: pairs x G x slices.
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodeParams p) {
@@ -590,68 +591,65 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodePa
   const int m_off = G * LEANK_HEAD_DIM + g;
   const int l_off = G * LEANK_HEAD_DIM + G + g;
   const int t = threadIdx.x;
-
-  float m = -INFINITY;
-  for (int n = t; n < n_items; n += kThreads) m = fmaxf(m, first[n * stride + m_off]);
-  s_max[t] = m;
-  __syncthreads();
-  for (int half = kThreads / 2; half > 0; half /= 2) {
-    if (t < half) s_max[t] = fmaxf(s_max[t], s_max[t + half]);
-    __syncthreads();
-  }
-  const float m_all = s_max[0];
-  const float m_use = m_all == -INFINITY ? 0.0f : m_all;
-
   const int grp = t / quads;
   const int quad = t - grp * quads;
   const int ch = g * LEANK_HEAD_DIM + (slice * quads + quad) * 4;
+
+  // one pass: this thread's items n = grp, grp + groups, ... (all their
+  // loads issued together) merged with a running maximum
+  float m = -INFINITY, l = 0.0f;
   float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  float l = 0.0f;
-  int n = grp;
-  for (; n + 3 * groups < n_items; n += 4 * groups) {
-    float f[4], lw[4];
+  for (int n0 = grp; n0 < n_items; n0 += 4 * groups) {
+    float mi[4], li[4];
     float4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float* rn = first + (n + u * groups) * stride;
-      f[u] = rn[m_off];
-      lw[u] = rn[l_off];
+      const int n = n0 + u * groups;
+      const float* rn = first + static_cast<int64_t>(n < n_items ? n : n0) * stride;
+      mi[u] = n < n_items ? rn[m_off] : -INFINITY;
+      li[u] = rn[l_off];
       v[u] = *reinterpret_cast<const float4*>(rn + ch);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float w = fast_exp2(f[u] - m_use);
-      a.x = fmaf(v[u].x, w, a.x);
-      a.y = fmaf(v[u].y, w, a.y);
-      a.z = fmaf(v[u].z, w, a.z);
-      a.w = fmaf(v[u].w, w, a.w);
-      l = fmaf(lw[u], w, l);
+      const float mn = fmaxf(m, mi[u]);
+      const float mu = mn == -INFINITY ? 0.0f : mn;
+      const float fo = fast_exp2(m - mu), fi = fast_exp2(mi[u] - mu);  // 0 for -inf
+      a.x = fmaf(v[u].x, fi, a.x * fo);
+      a.y = fmaf(v[u].y, fi, a.y * fo);
+      a.z = fmaf(v[u].z, fi, a.z * fo);
+      a.w = fmaf(v[u].w, fi, a.w * fo);
+      l = fmaf(li[u], fi, l * fo);
+      m = mn;
     }
   }
-  for (; n < n_items; n += groups) {
-    const float* rn = first + n * stride;
-    const float w = fast_exp2(rn[m_off] - m_use);
-    const float4 v = *reinterpret_cast<const float4*>(rn + ch);
-    a.x = fmaf(v.x, w, a.x);
-    a.y = fmaf(v.y, w, a.y);
-    a.z = fmaf(v.z, w, a.z);
-    a.w = fmaf(v.w, w, a.w);
-    l = fmaf(rn[l_off], w, l);
-  }
+  s_max[t] = m;
   s_acc[t] = a;
   s_sum[t] = l;
   __syncthreads();
-  if (t < quads) {
-    float4 o = s_acc[t];
-    float total = s_sum[t];
-    for (int j = 1; j < groups; ++j) {
-      const float4 x = s_acc[j * quads + t];
-      o.x += x.x;
-      o.y += x.y;
-      o.z += x.z;
-      o.w += x.w;
-      total += s_sum[j * quads + t];
+  // the item groups' parts, merged as a fixed tree (groups is a power of two)
+  for (int half = groups / 2; half > 0; half /= 2) {
+    if (grp < half) {
+      const int o = t + half * quads;
+      const float m1 = s_max[t], m2 = s_max[o];
+      const float mn = fmaxf(m1, m2);
+      const float mu = mn == -INFINITY ? 0.0f : mn;
+      const float f1 = fast_exp2(m1 - mu), f2 = fast_exp2(m2 - mu);
+      const float4 x = s_acc[o];
+      float4 y = s_acc[t];
+      y.x = fmaf(x.x, f2, y.x * f1);
+      y.y = fmaf(x.y, f2, y.y * f1);
+      y.z = fmaf(x.z, f2, y.z * f1);
+      y.w = fmaf(x.w, f2, y.w * f1);
+      s_acc[t] = y;
+      s_sum[t] = fmaf(s_sum[o], f2, s_sum[t] * f1);
+      s_max[t] = mn;
     }
+    __syncthreads();
+  }
+  if (t < quads) {
+    const float4 o = s_acc[t];
+    const float total = s_sum[t];
     const float inv = total > 0.0f ? 1.0f / total : 0.0f;  // an empty row gives zeros
     float* out = p.out + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM + ch;
     *reinterpret_cast<float4*>(out) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);

@@ -15,6 +15,10 @@ namespace {
 // Work-item sizing (compile-time tuning knobs; defaults measured on MI355X).
 // Items are sized so that one decode call makes about kTargetCUs *
 // LEANK_ITEMS_PER_CU of them, within [LEANK_ITEM_KB_MIN, LEANK_ITEM_KB_MAX].
+// A call too small for that makes one round of the workgroups the chip runs
+// at once (kTargetCUs * kRoundPerCU) instead, with items no smaller than the
+// minimum: just over one round would leave a short second round running on
+// a nearly idle chip.
 #ifndef LEANK_ITEMS_PER_CU
 #define LEANK_ITEMS_PER_CU 5
 #endif
@@ -26,6 +30,7 @@ namespace {
 #endif
 
 constexpr int64_t kTargetCUs = 256;  // compute units of an MI355X
+constexpr int64_t kRoundPerCU = 3;   // split-kernel workgroups resident per compute unit
 constexpr int64_t kRowQuantum = 64;  // item row counts are multiples of this
 constexpr int64_t kItemBytesMin = int64_t{LEANK_ITEM_KB_MIN} << 10;
 constexpr int64_t kItemBytesMax = int64_t{LEANK_ITEM_KB_MAX} << 10;
@@ -171,8 +176,9 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPl
   for (int h = 0; h < c->n_kv_heads; ++h)
     if (c->kept_count[h] > 0)
       stream_bytes += static_cast<int64_t>(c->batch) * w->t_mid * middle_row_bytes(c, c->kept_count[h]);
-  const int64_t target = std::min(kItemBytesMax, std::max(kItemBytesMin,
-                                  stream_bytes / (kTargetCUs * LEANK_ITEMS_PER_CU)));
+  int64_t target = stream_bytes / (kTargetCUs * LEANK_ITEMS_PER_CU);
+  if (target < kItemBytesMin) target = std::max(kItemBytesMin, stream_bytes / (kTargetCUs * kRoundPerCU));
+  target = std::min(kItemBytesMax, target);
 
   // item counts at the smallest item size bound the workspace for any ctx <= this one
   int64_t bound_per_b = 0, b, unused_n, unused_rows;
