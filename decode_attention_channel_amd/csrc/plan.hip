@@ -23,7 +23,7 @@ namespace {
 #define LEANK_ITEMS_PER_CU 5
 #endif
 #ifndef LEANK_ITEM_KB_MIN
-#define LEANK_ITEM_KB_MIN 64
+#define LEANK_ITEM_KB_MIN 128
 #endif
 #ifndef LEANK_ITEM_KB_MAX
 #define LEANK_ITEM_KB_MAX 448
