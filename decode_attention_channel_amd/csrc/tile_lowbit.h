@@ -84,11 +84,13 @@ struct QGroup {
   const float* v_par;
 };
 
+// page: the group's physical page (paged streams; read by the caller, so
+// that a loop can fetch it ahead of use).
 template <int QB>
-__device__ __forceinline__ QGroup q_group(const QSegment& q, int c, int g) {
+__device__ __forceinline__ QGroup q_group_at_page(const QSegment& q, int c, int g, int page) {
   QGroup a;
   if (q.pool) {
-    const uint8_t* base = q.pool + static_cast<int64_t>(q.pages[g]) * q.page_bytes;
+    const uint8_t* base = q.pool + static_cast<int64_t>(page) * q.page_bytes;
     a.k_codes = base + q.pk_codes;
     a.k_par = reinterpret_cast<const float*>(base + q.pk_par);
     a.v_codes = base + q.pv_codes;
@@ -101,6 +103,11 @@ __device__ __forceinline__ QGroup q_group(const QSegment& q, int c, int g) {
     a.v_par = q.v_par + static_cast<int64_t>(g) * LEANK_QUANT_GROUP * 2;
   }
   return a;
+}
+
+template <int QB>
+__device__ __forceinline__ QGroup q_group(const QSegment& q, int c, int g) {
+  return q_group_at_page<QB>(q, c, g, q.pool ? q.pages[g] : 0);
 }
 
 // Raw operands of one tile of the open K group (the group that is not
@@ -242,34 +249,51 @@ __device__ __forceinline__ float wave_max(float x) {
 // (c * QB / 8 bytes), V codes of both 32-row halves, the row's V (scale, min).
 template <int KB, int QB>
 struct GroupRegs {
-  f32x4_t par;           // 16 bytes of the group's (scale, min) pairs (lanes < c / 2)
+  f32x4_t par;           // 16 bytes of the group's (scale, min) pairs (used in lanes < c / 2)
   uint32_t kc[KB * QB];  // 4-byte words of the K code row (8 or 4 channels each)
   uint32_t vc[2][8][QB == 8 ? 2 : 1];
   float vs, vm;
 };
 
-template <int KB, int QB>
-__device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, GroupRegs<KB, QB>& gr) {
+// kBranchFree: every lane issues every load (past the data it reloads the
+// first words, which are not used), so the loads take no branches and the
+// compiler's waits for them stay exact in a software pipeline; otherwise
+// words past the data are zeros.
+template <int KB, int QB, bool kBranchFree>
+__device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, int page,
+                                           GroupRegs<KB, QB>& gr) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const QGroup at = q_group<QB>(q, c, g0 / LEANK_QUANT_GROUP);
+  const QGroup at = q_group_at_page<QB>(q, c, g0 / LEANK_QUANT_GROUP, page);
   // the group's parameters first: the query tables wait only for them
-  gr.par = 4 * lane < 2 * c ? *reinterpret_cast<const f32x4_t*>(at.k_par + 4 * lane)
-                            : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // (they use lanes 4 lane < 2 c)
+  if constexpr (kBranchFree)
+    gr.par = *reinterpret_cast<const f32x4_t*>(at.k_par + (4 * lane < 2 * c ? 4 * lane : 0));
+  else
+    gr.par = 4 * lane < 2 * c ? *reinterpret_cast<const f32x4_t*>(at.k_par + 4 * lane)
+                              : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   // the row's codes: c * QB / 8 bytes, a multiple of 4 (8-bit: of 8)
   const uint8_t* krow = at.k_codes + lane * c * QB / 8;
   if constexpr (QB == 8) {
 #pragma unroll
     for (int i = 0; i < KB * QB / 2; ++i) {
-      const uint2 w = 8 * i < c ? *reinterpret_cast<const uint2*>(krow + 8 * i) : make_uint2(0u, 0u);
+      uint2 w;
+      if constexpr (kBranchFree)
+        w = *reinterpret_cast<const uint2*>(krow + (8 * i < c ? 8 * i : 0));
+      else
+        w = 8 * i < c ? *reinterpret_cast<const uint2*>(krow + 8 * i) : make_uint2(0u, 0u);
       gr.kc[2 * i] = w.x;
       gr.kc[2 * i + 1] = w.y;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < KB * QB; ++i)
-      gr.kc[i] = 8 * i < c ? *reinterpret_cast<const uint32_t*>(krow + 4 * i) : 0u;
+    for (int i = 0; i < KB * QB; ++i) {
+      if constexpr (kBranchFree)
+        gr.kc[i] = *reinterpret_cast<const uint32_t*>(krow + (8 * i < c ? 4 * i : 0));
+      else
+        gr.kc[i] = 8 * i < c ? *reinterpret_cast<const uint32_t*>(krow + 4 * i) : 0u;
+    }
   }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -540,6 +564,40 @@ __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&v
   }
 }
 
+// Whether a wavefront loads its next complete group while it scores the
+// current one: 4-bit codes with up to 4 query heads per KV head, where the
+// second set of group registers fits the kernel's budget without spills.
+template <int G, int QB>
+constexpr bool kPrefetchGroups = QB == 4 && G <= 4;
+
+// This wavefront's complete groups g0, g0 + 4 * 64, ... below full_end (a
+// multiple of 64; g0 < full_end) as a software pipeline: the next group's loads (and, for
+// a paged stream, the page of the group after it) are in flight while a
+// group is scored.  The loop body holds no branch around a load.
+template <int G, int KB, int QB, bool kPaged>
+__device__ __forceinline__ void attend_groups_pipelined(const QSegment& q, int& g0, int full_end, int c,
+                                                        const uint16_t* s_q, const int16_t* s_idx,
+                                                        float qk_scale, uint16_t* p_lds,
+                                                        RowState<(G + 3) / 4>& rs, WaveState& st) {
+  constexpr int kStep = kWaves * LEANK_QUANT_GROUP;
+  const int last = full_end - LEANK_QUANT_GROUP;
+  GroupRegs<KB, QB> cur, nxt;
+  int page = kPaged ? q.pages[g0 / LEANK_QUANT_GROUP] : 0;
+  load_group<KB, QB, true>(q, c, g0, page, cur);
+  if (kPaged) page = q.pages[min(g0 + kStep, last) / LEANK_QUANT_GROUP];
+  for (; g0 + kStep < full_end; g0 += kStep) {
+    load_group<KB, QB, true>(q, c, g0 + kStep, page, nxt);
+    if (kPaged) page = q.pages[min(g0 + 2 * kStep, last) / LEANK_QUANT_GROUP];
+    attend_group<G, KB, QB>(cur, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+    // the copy waits for the next group's loads: keep it after the group's
+    // work, where those loads have had the whole group to land
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
+  }
+  attend_group<G, KB, QB>(cur, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+  g0 += kStep;  // the wavefront's first group at or past full_end
+}
+
 // Middle rows [r0, r1) of a low-bit stream (r0 on a group boundary): the
 // wavefront's complete groups through the row-per-lane path, then, if it
 // takes it, the open group (staged rows) in the 16x16 tile layout, whose
@@ -565,10 +623,17 @@ __device__ __forceinline__ void attend_range_q(const QSegment& q, int r0, int r1
         rs.vmin[qd][i] = 0.0f;
       }
     }
-    for (; g0 < full_end; g0 += kWaves * LEANK_QUANT_GROUP) {
-      GroupRegs<KB, QB> gr;
-      load_group<KB, QB>(q, c, g0, gr);
-      attend_group<G, KB, QB>(gr, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+    if constexpr (kPrefetchGroups<G, QB>) {
+      if (q.pool)
+        attend_groups_pipelined<G, KB, QB, true>(q, g0, full_end, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+      else
+        attend_groups_pipelined<G, KB, QB, false>(q, g0, full_end, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+    } else {
+      for (; g0 < full_end; g0 += kWaves * LEANK_QUANT_GROUP) {
+        GroupRegs<KB, QB> gr;
+        load_group<KB, QB, false>(q, c, g0, q.pool ? q.pages[g0 / LEANK_QUANT_GROUP] : 0, gr);
+        attend_group<G, KB, QB>(gr, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+      }
     }
     // fold into the tile layout: head 4 grp + i of lane (col, grp), whose
     // 16 lanes' sums the record adds up
