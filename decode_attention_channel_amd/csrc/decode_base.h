@@ -22,6 +22,9 @@ namespace leank {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTileRows = 32;
+// largest item count per (batch row, KV head) pair that the one-wavefront
+// combine merges (larger counts use the workgroup combine)
+constexpr int kWaveCombineItems = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // The reference max only moves when a tile's max exceeds it by more than

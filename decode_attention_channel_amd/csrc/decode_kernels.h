@@ -508,57 +508,58 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
 }
 
 // Merges the records of one (batch row, KV head) pair for one query head g
-// with one wavefront, for pairs of at most 64 items (used up to 16): lane i holds item i's
-// maximum and weight sum, the wavefront reduces them, then every lane sums
-// its two channels over the items in item order (loads issued four items
-// ahead), so no LDS or barrier is involved.  Grid: pairs x G / 4 workgroups
-// of 4 wavefronts.
+// with one wavefront, for pairs of at most kWaveCombineItems items: every
+// load is issued up front (each lane's two channels of every item, and lane
+// i's maximum and weight sum of item i), so the merge takes one round trip
+// to memory; the 16-lane row reductions and the weighted sum over the items
+// in item order follow, with no LDS or barrier.  Grid: one workgroup of G
+// wavefronts per pair (wavefront g: query head g), so the pair's head
+// fields come through scalar loads.
 template <int G>
-__global__ __launch_bounds__(kThreads) void decode_combine_wave_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64 * G) void decode_combine_wave_kernel(const DecodeParams p) {
   const int lane = threadIdx.x & 63;
-  const int64_t unit = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  const int64_t pair = unit / G;
-  const int g = static_cast<int>(unit - pair * G);
-  if (pair >= static_cast<int64_t>(p.n_batch) * p.n_kv) return;  // whole wavefront
-  const int b = static_cast<int>(pair / p.n_kv);
-  const int h = static_cast<int>(pair - static_cast<int64_t>(b) * p.n_kv);
+  const int g = threadIdx.x >> 6;
+  const int b = static_cast<int>(blockIdx.x / p.n_kv);
+  const int h = static_cast<int>(blockIdx.x - b * p.n_kv);
   const DecodeHead hd = p.heads[h];
-  const int n_items = p.n_sl_items + hd.n_mid;
+  const int n_items = p.n_sl_items + hd.n_mid;  // at most kWaveCombineItems
   const int64_t stride = p.partial_stride;
   const float* first = p.partials + (static_cast<int64_t>(b) * p.items_per_b + hd.base) * stride;
   const int m_off = G * LEANK_HEAD_DIM + g;
   const int l_off = G * LEANK_HEAD_DIM + G + g;
 
-  const float m_i = lane < n_items ? first[lane * stride + m_off] : -INFINITY;
-  const float l_i = lane < n_items ? first[lane * stride + l_off] : 0.0f;
-  float m_all = m_i;
-  for (int off = 32; off > 0; off >>= 1) m_all = fmaxf(m_all, __shfl_xor(m_all, off));
-  const float m_use = m_all == -INFINITY ? 0.0f : m_all;
-  const float w_i = lane < n_items ? fast_exp2(m_i - m_use) : 0.0f;
-  const float total = wave_sum(w_i * l_i);
-
-  const float* acc = first + g * LEANK_HEAD_DIM + 2 * lane;
-  float2 a = make_float2(0.0f, 0.0f);
-  int n = 0;
-  for (; n + 4 <= n_items; n += 4) {
-    float2 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float2*>(acc + (n + u) * stride);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = __shfl(w_i, n + u);
-      a.x = fmaf(v[u].x, w, a.x);
-      a.y = fmaf(v[u].y, w, a.y);
-    }
+  float* out = p.out + (static_cast<int64_t>(b) * p.n_q + h * G + g) * LEANK_HEAD_DIM + 2 * lane;
+  if (n_items == 0) {  // no rows: zeros
+    *reinterpret_cast<float2*>(out) = make_float2(0.0f, 0.0f);
+    return;
   }
-  for (; n < n_items; ++n) {
-    const float2 v = *reinterpret_cast<const float2*>(acc + n * stride);
-    const float w = __shfl(w_i, n);
-    a.x = fmaf(v.x, w, a.x);
-    a.y = fmaf(v.y, w, a.y);
+  // Loads past the pair's items re-read its last item (their weights are
+  // 0), so that none of them takes a branch.
+  const int last = n_items - 1;
+  const float* acc = first + g * LEANK_HEAD_DIM + 2 * lane;
+  float2 v[kWaveCombineItems];
+#pragma unroll
+  for (int u = 0; u < kWaveCombineItems; ++u)
+    v[u] = *reinterpret_cast<const float2*>(acc + min(u, last) * stride);
+  const bool has = lane < n_items;
+  const float m_ld = first[min(lane, last) * stride + m_off];
+  const float l_ld = first[min(lane, last) * stride + l_off];
+  const float m_i = has ? m_ld : -INFINITY;
+  const float l_i = has ? l_ld : 0.0f;
+
+  // items sit in lanes 0..15 (row 0): row reductions, read from lane 0
+  const float m_all = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row_max16(m_i))));
+  const float m_use = m_all == -INFINITY ? 0.0f : m_all;
+  const float w_i = has ? fast_exp2(m_i - m_use) : 0.0f;
+  const float total = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row_sum16(w_i * l_i))));
+  float2 a = make_float2(0.0f, 0.0f);
+#pragma unroll
+  for (int u = 0; u < kWaveCombineItems; ++u) {
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_i), u));  // 0 past the items
+    a.x = fmaf(v[u].x, w, a.x);
+    a.y = fmaf(v[u].y, w, a.y);
   }
   const float inv = total > 0.0f ? 1.0f / total : 0.0f;  // an empty row gives zeros
-  float* out = p.out + (static_cast<int64_t>(b) * p.n_q + h * G + g) * LEANK_HEAD_DIM + 2 * lane;
   *reinterpret_cast<float2*>(out) = make_float2(a.x * inv, a.y * inv);
 }
 
@@ -673,10 +674,9 @@ int launch_decode(const DecodeParams& p, int64_t n_items, int64_t n_pairs, int k
     hipLaunchKernelGGL((decode_split_kernel<G, QB, 1>), grid, dim3(kThreads), 0, s, p);
   }
   LEANK_HIP_TRY(hipGetLastError());
-  if (p.combine_slices == 0) {  // every pair has at most 64 items
-    hipLaunchKernelGGL(decode_combine_wave_kernel<G>,
-                       dim3(static_cast<unsigned>((n_pairs * G + kWaves - 1) / kWaves)),
-                       dim3(kThreads), 0, s, p);
+  if (p.combine_slices == 0) {  // every pair has at most kWaveCombineItems items
+    hipLaunchKernelGGL(decode_combine_wave_kernel<G>, dim3(static_cast<unsigned>(n_pairs)), dim3(64 * G), 0,
+                       s, p);
   } else {
     hipLaunchKernelGGL(decode_combine_kernel<G>,
                        dim3(static_cast<unsigned>(n_pairs * G * p.combine_slices)), dim3(kThreads),
