@@ -159,3 +159,38 @@ def test_paged_q_ragged(bits):
                                        n_sink, window, bits), f"paged quant ragged step {s} row {b}")
                 assert_quant_cache_matches(cache, kh[b:b + 1, :, :n], vh[b:b + 1, :, :n], mask, rows=[b])
     unused_pages_untouched(cache)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_full_workload_paged_quant_sampled(bits):
+    """The Llama B64 4K cache with its middle in shuffled 64-row pages: two
+    fused steps against the oracle on sampled (row, query head) outputs.
+    Each wavefront walks several complete groups per item here, so the
+    group loop (and, at 4 bits, its page prefetch) runs at full length."""
+    from synthetic import alpha_for, get_config, make_kv, make_q
+
+    cfg = get_config("llama_b64_4k")
+    om, okc, oki = oracle.build_mask(alpha_for(cfg), cfg.prune_pct, cfg.align)
+    case("paged quant full workload", bits)
+    ppr = -(-(cfg.ctx - cfg.n_sink - cfg.window) // 64)
+    n_pages = cfg.batch * ppr + 3
+    table = shuffled_block_table(np.random.default_rng(bits + 11), cfg.batch, ppr, n_pages)
+    cache = dac.LayerCache(okc[0].tolist(), torch.from_numpy(oki[0]).to(DEV), cfg.batch,
+                           cfg.n_q_heads, cfg.n_kv_heads, cfg.n_sink, cfg.window, cfg.ctx,
+                           device=DEV, n_pages=n_pages, block_table=table, quant_bits=bits)
+    k, v = make_kv(cfg, 0, device=DEV)
+    t0 = cfg.ctx - 2
+    dac.leank_pack_k(cache, k[:, :, :t0].contiguous(), v[:, :, :t0].contiguous())
+    rng = np.random.default_rng(bits + 5)
+    pairs = sorted({(int(rng.integers(cfg.batch)), int(rng.integers(cfg.n_q_heads)))
+                    for _ in range(16)} | {(0, 0), (cfg.batch - 1, cfg.n_q_heads - 1)})
+    kh, vh = bf16_bits(k), bf16_bits(v)
+    for s in range(2):
+        q = make_q(cfg, 0, step=s + 1, device=DEV)
+        out = dac.leank_decode_step(cache, q, k[:, :, t0 + s].contiguous(),
+                                    v[:, :, t0 + s].contiguous())
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        ref = oracle.decode_q(bf16_bits(q), kh[:, :, :t0 + s + 1], vh[:, :, :t0 + s + 1], om[0],
+                              cfg.n_sink, cfg.window, bits, pairs=pairs)
+        assert_close(np.stack([got[b, j] for b, j in pairs]), ref, f"paged bits {bits} step {s}")
