@@ -2,7 +2,6 @@
 // matrix-instruction and cross-lane helpers, and the per-wavefront softmax
 // state.  Compile-time knobs (defaults are the measured best on MI355X):
 //   LEANK_NT_LOADS   1 = stream K/V with non-temporal loads
-//   LEANK_PREFETCH   1 = load the next bf16 tile while the current one computes
 #pragma once
 
 #include <math.h>
@@ -12,9 +11,6 @@
 
 #ifndef LEANK_NT_LOADS
 #define LEANK_NT_LOADS 1
-#endif
-#ifndef LEANK_PREFETCH
-#define LEANK_PREFETCH 0
 #endif
 
 namespace leank {
@@ -175,6 +171,14 @@ __device__ __forceinline__ void gather_q(const uint16_t* s_q, const int16_t* s_i
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
+  if (dense && c == LEANK_HEAD_DIM) {
+    // all channels: one 16-byte LDS read per block
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+      qa[kk] = col < G ? *reinterpret_cast<const u32x4_alias_t*>(s_q + col * LEANK_HEAD_DIM + 32 * kk + 8 * grp)
+                       : u32x4_t{0u, 0u, 0u, 0u};
+    return;
+  }
 #pragma unroll
   for (int kk = 0; kk < KB; ++kk) {
 #pragma unroll

@@ -135,31 +135,35 @@ __device__ __forceinline__ void compute_tile(TileRegs<KB>& tr, int nvalid, int e
   }
 }
 
-// Rows [r0, r1) of one stream, except row excl (-1: none).
+// Rows [r0, r1) of one stream, except row excl (-1: none), for a workgroup
+// whose q rows and kept ids are still on their way to LDS: each wavefront
+// issues its first tile's loads, then joins the workgroup barrier that
+// publishes the staging, then gathers its query operand, so the two memory
+// latencies at the start of an item overlap.  Every thread of the
+// workgroup must call this (it holds the barrier).
 template <int G, int KB>
-__device__ __forceinline__ void attend_range(const uint16_t* kb, int kstride, const uint16_t* vb,
-                                             int r0, int r1, int excl, int c,
-                                             const u32x4_t (&qa)[KB], float qk_scale,
-                                             uint16_t* p_lds, WaveState& st) {
+__device__ __forceinline__ void attend_range_staged(const uint16_t* kb, int kstride,
+                                                    const uint16_t* vb, int r0, int r1, int excl,
+                                                    int c, const uint16_t* s_q,
+                                                    const int16_t* s_idx, bool dense,
+                                                    float qk_scale, uint16_t* p_lds,
+                                                    WaveState& st) {
   const int wave = threadIdx.x >> 6;
   int t0 = r0 + wave * kTileRows;
-#if LEANK_PREFETCH
-  // the next tile's loads are in flight while this one computes
-  TileRegs<KB> cur;
-  if (t0 < r1) load_tile<KB>(kb, kstride, vb, t0, r1 - t0, c, cur);
-  for (; t0 < r1; t0 += kWaves * kTileRows) {
-    const int tn = t0 + kWaves * kTileRows;
-    TileRegs<KB> nxt;
-    if (tn < r1) load_tile<KB>(kb, kstride, vb, tn, r1 - tn, c, nxt);
+  TileRegs<KB> first;
+  if (t0 < r1) load_tile<KB>(kb, kstride, vb, t0, r1 - t0, c, first);
+  __syncthreads();
+  u32x4_t qa[KB];
+  gather_q<G, KB>(s_q, s_idx, dense, c, qa);
+  if (t0 < r1) {
     const int nvalid = r1 - t0;
     if (nvalid >= kTileRows && static_cast<unsigned>(excl - t0) >= kTileRows) {
-      compute_tile<G, KB, false>(cur, kTileRows, -1, qa, qk_scale, p_lds, st);
+      compute_tile<G, KB, false>(first, kTileRows, -1, qa, qk_scale, p_lds, st);
     } else {
-      compute_tile<G, KB, true>(cur, nvalid, excl - t0, qa, qk_scale, p_lds, st);
+      compute_tile<G, KB, true>(first, nvalid, excl - t0, qa, qk_scale, p_lds, st);
     }
-    cur = nxt;
+    t0 += kWaves * kTileRows;
   }
-#else
   for (; t0 < r1; t0 += kWaves * kTileRows) {
     const int nvalid = r1 - t0;
     TileRegs<KB> cur;
@@ -170,7 +174,6 @@ __device__ __forceinline__ void attend_range(const uint16_t* kb, int kstride, co
       compute_tile<G, KB, true>(cur, nvalid, excl - t0, qa, qk_scale, p_lds, st);
     }
   }
-#endif
 }
 
 // Middle rows [r0, r1) of a paged stream: r0 is a multiple of the page
