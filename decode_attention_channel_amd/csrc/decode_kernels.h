@@ -67,8 +67,8 @@
 namespace leank {
 
 // Middle rows of item `chunk_id` of head hd in batch row b (t_mid middle
-// rows in this row) of a low-bit or paged stream: the head's kept channels
-// select the tile width (contiguous bf16 middles: attend_middle_staged).
+// rows in this row) of a low-bit stream: the head's kept channels select
+// the tile width (bf16 middles: attend_middle_staged).
 template <int G, int QB, int KBMAX>
 __device__ __forceinline__ void attend_middle(const DecodeParams& p, const DecodeHead& hd, int b,
                                               int chunk_id, int t_mid, const uint16_t* s_q,
@@ -101,50 +101,44 @@ __device__ __forceinline__ void attend_middle(const DecodeParams& p, const Decod
         }
       }
     }
-  } else if (p.paged) {
-    switch ((c + 31) / 32) {
-      case 1: {
-        u32x4_t qa[1];
-        gather_q<G, 1>(s_q, s_idx, false, c, qa);
-        attend_range_paged<G, 1>(p.pool, p.page_elems, s_pages, hd.k_off, hd.v_off, r0, r1, c, qa,
-                                 p.qk_scale, p_lds, st);
-        break;
-      }
-      case 2: {
-        u32x4_t qa[2];
-        gather_q<G, 2>(s_q, s_idx, false, c, qa);
-        attend_range_paged<G, 2>(p.pool, p.page_elems, s_pages, hd.k_off, hd.v_off, r0, r1, c, qa,
-                                 p.qk_scale, p_lds, st);
-        break;
-      }
-      case 3: {
-        u32x4_t qa[3];
-        gather_q<G, 3>(s_q, s_idx, false, c, qa);
-        attend_range_paged<G, 3>(p.pool, p.page_elems, s_pages, hd.k_off, hd.v_off, r0, r1, c, qa,
-                                 p.qk_scale, p_lds, st);
-        break;
-      }
-      default: {
-        u32x4_t qa[4];
-        gather_q<G, 4>(s_q, s_idx, false, c, qa);
-        attend_range_paged<G, 4>(p.pool, p.page_elems, s_pages, hd.k_off, hd.v_off, r0, r1, c, qa,
-                                 p.qk_scale, p_lds, st);
-        break;
-      }
-    }
   }
 }
 
-// Contiguous bf16 middle rows of item `chunk_id` (the staged form: holds
-// the workgroup barrier that publishes q and the kept ids).
+// bf16 middle rows of item `chunk_id`, contiguous or paged (the staged
+// form: holds the workgroup barrier that publishes q, the kept ids and the
+// item's pages).
 template <int G>
 __device__ __forceinline__ void attend_middle_staged(const DecodeParams& p, const DecodeHead& hd,
                                                      int b, int chunk_id, int t_mid,
                                                      const uint16_t* s_q, const int16_t* s_idx,
-                                                     uint16_t* p_lds, WaveState& st) {
+                                                     const int32_t* s_pages, uint16_t* p_lds,
+                                                     WaveState& st) {
   const int r0 = chunk_id * hd.mid_rows;
   const int r1 = min(t_mid, r0 + hd.mid_rows);
   const int c = hd.kept;
+  if (p.paged) {
+    const int32_t* g_pages =
+        p.block_table + static_cast<int64_t>(b) * p.pages_per_row + r0 / LEANK_PAGE_ROWS;
+    switch ((c + 31) / 32) {
+      case 1:
+        attend_range_paged_staged<G, 1>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
+                                        r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
+        break;
+      case 2:
+        attend_range_paged_staged<G, 2>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
+                                        r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
+        break;
+      case 3:
+        attend_range_paged_staged<G, 3>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
+                                        r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
+        break;
+      default:
+        attend_range_paged_staged<G, 4>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
+                                        r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
+        break;
+    }
+    return;
+  }
   const uint16_t* kb = p.k_prun + hd.k_off + static_cast<int64_t>(b) * p.mid_cap * c;
   const uint16_t* vb = p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM;
   switch ((c + 31) / 32) {
@@ -304,7 +298,7 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   }
   // the staging above is published by the workgroup barrier inside the
   // attend call (bf16 streams: after each wavefront has issued its first
-  // tile's loads) or just below (paged and low-bit middles)
+  // tile's loads) or just below (low-bit middles)
   if (!middle) {
     const int r0 = local * p.sl_rows;
     const int r1 = min(t_sl, r0 + p.sl_rows);
@@ -312,8 +306,8 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     const uint16_t* vb = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM;
     attend_range_staged<G, 4>(kb, LEANK_HEAD_DIM, vb, r0, r1, excl, LEANK_HEAD_DIM, s_q, s_idx,
                               true, p.qk_scale, p_lds, st);
-  } else if (QB == 0 && !p.paged) {
-    attend_middle_staged<G>(p, hd, b, local - p.n_sl_items, t_mid, s_q, s_idx, p_lds, st);
+  } else if (QB == 0) {
+    attend_middle_staged<G>(p, hd, b, local - p.n_sl_items, t_mid, s_q, s_idx, s_pages, p_lds, st);
   } else {
     __syncthreads();
     attend_middle<G, QB, KBMAX>(p, hd, b, local - p.n_sl_items, t_mid, s_q, s_idx, s_pages, p_lds,

@@ -178,20 +178,40 @@ __device__ __forceinline__ void attend_range_staged(const uint16_t* kb, int kstr
 
 // Middle rows [r0, r1) of a paged stream: r0 is a multiple of the page
 // size and s_pages holds the physical pages of rows r0, r0 + 64, ...
-// (tiles never straddle a page: both are 32-row aligned).
+// (tiles never straddle a page: both are 32-row aligned).  Staged as
+// attend_range_staged: the first tile's page comes from g_pages, the block
+// table entries of the same rows in global memory, while s_pages and the q
+// rows are still on their way to LDS.  Every thread of the workgroup must
+// call this (it holds the barrier).
 template <int G, int KB>
-__device__ __forceinline__ void attend_range_paged(const uint16_t* pool, int64_t page_elems,
-                                                   const int32_t* s_pages, int64_t k_off,
-                                                   int64_t v_off, int r0, int r1, int c,
-                                                   const u32x4_t (&qa)[KB], float qk_scale,
-                                                   uint16_t* p_lds, WaveState& st) {
+__device__ __forceinline__ void attend_range_paged_staged(
+    const uint16_t* pool, int64_t page_elems, const int32_t* g_pages, const int32_t* s_pages,
+    int64_t k_off, int64_t v_off, int r0, int r1, int c, const uint16_t* s_q,
+    const int16_t* s_idx, float qk_scale, uint16_t* p_lds, WaveState& st) {
   const int wave = threadIdx.x >> 6;
-  for (int t0 = r0 + wave * kTileRows; t0 < r1; t0 += kWaves * kTileRows) {
+  int t0 = r0 + wave * kTileRows;
+  TileRegs<KB> first;
+  if (t0 < r1) {
+    const uint16_t* page = pool + static_cast<int64_t>(g_pages[(t0 - r0) / LEANK_PAGE_ROWS]) * page_elems;
+    load_tile<KB>(page + k_off, c, page + v_off, t0 % LEANK_PAGE_ROWS, r1 - t0, c, first);
+  }
+  __syncthreads();
+  u32x4_t qa[KB];
+  gather_q<G, KB>(s_q, s_idx, false, c, qa);
+  if (t0 < r1) {
+    const int nvalid = r1 - t0;
+    if (nvalid >= kTileRows) {
+      compute_tile<G, KB, false>(first, kTileRows, -1, qa, qk_scale, p_lds, st);
+    } else {
+      compute_tile<G, KB, true>(first, nvalid, -1, qa, qk_scale, p_lds, st);
+    }
+    t0 += kWaves * kTileRows;
+  }
+  for (; t0 < r1; t0 += kWaves * kTileRows) {
     const int nvalid = r1 - t0;
     const uint16_t* page = pool + static_cast<int64_t>(s_pages[(t0 - r0) / LEANK_PAGE_ROWS]) * page_elems;
-    const int t_in = t0 % LEANK_PAGE_ROWS;
     TileRegs<KB> cur;
-    load_tile<KB>(page + k_off, c, page + v_off, t_in, nvalid, c, cur);
+    load_tile<KB>(page + k_off, c, page + v_off, t0 % LEANK_PAGE_ROWS, nvalid, c, cur);
     if (nvalid >= kTileRows) {
       compute_tile<G, KB, false>(cur, kTileRows, -1, qa, qk_scale, p_lds, st);
     } else {
