@@ -177,10 +177,16 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
 #define LEANK_COMBINE_WAVE 1
 #endif
   // channel slices per (pair, query head): 8 * slices item groups per
-  // workgroup, so that each thread merges about two items (32 slices at most:
-  // one float4 of channels per workgroup)
+  // workgroup, with up to LEANK_COMBINE_SLICE_ITEMS items per slice, so
+  // that each thread merges up to 8 items (32 slices at most: one float4 of
+  // channels per workgroup).  Measured on the 128K-token layer at batch 1
+  // (412 items in its one live pair): 16 / 32 / 64 / 128 / 256 items per
+  // slice gave 22.6 / 21.3 / 21.0 / 21.6 / 22.6 us per step.
+#ifndef LEANK_COMBINE_SLICE_ITEMS
+#define LEANK_COMBINE_SLICE_ITEMS 64
+#endif
   int slices = 1;
-  while (slices < 32 && 16 * slices < max_items) slices *= 2;
+  while (slices < 32 && LEANK_COMBINE_SLICE_ITEMS * slices < max_items) slices *= 2;
   p.combine_slices = slices;
   // few items per pair: one wavefront per (pair, head) merges them without
   // barriers (measured faster up to 16 items; the workgroup form wins beyond)

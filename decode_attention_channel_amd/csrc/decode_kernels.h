@@ -563,13 +563,14 @@ __global__ __launch_bounds__(64 * G) void decode_combine_wave_kernel(const Decod
 // channel slices of that head -- and writes the output.  Threads form
 // item groups x float4 channel quads; item group j merges items j,
 // j + groups, ... in one pass with a running maximum, and the groups'
-// (max, sum, acc) are then merged as a fixed tree, so the result does not
-// depend on timing.  Grid: pairs x G x slices.
+// (max, sum, acc) are then merged in a fixed order (across lanes, then
+// across wavefronts), so the result does not depend on timing.  Grid:
+// pairs x G x slices.
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodeParams p) {
-  __shared__ float s_max[kThreads];
-  __shared__ float4 s_acc[kThreads];
-  __shared__ float s_sum[kThreads];
+  __shared__ float s_max[kWaves * 32];
+  __shared__ float4 s_acc[kWaves * 32];
+  __shared__ float s_sum[kWaves * 32];
   const int slices = p.combine_slices;
   const int quads = LEANK_HEAD_DIM / 4 / slices;  // float4 quads per workgroup
   const int groups = kThreads / quads;
@@ -619,33 +620,56 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodePa
       m = mn;
     }
   }
-  s_max[t] = m;
-  s_acc[t] = a;
-  s_sum[t] = l;
-  __syncthreads();
-  // the item groups' parts, merged as a fixed tree (groups is a power of two)
-  for (int half = groups / 2; half > 0; half /= 2) {
-    if (grp < half) {
-      const int o = t + half * quads;
-      const float m1 = s_max[t], m2 = s_max[o];
-      const float mn = fmaxf(m1, m2);
-      const float mu = mn == -INFINITY ? 0.0f : mn;
-      const float f1 = fast_exp2(m1 - mu), f2 = fast_exp2(m2 - mu);
-      const float4 x = s_acc[o];
-      float4 y = s_acc[t];
-      y.x = fmaf(x.x, f2, y.x * f1);
-      y.y = fmaf(x.y, f2, y.y * f1);
-      y.z = fmaf(x.z, f2, y.z * f1);
-      y.w = fmaf(x.w, f2, y.w * f1);
-      s_acc[t] = y;
-      s_sum[t] = fmaf(s_sum[o], f2, s_sum[t] * f1);
-      s_max[t] = mn;
-    }
-    __syncthreads();
+  // the item groups' parts, merged as a fixed tree: first across the
+  // lanes of each wavefront (groups quads lanes apart), then the four
+  // wavefronts' parts in order through LDS
+  for (int off = quads; off < 64; off *= 2) {
+    const float m2 = __shfl_xor(m, off);
+    const float l2 = __shfl_xor(l, off);
+    float4 x;
+    x.x = __shfl_xor(a.x, off);
+    x.y = __shfl_xor(a.y, off);
+    x.z = __shfl_xor(a.z, off);
+    x.w = __shfl_xor(a.w, off);
+    const float mn = fmaxf(m, m2);
+    const float mu = mn == -INFINITY ? 0.0f : mn;
+    const float f1 = fast_exp2(m - mu), f2 = fast_exp2(m2 - mu);
+    a.x = fmaf(x.x, f2, a.x * f1);
+    a.y = fmaf(x.y, f2, a.y * f1);
+    a.z = fmaf(x.z, f2, a.z * f1);
+    a.w = fmaf(x.w, f2, a.w * f1);
+    l = fmaf(l2, f2, l * f1);
+    m = mn;
   }
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  if (lane < quads) {
+    s_max[wave * quads + lane] = m;
+    s_acc[wave * quads + lane] = a;
+    s_sum[wave * quads + lane] = l;
+  }
+  __syncthreads();
   if (t < quads) {
-    const float4 o = s_acc[t];
-    const float total = s_sum[t];
+    float mw[kWaves];
+    float mn = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      mw[w] = s_max[w * quads + t];
+      mn = fmaxf(mn, mw[w]);
+    }
+    const float mu = mn == -INFINITY ? 0.0f : mn;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float total = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(mw[w] - mu);
+      const float4 x = s_acc[w * quads + t];
+      o.x = fmaf(x.x, f, o.x);
+      o.y = fmaf(x.y, f, o.y);
+      o.z = fmaf(x.z, f, o.z);
+      o.w = fmaf(x.w, f, o.w);
+      total = fmaf(s_sum[w * quads + t], f, total);
+    }
     const float inv = total > 0.0f ? 1.0f / total : 0.0f;  // an empty row gives zeros
     float* out = p.out + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM + ch;
     *reinterpret_cast<float4*>(out) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);

@@ -207,6 +207,17 @@ def test_decode_no_pruning_and_all_dead():
         assert_close(got, ref, str(counts))
 
 
+@pytest.mark.parametrize("ctx", [12_000, 25_000, 50_000, 100_000, 200_000, 340_000])
+def test_decode_many_items_per_pair(ctx):
+    # one long batch row: its live pair's record count grows from a few dozen
+    # to over a thousand, so the workgroup combine runs with every channel
+    # slice count (1 to 32 slices of the 128 channels)
+    mask = mask_with_counts(np.random.default_rng(ctx), [128, 0])
+    case("decode many items", ctx)
+    got, ref = _decode_case(mask, 1, 4, 64, 512, ctx, seed=ctx)
+    assert_close(got, ref, f"ctx={ctx}")
+
+
 def test_decode_large_scores():
     # large K spreads the softmax over few tokens: exercises the running max
     mask = mask_with_counts(np.random.default_rng(5), [32, 64, 0, 128])
