@@ -29,6 +29,21 @@ namespace {
 #define LEANK_ITEM_KB_MAX 448
 #endif
 
+// Item sizing weighs the bytes of a low-bit middle row by
+// LEANK_Q4_ROW_COST / LEANK_Q8_ROW_COST percent: a 4-bit row costs more
+// time per byte than a bf16 row (its codes are expanded on the way into the
+// matrix instructions).  Measured on the Llama batch-64 4K step with a
+// 4-bit middle: 100 / 150 / 200 / 300 percent gave 76.5 / 76.4 / 72.6 /
+// 77.5 us (at 200 the full-width rows of a pair make one item, not two);
+// with an 8-bit middle 100 / 150 / 200 / 300 gave 89.5 / 91.4 / 91.6 /
+// 95.5 us.
+#ifndef LEANK_Q4_ROW_COST
+#define LEANK_Q4_ROW_COST 200
+#endif
+#ifndef LEANK_Q8_ROW_COST
+#define LEANK_Q8_ROW_COST 100
+#endif
+
 constexpr int64_t kTargetCUs = 256;  // compute units of an MI355X
 constexpr int64_t kRoundPerCU = 3;   // split-kernel workgroups resident per compute unit
 constexpr int64_t kRowQuantum = 64;  // item row counts are multiples of this
@@ -69,6 +84,16 @@ int64_t middle_row_bytes(const leank_layer_cache* c, int kept) {
   // codes of K and V, the row's V scale and minimum (K parameters are per group)
   return (static_cast<int64_t>(kept) + LEANK_HEAD_DIM) * c->quant_bits / 8 + 8;
 }
+
+namespace {
+// Sizing weight of one middle row: its bytes, scaled for low-bit rows.
+int64_t middle_row_cost(const leank_layer_cache* c, int kept) {
+  const int64_t bytes = middle_row_bytes(c, kept);
+  if (c->quant_bits == 4) return bytes * LEANK_Q4_ROW_COST / 100;
+  if (c->quant_bits == 8) return bytes * LEANK_Q8_ROW_COST / 100;
+  return bytes;
+}
+}  // namespace
 
 int validate_cache(const leank_layer_cache* c, bool need_buffers) {
   if (!c) return LEANK_EINVAL;
@@ -171,11 +196,12 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPl
   w->group = c->n_q_heads / c->n_kv_heads;
   w->t_sl = static_cast<int32_t>(std::min<int64_t>(ctx_len, slots));
   w->t_mid = static_cast<int32_t>(std::max<int64_t>(0, ctx_len - slots));
-  // bytes the call streams (K and V rows of both regions)
+  // bytes the call streams (K and V rows of both regions; low-bit middle
+  // rows weighted by their cost)
   int64_t stream_bytes = static_cast<int64_t>(c->batch) * c->n_kv_heads * w->t_sl * 4 * LEANK_HEAD_DIM;
   for (int h = 0; h < c->n_kv_heads; ++h)
     if (c->kept_count[h] > 0)
-      stream_bytes += static_cast<int64_t>(c->batch) * w->t_mid * middle_row_bytes(c, c->kept_count[h]);
+      stream_bytes += static_cast<int64_t>(c->batch) * w->t_mid * middle_row_cost(c, c->kept_count[h]);
   int64_t target = stream_bytes / (kTargetCUs * LEANK_ITEMS_PER_CU);
   if (target < kItemBytesMin) target = std::max(kItemBytesMin, stream_bytes / (kTargetCUs * kRoundPerCU));
   target = std::min(kItemBytesMax, target);
@@ -195,7 +221,7 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPl
     w->head_base[h] = base;
     const int kept = c->kept_count[h];
     if (kept > 0) {
-      const int64_t row_bytes = middle_row_bytes(c, kept);
+      const int64_t row_bytes = middle_row_cost(c, kept);
       split_rows(w->t_mid, row_target(row_bytes, kItemBytesMin), &n32, &rows32, &b);
       bound_per_b += b;
       int64_t rows = row_target(row_bytes, target);
