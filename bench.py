@@ -18,7 +18,8 @@ roofline figures from HIP events on the launch stream, the same step as two
 calls (leank_pack_k, then leank_decode_attn), the same step with the middle
 held in 8-bit and 4-bit streams and in 64-row pages through a shuffled block
 table, the same kernels at 0% pruning, the
-Qwen2.5-7B-shaped cache, and the CPU oracle's time for the same step (a
+Qwen2.5-7B-shaped cache, the 128K-token batch-1 workload (one layer, and all
+32 layers per token), and the CPU oracle's time for the same step (a
 baseline, not a target).
 """
 
@@ -218,6 +219,73 @@ def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20, fused=Tru
     return res
 
 
+def whole_model(cfg, steps=20, warmup=3):
+    """All layers of a multi-layer workload per token: each layer has its own
+    mask (one global threshold over every layer, as the mask is built),
+    cache and query; a step is one leank_decode_step call per layer, in
+    layer order.  Returns per-token time and the algorithmic bytes of every
+    layer's attention."""
+    import torch
+
+    import decode_attention_channel_amd as dac
+    from synthetic import alpha_for, make_kv, make_q, make_step_kv
+
+    dev = torch.device("cuda:0")
+    alpha = torch.from_numpy(alpha_for(cfg)).to(dev)
+    mask, kept_count, kept_idx = dac.leank_build_mask(alpha, cfg.prune_pct, cfg.align)
+    counts_all = kept_count.cpu().tolist()
+    max_ctx = cfg.ctx + steps + warmup + 2
+    layers = []
+    for layer in range(cfg.n_layers):
+        cache = dac.LayerCache(counts_all[layer], kept_idx[layer].contiguous(), cfg.batch,
+                               cfg.n_q_heads, cfg.n_kv_heads, cfg.n_sink, cfg.window, max_ctx)
+        k, v = make_kv(cfg, layer, n_tokens=cfg.ctx - 1, device=dev)
+        dac.leank_pack_k(cache, k, v)
+        del k, v
+        cache.workspace()
+        new = [make_step_kv(cfg, layer, s, device=dev) for s in range(steps + warmup)]
+        out = torch.empty((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+        layers.append((cache, make_q(cfg, layer, device=dev), new, out))
+    torch.cuda.synchronize()
+
+    def token(s):
+        for cache, q, new, out in layers:
+            dac.leank_decode_step(cache, q, new[s][0], new[s][1], out=out)
+
+    for s in range(warmup):
+        token(s)
+    torch.cuda.synchronize()
+    ctx0 = layers[0][0].length
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s in range(steps):
+        token(warmup + s)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / steps
+    # each step attends over its own context (the append comes first)
+    byt = sum(dac.leank_decode_bytes(cache, ctx0 + s + 1)
+              for cache, _, _, _ in layers for s in range(steps)) / steps
+    live = sum(1 for row in counts_all for c in row if c > 0)
+    res = {
+        "us_per_token": us,
+        "us_per_layer_mean": us / cfg.n_layers,
+        "decode_bytes_per_token": byt,
+        "achieved_GBps": byt / (us * 1e-6) / 1e9,
+        "frac_of_peak": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        "layers": cfg.n_layers,
+        "live_kv_heads": live,
+        "kv_heads": cfg.n_layers * cfg.n_kv_heads,
+        "ctx_range_timed": [ctx0 + 1, ctx0 + steps],
+        "steps": steps,
+    }
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg, target_seconds):
     """The CPU oracle on the same workload's decode step, on host cores.
 
@@ -360,6 +428,7 @@ def main():
                             quant_bits=4, paged=True)
         long_cfg = get_config("llama32_b1_128k")
         long_ctx = workload(long_cfg, copies=args.copies, steps=args.steps, warmup=args.warmup)
+        long_model = whole_model(long_cfg)
         extras = {
             "unfused_pack_then_decode": unfused,
             "lowbit_middle_8bit": q8,
@@ -373,6 +442,7 @@ def main():
             "qwen_b16_32k_dense_0pct": qwen_dense,
             "qwen_speedup_vs_0pct_step": qwen_dense["us_per_step"] / qwen["us_per_step"],
             "llama_b1_128k_layer0": long_ctx,
+            "llama_b1_128k_all_32_layers": long_model,
         }
     if args.copy_calibration:
         extras["copy_calibration"] = copy_calibration()
