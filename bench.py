@@ -34,6 +34,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+SHAPES = {
+    "llama_b64_4k": "Llama-3.1-8B attention, one layer",
+    "qwen_b16_32k": "Qwen2.5-7B attention, one layer",
+    "llama32_b1_128k": "Llama-3.1-8B attention, layer 0 of the 32-layer 128K-token cache",
+}
 METRIC = ("pruned decode-attn µs/step & achieved HBM GB/s (% of 8 TB/s), "
           "Llama-3.1-8B shape")
 
@@ -44,6 +49,10 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=6, help="rotating cache copies")
+    ap.add_argument("--workload", default="llama_b64_4k",
+                    help="workload of the main line (llama_b64_4k is the headline; another "
+                         "one-layer workload, e.g. qwen_b16_32k or llama32_b1_128k (its layer "
+                         "0), is for profiling it alone with --skip-extras)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the main workload (no 0%% pruning, Qwen or CPU baseline)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -408,7 +417,12 @@ def main():
     import decode_attention_channel_amd as dac
 
     dac.lib()  # fail loudly if the HIP library is missing
-    cfg = get_config("llama_b64_4k")
+    cfg = get_config(args.workload)
+    headline = cfg.name == "llama_b64_4k"
+    if not headline and not args.skip_extras:
+        print("--workload other than llama_b64_4k profiles that workload alone: add --skip-extras",
+              file=sys.stderr)
+        sys.exit(2)
     torch.cuda.synchronize()
     main_res = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup)
     extras = {}
@@ -465,7 +479,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": cfg.name,
-            "shape": "Llama-3.1-8B attention, one layer",
+            "shape": SHAPES.get(cfg.name, cfg.name),
             "batch": cfg.batch,
             "n_q_heads": cfg.n_q_heads,
             "n_kv_heads": cfg.n_kv_heads,
@@ -481,13 +495,15 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("leank_decode_step = decode_split_kernel<4> + decode_combine_kernel<4>; "
+            "kernel": (f"leank_decode_step = decode_split_kernel<{cfg.group}> + its combine "
+                       f"(decode_combine_wave_kernel<{cfg.group}> up to 16 items per pair, "
+                       f"else decode_combine_kernel<{cfg.group}>); "
                        "one launch pair per step, averaged over the timed steps"),
             "achieved": main_res["achieved_GBps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": main_res["frac_of_peak"],
-            "traffic": measured_traffic(),
+            "traffic": measured_traffic() if headline else None,
             "bytes_per_launch": main_res["decode_bytes_mean"],
             "launch_us": main_res["us_per_step"],
         },
