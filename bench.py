@@ -50,6 +50,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=6, help="rotating cache copies")
     ap.add_argument("--workload", default="llama_b64_4k",
+                    choices=["llama_b64_4k", "qwen_b16_32k", "llama32_b1_128k"],
                     help="workload of the main line (llama_b64_4k is the headline; another "
                          "one-layer workload, e.g. qwen_b16_32k or llama32_b1_128k (its layer "
                          "0), is for profiling it alone with --skip-extras)")
@@ -407,9 +408,15 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
               "multi-GPU path; every figure is one GPU's.", file=sys.stderr)
         sys.exit(2)
-    import torch
-
     from synthetic import get_config
+
+    cfg = get_config(args.workload)
+    headline = cfg.name == "llama_b64_4k"
+    if not headline and not args.skip_extras:
+        print("--workload other than llama_b64_4k profiles that workload alone: add --skip-extras",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -417,12 +424,6 @@ def main():
     import decode_attention_channel_amd as dac
 
     dac.lib()  # fail loudly if the HIP library is missing
-    cfg = get_config(args.workload)
-    headline = cfg.name == "llama_b64_4k"
-    if not headline and not args.skip_extras:
-        print("--workload other than llama_b64_4k profiles that workload alone: add --skip-extras",
-              file=sys.stderr)
-        sys.exit(2)
     torch.cuda.synchronize()
     main_res = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup)
     extras = {}
