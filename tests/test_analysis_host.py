@@ -5,7 +5,7 @@ import pytest
 
 import decode_attention_channel_amd as dac
 import oracle
-from synthetic import CONFIGS, alpha_for
+from synthetic import alpha_for, get_config
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
@@ -21,7 +21,7 @@ def test_retention_and_hf_ratio_match_oracle(cfg):
 
 def test_synthetic_alpha_keeps_low_frequency_pairs_more():
     # the recipe's f_c rises with the pair index, so retention should too
-    cfg = CONFIGS[4]
+    cfg = get_config("llama32_b64_gen")
     mask, _, _ = oracle.build_mask(alpha_for(cfg), cfg.prune_pct, cfg.align)
     ret = dac.leank_pair_retention(mask)
     assert ret[:16].mean() < ret[48:].mean()
@@ -29,7 +29,7 @@ def test_synthetic_alpha_keeps_low_frequency_pairs_more():
 
 def test_rank_correlation_matches_oracle():
     rng = np.random.default_rng(3)
-    for cfg in CONFIGS[:3]:
+    for cfg in (get_config("tiny"), get_config("llama_b64_4k"), get_config("qwen_b16_32k")):
         a = alpha_for(cfg)
         b = alpha_for(cfg, seed=cfg.alpha_seed + 1)
         for x, y in ((a, b), (a, a * 1.5 + 0.1), (np.round(a, 1), np.round(b, 1))):
