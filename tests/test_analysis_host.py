@@ -5,7 +5,7 @@ import pytest
 
 import decode_attention_channel_amd as dac
 import oracle
-from synthetic import alpha_for, get_config
+from synthetic import CONFIGS, alpha_for, get_config
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: c.name)
