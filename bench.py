@@ -57,7 +57,7 @@ def parse_args():
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the main workload (no 0%% pruning, Qwen or CPU baseline)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time for the oracle baseline sample")
+                    help="target wall time for the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
     return ap.parse_args()
@@ -300,8 +300,8 @@ def cpu_baseline(cfg, target_seconds):
     """The CPU oracle on the same workload's decode step, on host cores.
 
     Samples whole batch rows (all query heads of a row, full context),
-    cycling through the batch until about `target_seconds` of CPU time have
-    been spent, and scales the mean time per row to the full batch.
+    cycling through the batch until about `target_seconds` of wall time have
+    passed, and scales the mean wall time per row to the full batch.
     """
     import numpy as np
     import torch
@@ -340,7 +340,7 @@ def cpu_baseline(cfg, target_seconds):
         "sample": (f"{n} batch-row decodes of the {cfg.name} step ({n / cfg.batch:.1f} passes over "
                    f"the {cfg.batch} rows; each row = all {cfg.n_q_heads} query heads over the "
                    f"{cfg.ctx}-token cache), float64 numpy, mean per row x {cfg.batch}; "
-                   f"{sum(per_row):.1f} s of CPU time"),
+                   f"{sum(per_row):.1f} s wall time on {int(threads)} threads"),
     }
 
 
