@@ -191,6 +191,7 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   // few items per pair: one wavefront per (pair, head) merges them without
   // barriers (measured faster up to 16 items; the workgroup form wins beyond)
   if (LEANK_COMBINE_WAVE && max_items <= kWaveCombineItems) p.combine_slices = 0;
+  p.wave_items = max_items;
   p.qk_scale = scale * kLog2e;
   p.n_batch = c->batch;
   p.paged = c->page_rows != 0;

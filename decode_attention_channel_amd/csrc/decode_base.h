@@ -90,7 +90,7 @@ struct DecodeParams {
   const int32_t* block_table;  // [batch][pages_per_row]
   int64_t page_elems;
   int32_t pages_per_row;
-  int32_t pad_p;
+  int32_t wave_items;  // one-wavefront combine: the most items of any pair
   DecodeHead heads[LEANK_MAX_KV_HEADS];
 };
 
