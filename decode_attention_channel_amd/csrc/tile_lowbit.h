@@ -259,7 +259,9 @@ struct GroupRegs {
 // first words, which are not used), so the loads take no branches and the
 // compiler's waits for them stay exact in a software pipeline; otherwise
 // words past the data are zeros.
-template <int KB, int QB, bool kBranchFree>
+// kPart: 0 every load of the group, 1 its K codes and parameters only, 2 its
+// V codes only.
+template <int KB, int QB, bool kBranchFree, int kPart = 0>
 __device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, int page,
                                            GroupRegs<KB, QB>& gr) {
   const int lane = threadIdx.x & 63;
@@ -268,6 +270,7 @@ __device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, int
   const QGroup at = q_group_at_page<QB>(q, c, g0 / LEANK_QUANT_GROUP, page);
   // the group's parameters first: the query tables wait only for them
   // (they use lanes 4 lane < 2 c)
+  if constexpr (kPart != 2) {
   if constexpr (kBranchFree)
     gr.par = *reinterpret_cast<const f32x4_t*>(at.k_par + (4 * lane < 2 * c ? 4 * lane : 0));
   else
@@ -295,6 +298,8 @@ __device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, int
         gr.kc[i] = 8 * i < c ? *reinterpret_cast<const uint32_t*>(krow + 4 * i) : 0u;
     }
   }
+  }
+  if constexpr (kPart != 1) {
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const uint8_t* vt = at.v_codes + ((4 * half + grp) * LEANK_HEAD_DIM + col) * (LEANK_V_BLOCK * QB / 8);
@@ -310,9 +315,12 @@ __device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, int
       }
     }
   }
-  const float2 pr = *reinterpret_cast<const float2*>(at.v_par + lane * 2);
-  gr.vs = pr.x;
-  gr.vm = pr.y;
+  }
+  if constexpr (kPart != 2) {
+    const float2 pr = *reinterpret_cast<const float2*>(at.v_par + lane * 2);
+    gr.vs = pr.x;
+    gr.vm = pr.y;
+  }
 }
 
 // Builds the group's query tables in this wavefront's LDS and returns the
@@ -598,6 +606,40 @@ __device__ __forceinline__ void attend_groups_pipelined(const QSegment& q, int& 
   g0 += kStep;  // the wavefront's first group at or past full_end
 }
 
+// Whether a wavefront loads only the K part of its next group (K codes and
+// parameters, 14 VGPRs at 8 bits) while it scores the current one: 8-bit
+// codes with up to 4 query heads per KV head, where the whole next group
+// (46 VGPRs) spills at three waves per SIMD.
+template <int G, int QB>
+constexpr bool kPrefetchGroupK = QB == 8 && G <= 4;
+
+// As attend_groups_pipelined, with only the next group's K codes and
+// parameters in flight while a group is scored; its V codes are issued when
+// the group is done and land behind the next group's tables and scores.
+template <int G, int KB, int QB, bool kPaged>
+__device__ __forceinline__ void attend_groups_kpart_pipelined(const QSegment& q, int& g0, int full_end, int c,
+                                                    const uint16_t* s_q, const int16_t* s_idx,
+                                                    float qk_scale, uint16_t* p_lds,
+                                                    RowState<(G + 3) / 4>& rs, WaveState& st) {
+  constexpr int kStep = kWaves * LEANK_QUANT_GROUP;
+  GroupRegs<KB, QB> cur, nxt;
+  load_group<KB, QB, true>(q, c, g0, kPaged ? q.pages[g0 / LEANK_QUANT_GROUP] : 0, cur);
+  for (; g0 + kStep < full_end; g0 += kStep) {
+    const int pn = kPaged ? q.pages[(g0 + kStep) / LEANK_QUANT_GROUP] : 0;
+    load_group<KB, QB, true, 1>(q, c, g0 + kStep, pn, nxt);
+    attend_group<G, KB, QB>(cur, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+    __builtin_amdgcn_sched_barrier(0);
+    cur.par = nxt.par;
+#pragma unroll
+    for (int i = 0; i < KB * QB; ++i) cur.kc[i] = nxt.kc[i];
+    cur.vs = nxt.vs;
+    cur.vm = nxt.vm;
+    load_group<KB, QB, true, 2>(q, c, g0 + kStep, pn, cur);
+  }
+  attend_group<G, KB, QB>(cur, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+  g0 += kStep;
+}
+
 // Middle rows [r0, r1) of a low-bit stream (r0 on a group boundary): the
 // wavefront's complete groups through the row-per-lane path, then, if it
 // takes it, the open group (staged rows) in the 16x16 tile layout, whose
@@ -628,6 +670,13 @@ __device__ __forceinline__ void attend_range_q(const QSegment& q, int r0, int r1
         attend_groups_pipelined<G, KB, QB, true>(q, g0, full_end, c, s_q, s_idx, qk_scale, p_lds, rs, st);
       else
         attend_groups_pipelined<G, KB, QB, false>(q, g0, full_end, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+    } else if constexpr (kPrefetchGroupK<G, QB>) {
+      if (q.pool)
+        attend_groups_kpart_pipelined<G, KB, QB, true>(q, g0, full_end, c, s_q, s_idx, qk_scale,
+                                                       p_lds, rs, st);
+      else
+        attend_groups_kpart_pipelined<G, KB, QB, false>(q, g0, full_end, c, s_q, s_idx, qk_scale,
+                                                        p_lds, rs, st);
     } else {
       for (; g0 < full_end; g0 += kWaves * LEANK_QUANT_GROUP) {
         GroupRegs<KB, QB> gr;
