@@ -189,7 +189,7 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   while (slices < 32 && LEANK_COMBINE_SLICE_ITEMS * slices < max_items) slices *= 2;
   p.combine_slices = slices;
   // few items per pair: one wavefront per (pair, head) merges them without
-  // barriers (measured faster up to 16 items; the workgroup form wins beyond)
+  // barriers (measured faster up to 32 items)
   if (LEANK_COMBINE_WAVE && max_items <= kWaveCombineItems) p.combine_slices = 0;
   p.wave_items = max_items;
   p.qk_scale = scale * kLog2e;

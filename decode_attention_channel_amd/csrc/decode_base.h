@@ -20,7 +20,10 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTileRows = 32;
 // largest item count per (batch row, KV head) pair that the one-wavefront
 // combine merges (larger counts use the workgroup combine)
-constexpr int kWaveCombineItems = 16;
+#ifndef LEANK_WAVE_COMBINE_ITEMS
+#define LEANK_WAVE_COMBINE_ITEMS 32
+#endif
+constexpr int kWaveCombineItems = LEANK_WAVE_COMBINE_ITEMS;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // The reference max only moves when a tile's max exceeds it by more than

@@ -506,13 +506,15 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
 // with one wavefront, for pairs of at most kWaveCombineItems items: every
 // load is issued up front (each lane's two channels of every item, and lane
 // i's maximum and weight sum of item i), so the merge takes one round trip
-// to memory; the 16-lane row reductions and the weighted sum over the items
-// in item order follow, with no LDS or barrier.  Grid: one workgroup of G
+// to memory; the 16-lane row reductions (two rows for 32 items) and the
+// weighted sum over the items in item order follow, with no LDS or barrier.  Grid: one workgroup of G
 // wavefronts per pair (wavefront g: query head g), so the pair's head
-// fields come through scalar loads.  NI (4, 8 or 16) covers the most items
-// of any pair of the call: loads past a pair's items re-read its last one,
-// so a smaller NI issues fewer of them (Llama batch-64 step: 113.7 ->
-// 113.05 us with NI 4 instead of 16).
+// fields come through scalar loads.  NI (4, 8, 16 or 32) covers the most
+// items of any pair of the call: loads past a pair's items re-read its last
+// one, so a smaller NI issues fewer of them (Llama batch-64 step: 113.7 ->
+// 113.05 us with NI 4 instead of 16).  Up to 32 items this form beats the
+// workgroup combine (Qwen batch-16 32K step, 27 items per pair: 93.2 ->
+// 92.6 us).
 template <int G, int NI>
 __global__ __launch_bounds__(64 * G) void decode_combine_wave_kernel(const DecodeParams p) {
   const int lane = threadIdx.x & 63;
@@ -545,11 +547,19 @@ __global__ __launch_bounds__(64 * G) void decode_combine_wave_kernel(const Decod
   const float m_i = has ? m_ld : -INFINITY;
   const float l_i = has ? l_ld : 0.0f;
 
-  // items sit in lanes 0..15 (row 0): row reductions, read from lane 0
-  const float m_all = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row_max16(m_i))));
+  // items sit in lanes 0..NI-1: one 16-lane row, or two for NI = 32
+  const float m_r = row_max16(m_i);
+  const float m_all =
+      NI <= 16 ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(m_r)))
+               : fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_r), 0)),
+                       __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_r), 16)));
   const float m_use = m_all == -INFINITY ? 0.0f : m_all;
   const float w_i = has ? fast_exp2(m_i - m_use) : 0.0f;
-  const float total = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(row_sum16(w_i * l_i))));
+  const float t_r = row_sum16(w_i * l_i);
+  const float total =
+      NI <= 16 ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(t_r)))
+               : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t_r), 0)) +
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t_r), 16));
   float2 a = make_float2(0.0f, 0.0f);
 #pragma unroll
   for (int u = 0; u < NI; ++u) {
@@ -710,6 +720,8 @@ int launch_decode(const DecodeParams& p, int64_t n_items, int64_t n_pairs, int k
       hipLaunchKernelGGL((decode_combine_wave_kernel<G, 4>), pairs, dim3(64 * G), 0, s, p);
     else if (p.wave_items <= 8)
       hipLaunchKernelGGL((decode_combine_wave_kernel<G, 8>), pairs, dim3(64 * G), 0, s, p);
+    else if (p.wave_items <= 16)
+      hipLaunchKernelGGL((decode_combine_wave_kernel<G, 16>), pairs, dim3(64 * G), 0, s, p);
     else
       hipLaunchKernelGGL((decode_combine_wave_kernel<G, kWaveCombineItems>), pairs, dim3(64 * G), 0, s, p);
   } else {
