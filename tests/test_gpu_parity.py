@@ -207,11 +207,12 @@ def test_decode_no_pruning_and_all_dead():
         assert_close(got, ref, str(counts))
 
 
-@pytest.mark.parametrize("ctx", [12_000, 25_000, 50_000, 100_000, 200_000, 340_000])
+@pytest.mark.parametrize("ctx", [4_000, 7_000, 12_000, 25_000, 50_000, 100_000, 200_000, 340_000])
 def test_decode_many_items_per_pair(ctx):
-    # one long batch row: its live pair's record count grows from a few dozen
-    # to over a thousand, so the workgroup combine runs with every channel
-    # slice count (1 to 32 slices of the 128 channels)
+    # one long batch row: its live pair's record count grows from about 17
+    # (the one-wavefront combine's two-row form) to over a thousand, so the
+    # workgroup combine runs with every channel slice count (1 to 32 slices
+    # of the 128 channels)
     mask = mask_with_counts(np.random.default_rng(ctx), [128, 0])
     case("decode many items", ctx)
     got, ref = _decode_case(mask, 1, 4, 64, 512, ctx, seed=ctx)
