@@ -24,6 +24,9 @@ constexpr int kTileRows = 32;
 #define LEANK_WAVE_COMBINE_ITEMS 32
 #endif
 constexpr int kWaveCombineItems = LEANK_WAVE_COMBINE_ITEMS;
+// its reductions cover one or two 16-lane rows of item lanes
+static_assert(kWaveCombineItems == 16 || kWaveCombineItems == 32,
+              "the one-wavefront combine merges up to 16 or 32 items");
 constexpr float kLog2e = 1.4426950408889634f;
 
 // The reference max only moves when a tile's max exceeds it by more than
