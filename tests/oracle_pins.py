@@ -18,8 +18,10 @@ the module disagrees with:
 * the KV-cache sizes the pages work out (tests/golden/kv_cache_sizes.json);
 * for the low-bit middle streams: values already on a quantization grid
   come back exactly, every value lands on its nearest level (brute force
-  over all levels), each group's minimum and maximum land on the end
-  levels, attention over grid-exact caches equals the unquantized
+  over all levels), values half-way between two levels take the even code,
+  each group's minimum and maximum land on the end levels, every (batch row,
+  live head) of a low-bit pack gives back its own middle exactly on
+  grid-exact inputs, attention over grid-exact caches equals the unquantized
   definition, and the byte count equals the size of the packed arrays.
 
 The same functions run against deliberately broken copies of the oracle in
@@ -582,6 +584,80 @@ def pin_quant_middle_groups(O):
             assert qm["v_codes"][r, np.argmax(vx[r])] == top
 
 
+def pin_quant_ties_to_even(O):
+    # values exactly half-way between two levels (float32-exact: the quotient
+    # (x - lo) / scale is k + 1/2 with no rounding) take the even code, the
+    # IEEE default rounding of the reading the low-bit streams follow
+    for bits in (2, 4, 8):
+        top = 2 ** bits - 1
+        k = np.arange(top)
+        for lo, step in ((0.0, 1.0), (-3.0, 0.25)):
+            x = lo + np.concatenate([[0.0, float(top)], k + 0.5]) * step
+            want = np.concatenate([[0, top], k + (k & 1)])
+            for axis, arr in ((0, x[:, None]), (1, x[None, :])):
+                codes, scale, lo_q = O.quantize_asym(arr.astype(np.float32), bits, axis=axis)
+                assert np.all(scale == np.float32(step)) and np.all(lo_q == np.float32(lo))
+                assert np.array_equal(codes.reshape(-1).astype(np.int64), want), (bits, lo, axis)
+
+
+def pin_pack_q_contents(O):
+    # grid-exact K/V (both ends of every grid present), coded by position,
+    # channel, batch row and head: every (b, live h) of the low-bit pack must
+    # give back exactly that pair's own middle -- its kept K channels of the
+    # complete groups from the codes, the open group's K rows as bf16, and
+    # its V rows from the codes -- and a dead head holds nothing
+    n_sink, window, d, group = 3, 5, 128, 64
+    batch, n_kv, kept = 2, 3, [32, 0, 64]
+    rng = np.random.default_rng(46)
+    kept_idx = np.full((n_kv, d), -1, dtype=np.int64)
+    for h, c in enumerate(kept):
+        kept_idx[h, :c] = np.sort(rng.choice(d, size=c, replace=False))
+    t_mid = 2 * group + 19
+    ctx_len = n_sink + t_mid + window
+    t = np.arange(ctx_len)[None, None, :, None]
+    ch = np.arange(d)[None, None, None, :]
+    bb = np.arange(batch)[:, None, None, None]
+    hh = np.arange(n_kv)[None, :, None, None]
+    for bits in (4, 8):
+        top = 2 ** bits - 1
+        lvl_k = np.broadcast_to((3 * t + 5 * ch + 7 * bb + 11 * hh) % (top + 1),
+                                (batch, n_kv, ctx_len, d)).copy()
+        lvl_v = np.broadcast_to((5 * t + 3 * ch + 11 * bb + 7 * hh) % (top + 1),
+                                (batch, n_kv, ctx_len, d)).copy()
+        for b in range(batch):
+            for h in range(n_kv):
+                for g in range(t_mid // group):       # K: each channel spans its group's grid
+                    r0 = n_sink + g * group
+                    lvl_k[b, h, r0 + (b + h) % 32, :] = 0
+                    lvl_k[b, h, r0 + 32 + (b + 2 * h) % 32, :] = top
+                for r in range(ctx_len):              # V: each row spans its grid
+                    lvl_v[b, h, r, (r + b) % 64] = 0
+                    lvl_v[b, h, r, 64 + (r + h) % 64] = top
+        lo_k = -2.0 + 0.25 * bb + 0.5 * hh
+        lo_v = -1.5 + 0.5 * bb + 0.25 * hh
+        k = _f32_to_bf16_bits(lo_k + lvl_k * 0.125)       # multiples of 1/8 below 32: exact
+        v = _f32_to_bf16_bits(lo_v + lvl_v * 0.125)
+        ref = O.pack_reference_q(k, v, kept, kept_idx, n_sink, window, bits, group)
+        assert ref["mid_q"][1] is None, bits
+        mids = np.arange(n_sink, n_sink + t_mid)
+        n_full = (t_mid // group) * group
+        for h in (0, 2):
+            idx = kept_idx[h, :kept[h]]
+            assert len(ref["mid_q"][h]) == batch
+            for b in range(batch):
+                m = ref["mid_q"][h][b]
+                want_k = _bits_to_f64(k[b, h][mids][:, idx]).numpy()
+                want_v = _bits_to_f64(v[b, h][mids]).numpy()
+                kc = m["k_codes"].astype(np.float64).reshape(-1, group, kept[h])
+                got_k = (kc * m["k_scale"].astype(np.float64)[:, None, :]
+                         + m["k_lo"].astype(np.float64)[:, None, :]).reshape(n_full, kept[h])
+                assert np.array_equal(got_k, want_k[:n_full]), (bits, h, b)
+                assert np.array_equal(m["k_stage"], k[b, h][mids][n_full:][:, idx]), (bits, h, b)
+                got_v = (m["v_codes"].astype(np.float64) * m["v_scale"].astype(np.float64)[:, None]
+                         + m["v_lo"].astype(np.float64)[:, None])
+                assert np.array_equal(got_v, want_v), (bits, h, b)
+
+
 def _grid_context(rng, batch, n_kv, ctx_len, d, bits, mid_lo, mid_hi, group):
     """K, V bits whose middle rows [mid_lo, mid_hi) lie on per-group
     (K, per channel) and per-row (V) grids with both ends present, so that
@@ -672,6 +748,8 @@ ALL_PINS = [
     pin_quant_closed_forms,
     pin_quant_nearest_level,
     pin_quant_middle_groups,
+    pin_quant_ties_to_even,
+    pin_pack_q_contents,
     pin_decode_q_grid_exact,
     pin_traffic_bytes_q,
 ]

@@ -98,6 +98,15 @@ MUTANTS = [
     ("quantized attention reads exact middle V",
      "v = dequantize(kq[\"v_codes\"], kq[\"v_scale\"][:, None], kq[\"v_lo\"][:, None])",
      "v = bf16_bits_to_f64(v_bits[b, h][middle_pos])"),
+    ("quantization rounds half-way values up",
+     "raw = np.rint((x - lo) / scale)",
+     "raw = np.floor((x - lo) / scale + 0.5)"),
+    ("low-bit pack quantizes batch row 0 for every row",
+     "mid_q.append([quantize_middle(kp[b], ref[\"v_mid\"][head][b], bits, group)",
+     "mid_q.append([quantize_middle(kp[0], ref[\"v_mid\"][head][0], bits, group)"),
+    ("low-bit pack pairs every head's K with the first live head's V",
+     "mid_q.append([quantize_middle(kp[b], ref[\"v_mid\"][head][b], bits, group)",
+     "mid_q.append([quantize_middle(kp[b], [m for m in ref[\"v_mid\"] if m is not None][0][b], bits, group)"),
     ("open K group left out of the byte count",
      "k = n_groups * group * c * bits // 8 + n_groups * c * 8 + n_stage * c * 2",
      "k = n_groups * group * c * bits // 8 + n_groups * c * 8"),
