@@ -52,6 +52,7 @@ __all__ = [
     "leank_pack_k_rows",
     "leank_decode_attn_rows",
     "leank_decode_step",
+    "leank_decode_step_noalloc",
     "leank_decode_step_rows",
     "leank_pair_retention",
     "leank_head_hf_ratio",
@@ -382,7 +383,7 @@ def _step_token(cache, t, name):
         raise ValueError(f"{name} must be [batch, n_kv_heads, 128] (or with a length-1 token axis)")
 
 
-def _step_common(cache, q, k_new, v_new, scale, out, workspace):
+def _step_common(cache, q, k_new, v_new, scale, out, workspace, need_workspace=True):
     _require(q, torch.bfloat16, "q", ndim=3, device=cache.device)
     if tuple(q.shape) != (cache.batch, cache.n_q_heads, HEAD_DIM):
         raise ValueError("q must be [batch, n_q_heads, 128]")
@@ -396,7 +397,7 @@ def _step_common(cache, q, k_new, v_new, scale, out, workspace):
         _require(out, torch.float32, "out", ndim=3, device=cache.device)
         if out.shape != q.shape:
             raise ValueError("out must match q's shape")
-    if workspace is None:
+    if workspace is None and need_workspace:
         workspace = cache.workspace()
     return scale, out, workspace
 
@@ -415,6 +416,23 @@ def leank_decode_step(cache, q, k_new, v_new, pos=None, scale=None, out=None, wo
                                      workspace.numel() * workspace.element_size(),
                                      stream_handle(stream))
     check(status, "leank_decode_step")
+    cache.length = int(pos) + 1
+    return out
+
+
+def leank_decode_step_noalloc(cache, q, k_new, v_new, pos=None, scale=None, out=None,
+                              stream=None):
+    """leank_decode_step with the split-K records in the library's own
+    device scratch (no workspace, no allocation in the library; out must be
+    given by a caller that cannot allocate either).  Calls that overlap on
+    one device race."""
+    if pos is None:
+        pos = cache.length
+    scale, out, _ = _step_common(cache, q, k_new, v_new, scale, out, None, need_workspace=False)
+    status = lib().leank_decode_step_noalloc(_desc(cache), ptr(q), ptr(k_new), ptr(v_new),
+                                             int(pos), float(scale), ptr(out),
+                                             stream_handle(stream))
+    check(status, "leank_decode_step_noalloc")
     cache.length = int(pos) + 1
     return out
 

@@ -20,6 +20,7 @@ PAGE_ROWS = 64
 MAX_KV_HEADS = 64
 MAX_GROUP = 8
 CHANNEL_QUANTUM = 8
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 OK, EINVAL, EUNSUPPORTED, ECAPACITY, EWORKSPACE, EHIP = 0, -1, -2, -3, -4, -5
 
@@ -137,6 +138,9 @@ _SIGNATURES = {
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "leank_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(LayerCacheDesc), ctypes.c_void_p,
+                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                 ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),
     "leank_pair_retention": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_void_p]),
     "leank_head_hf_ratio": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,

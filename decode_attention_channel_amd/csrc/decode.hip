@@ -4,8 +4,17 @@
 // decode_kernels.h, instantiated per group size in decode_g1.hip ..
 // decode_g8.hip.
 
+#include <mutex>
+
 #include "decode_kernels.h"
 #include "quant.h"
+
+// Scratch of leank_decode_step_noalloc: the split-K records of one call, in
+// a file-scope device array instead of a caller's workspace.  Each device
+// the library runs on holds its own copy until the process ends.  Host code
+// never uses this name as an address: the device address comes from
+// hipGetSymbolAddress, once per device (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[LEANK_NOALLOC_SCRATCH_BYTES];
 
 namespace leank {
 
@@ -77,6 +86,31 @@ extern "C" int leank_workspace_init(void* workspace, size_t workspace_bytes, voi
 
 namespace {
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device (with it current) and kept.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LEANK_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return LEANK_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LEANK_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LEANK_OK;
+}
+
+}  // namespace
+
+
+namespace {
+
 // What a call adds to plain decode attention over the cached rows.
 struct CallExtras {
   const int32_t* ctx_lens = nullptr;  // ragged decode: per-row lengths
@@ -84,6 +118,7 @@ struct CallExtras {
   const void* k_new = nullptr;
   const void* v_new = nullptr;
   const int64_t* row_pos = nullptr;   // ragged step: per-row positions
+  bool scratch = false;               // records in the library's device scratch, not a workspace
 };
 
 // plan_len: rows the regular items cover -- the context length of a decode
@@ -106,6 +141,11 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
     if (plan_len > c->max_ctx) return LEANK_ECAPACITY;
   }
   if (!(scale > 0.0f) || !isfinite(scale)) return LEANK_EINVAL;
+  if (x.scratch) {  // every argument is checked: look the device scratch up
+    st = scratch_ptr(&workspace);
+    if (st != LEANK_OK) return st;
+    workspace_bytes = LEANK_NOALLOC_SCRATCH_BYTES;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   bool step = x.step;
   bool lens_from_pos = false;  // attention over row_pos[b] + 1 tokens after a separate append
@@ -284,4 +324,16 @@ extern "C" int leank_decode_step_rows(const leank_layer_cache* c, const void* q,
   x.v_new = v_new;
   x.row_pos = row_pos;
   return decode_impl(c, q, x, max_ctx_len - 1, scale, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int leank_decode_step_noalloc(const leank_layer_cache* c, const void* q,
+                                         const void* k_new, const void* v_new, int64_t pos,
+                                         float scale, float* out, void* stream) {
+  CallExtras x;
+  x.step = true;
+  x.k_new = k_new;
+  x.v_new = v_new;
+  x.scratch = true;
+  // the kernels write every record they read, so the scratch needs no clearing
+  return decode_impl(c, q, x, pos, scale, out, nullptr, 0, stream);
 }

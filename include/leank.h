@@ -19,7 +19,9 @@
  *
  * Conventions for every entry point:
  *   - All buffers are caller-owned.  The library allocates no device memory
- *     and keeps no state between calls; every function is re-entrant.
+ *     and keeps no state between calls; every function is re-entrant.  The
+ *     one exception is leank_decode_step_noalloc, for callers that cannot
+ *     allocate: it uses a scratch array the library holds on each device.
  *   - "device" pointers address HIP device memory of the current device;
  *     "host" pointers address ordinary host memory.
  *   - bf16 tensors are passed as raw 16-bit patterns (void*).
@@ -39,7 +41,7 @@
 extern "C" {
 #endif
 
-#define LEANK_ABI_VERSION 6
+#define LEANK_ABI_VERSION 7
 #define LEANK_HEAD_DIM 128      /* the only head_dim the kernels implement   */
 #define LEANK_MAX_KV_HEADS 64   /* per-layer KV heads a cache plan can hold  */
 #define LEANK_MAX_GROUP 8       /* query heads per KV head the kernels take  */
@@ -47,6 +49,7 @@ extern "C" {
 #define LEANK_V_BLOCK 8         /* V rows per transposed storage block        */
 #define LEANK_QUANT_GROUP 64    /* middle rows per K quantization group       */
 #define LEANK_PAGE_ROWS 64      /* middle rows per page of a paged cache      */
+#define LEANK_NOALLOC_SCRATCH_BYTES (16u << 20) /* scratch of leank_decode_step_noalloc */
 
 typedef enum {
   LEANK_OK = 0,
@@ -418,6 +421,26 @@ int leank_decode_step_rows(const leank_layer_cache* cache, const void* q, const 
                            const void* v_new, const int64_t* row_pos, int64_t max_ctx_len,
                            float scale, float* out, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/*
+ * leank_decode_step_noalloc -- leank_decode_step for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments and result as
+ * leank_decode_step without the workspace: the split-K records go to a
+ * scratch array of LEANK_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each device it runs on, from that device's first call until the process
+ * ends.  Allocates nothing (no hipMalloc, hipFree or allocating library
+ * call); the first call on a device looks the array's address up.
+ * Errors: as leank_decode_step, and LEANK_EWORKSPACE, before any launch,
+ * when the call needs more than LEANK_NOALLOC_SCRATCH_BYTES
+ * (leank_workspace_bytes(cache, pos + 1) larger).  Every call on a device
+ * shares that device's array: calls that overlap in time on one device
+ * (other streams, other threads) race and must be serialised by the
+ * caller.
+ */
+int leank_decode_step_noalloc(const leank_layer_cache* cache, const void* q, const void* k_new,
+                              const void* v_new, int64_t pos, float scale, float* out,
+                              void* stream);
 
 /*
  * leank_decode_bytes -- host.  Algorithmic HBM bytes of one

@@ -33,7 +33,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert "leank_build_mask" in names and "leank_pack_k" in names and "leank_decode_attn" in names
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.leank_abi_version() == 6
+    assert lib.leank_abi_version() == 7
     assert lib.leank_layer_cache_size() == ctypes.sizeof(_lib.LayerCacheDesc)
 
 
@@ -180,6 +180,29 @@ def test_step_calls_rejected_before_launch():
     assert step_rows(p, 101) == _lib.ECAPACITY
     assert step_rows(p, 10, k=0x1004) == _lib.EINVAL
     assert L.leank_decode_step(None, p, p, p, 5, 0.1, p, p, ws, None) == _lib.EINVAL
+
+
+def test_noalloc_step_rejected_before_launch():
+    """The allocation-free step checks every argument before it looks up its
+    device scratch (so these fail the same way with or without a GPU)."""
+    L = _lib.lib()
+    desc = _fake_buffers(dac.leank_plan_layer([32, 0], 2, 4, 2, 128, 4, 8, 100))
+    ref = ctypes.byref(desc)
+    p = 0x1000
+
+    def step(pos, k=p, v=p, q=p, scale=0.1, out=p):
+        return L.leank_decode_step_noalloc(ref, q, k, v, pos, scale, out, None)
+
+    assert step(100) == _lib.ECAPACITY
+    assert step(-1) == _lib.EINVAL
+    assert step(5, k=None) == _lib.EINVAL
+    assert step(5, v=0x1008) == _lib.EINVAL
+    assert step(5, q=0x1002) == _lib.EINVAL
+    assert step(5, out=None) == _lib.EINVAL
+    assert step(5, scale=float("inf")) == _lib.EINVAL
+    assert L.leank_decode_step_noalloc(None, p, p, p, 5, 0.1, p, None) == _lib.EINVAL
+    unset = dac.leank_plan_layer([32, 0], 2, 4, 2, 128, 4, 8, 100)
+    assert L.leank_decode_step_noalloc(ctypes.byref(unset), p, p, p, 5, 0.1, p, None) == _lib.EINVAL
 
 
 def test_workspace_covers_a_step_at_the_same_context():
