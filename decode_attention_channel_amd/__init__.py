@@ -68,8 +68,8 @@ def _normalize_device(device):
     return device
 
 
-def _require(t, dtype, name, ndim=None, device=None):
-    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+def _require(t, dtype, name, ndim=None, device=None, allow_cpu=False):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not (t.is_cuda or allow_cpu):
         raise TypeError(f"{name} must be a {dtype} tensor on the GPU")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -80,20 +80,27 @@ def _require(t, dtype, name, ndim=None, device=None):
 
 
 def leank_build_mask(alpha, prune_pct, align, stream=None):
-    """Channel mask from alpha float32 [L, H_kv, d] on the GPU (synchronous).
+    """Channel mask from alpha float32 [L, H_kv, d] (synchronous): on the
+    GPU for a device tensor (leank_build_mask), on the host for a CPU tensor
+    (leank_build_mask_host).
 
     Returns (mask uint8 [L,H,d], kept_count int32 [L,H], kept_idx int16 [L,H,d]),
     all on alpha's device.
     """
-    _require(alpha, torch.float32, "alpha", ndim=3)
+    _require(alpha, torch.float32, "alpha", ndim=3, allow_cpu=True)
     n_layers, n_heads, d = alpha.shape
     mask = torch.empty((n_layers, n_heads, d), dtype=torch.uint8, device=alpha.device)
     kept_count = torch.empty((n_layers, n_heads), dtype=torch.int32, device=alpha.device)
     kept_idx = torch.empty((n_layers, n_heads, d), dtype=torch.int16, device=alpha.device)
-    status = lib().leank_build_mask(ptr(alpha), n_layers, n_heads, d, int(prune_pct), int(align),
-                                    ptr(mask), ptr(kept_count), ptr(kept_idx),
-                                    stream_handle(stream))
-    check(status, "leank_build_mask")
+    if alpha.device.type == "cpu":
+        status = lib().leank_build_mask_host(ptr(alpha), n_layers, n_heads, d, int(prune_pct),
+                                             int(align), ptr(mask), ptr(kept_count), ptr(kept_idx))
+        check(status, "leank_build_mask_host")
+    else:
+        status = lib().leank_build_mask(ptr(alpha), n_layers, n_heads, d, int(prune_pct),
+                                        int(align), ptr(mask), ptr(kept_count), ptr(kept_idx),
+                                        stream_handle(stream))
+        check(status, "leank_build_mask")
     return mask, kept_count, kept_idx
 
 

@@ -1,4 +1,6 @@
 // leank_build_mask: stage-2 channel mask of the LeanK page, section 2.2.
+// leank_build_mask_host computes the same mask on the host from host
+// memory (the offline conversion of that section, with no device involved).
 //
 // Kernel 1 (one workgroup) finds the global threshold: the order statistic
 // of all alpha values at ascending rank ceil((n-1)*p/100), by a 4-pass
@@ -7,10 +9,33 @@
 // threshold, floors the count to the alignment and keeps the channels of
 // rank below that count in the head's (alpha desc, channel asc) order.
 
+#include <math.h>
+
+#include <algorithm>
+#include <numeric>
+#include <vector>
+
 #include "common.h"
 
 namespace leank {
 namespace {
+
+// Arguments both forms check before any work.  The kept counts a mask can
+// give are multiples of `align`; the cache plan takes multiples of
+// LEANK_CHANNEL_QUANTUM, so an align that is not one is refused here rather
+// than by the plan one call later.
+int check_mask_args(const void* alpha, int32_t n_layers, int32_t n_kv_heads, int32_t head_dim,
+                    int32_t prune_pct, int32_t align, const void* mask_out,
+                    const void* kept_count_out, const void* kept_idx_out) {
+  if (!alpha || !mask_out || !kept_count_out || !kept_idx_out) return LEANK_EINVAL;
+  if (n_layers < 1 || n_kv_heads < 1 || head_dim < 1 || head_dim > 1024) return LEANK_EINVAL;
+  if (prune_pct < 0 || prune_pct > 100) return LEANK_EINVAL;
+  if (align < 1 || head_dim % align) return LEANK_EINVAL;
+  if (align % LEANK_CHANNEL_QUANTUM) return LEANK_EUNSUPPORTED;
+  const int64_t heads = static_cast<int64_t>(n_layers) * n_kv_heads;
+  if (heads > INT32_MAX || heads * head_dim > INT32_MAX) return LEANK_EINVAL;
+  return LEANK_OK;
+}
 
 constexpr uint32_t kNanKey = 0xFFFFFFFFu;  // a NaN was seen (no finite/inf key is this large)
 
@@ -110,13 +135,11 @@ extern "C" int leank_build_mask(const float* alpha, int32_t n_layers, int32_t n_
                                 int32_t head_dim, int32_t prune_pct, int32_t align,
                                 uint8_t* mask_out, int32_t* kept_count_out,
                                 int16_t* kept_idx_out, void* stream) {
-  if (!alpha || !mask_out || !kept_count_out || !kept_idx_out) return LEANK_EINVAL;
-  if (n_layers < 1 || n_kv_heads < 1 || head_dim < 1 || head_dim > 1024) return LEANK_EINVAL;
-  if (prune_pct < 0 || prune_pct > 100) return LEANK_EINVAL;
-  if (align < 1 || head_dim % align) return LEANK_EINVAL;
+  const int st = check_mask_args(alpha, n_layers, n_kv_heads, head_dim, prune_pct, align, mask_out,
+                                 kept_count_out, kept_idx_out);
+  if (st != LEANK_OK) return st;
   const int64_t heads = static_cast<int64_t>(n_layers) * n_kv_heads;
   const int64_t n = heads * head_dim;
-  if (heads > INT32_MAX || n > INT32_MAX) return LEANK_EINVAL;
   const int64_t rank = ((n - 1) * prune_pct + 99) / 100;  // ceil((n-1) p / 100)
   hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -136,5 +159,43 @@ extern "C" int leank_build_mask(const float* alpha, int32_t n_layers, int32_t n_
                      alpha, head_dim, align, key, mask_out, kept_count_out, kept_idx_out);
   LEANK_HIP_TRY(hipGetLastError());
   LEANK_HIP_TRY(hipStreamSynchronize(s));
+  return LEANK_OK;
+}
+
+extern "C" int leank_build_mask_host(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
+                                     int32_t head_dim, int32_t prune_pct, int32_t align,
+                                     uint8_t* mask_out, int32_t* kept_count_out,
+                                     int16_t* kept_idx_out) {
+  const int st = check_mask_args(alpha, n_layers, n_kv_heads, head_dim, prune_pct, align, mask_out,
+                                 kept_count_out, kept_idx_out);
+  if (st != LEANK_OK) return st;
+  const int64_t heads = static_cast<int64_t>(n_layers) * n_kv_heads;
+  const int64_t n = heads * head_dim;
+  for (int64_t i = 0; i < n; ++i)
+    if (isnan(alpha[i])) return LEANK_EINVAL;
+  // the global threshold: the value at ascending rank ceil((n - 1) p / 100)
+  // (-0.0 and +0.0 compare equal, as in the float order)
+  const int64_t rank = ((n - 1) * prune_pct + 99) / 100;
+  std::vector<float> sorted(alpha, alpha + n);
+  std::nth_element(sorted.begin(), sorted.begin() + rank, sorted.end());
+  const float threshold = sorted[static_cast<size_t>(rank)];
+  // per head: channels at or above the threshold, floored to the alignment;
+  // that many of the head's largest alpha are kept, ties to the lower channel
+  std::vector<int> order(static_cast<size_t>(head_dim));
+  for (int64_t hd = 0; hd < heads; ++hd) {
+    const float* a = alpha + hd * head_dim;
+    int passing = 0;
+    for (int c = 0; c < head_dim; ++c) passing += a[c] >= threshold ? 1 : 0;
+    const int n_keep = passing / align * align;
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [a](int x, int y) { return a[x] > a[y]; });
+    std::sort(order.begin(), order.begin() + n_keep);
+    uint8_t* m = mask_out + hd * head_dim;
+    int16_t* idx = kept_idx_out + hd * head_dim;
+    std::fill(m, m + head_dim, uint8_t{0});
+    for (int j = 0; j < head_dim; ++j) idx[j] = j < n_keep ? static_cast<int16_t>(order[j]) : int16_t{-1};
+    for (int j = 0; j < n_keep; ++j) m[order[j]] = 1;
+    kept_count_out[hd] = n_keep;
+  }
   return LEANK_OK;
 }

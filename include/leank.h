@@ -79,10 +79,12 @@ size_t leank_layer_cache_size(void);
  *             values at ascending rank ceil((n-1)*prune_pct/100), which is
  *             the set a linear-interpolation percentile selects; channels
  *             with alpha >= threshold pass the global step.
- * align       >= 1 and divides head_dim.  Each head's passing count is
- *             floored to a multiple of align; that many channels with the
- *             largest alpha of the head are kept, ties towards the lower
- *             channel index.
+ * align       divides head_dim (LEANK_EINVAL otherwise) and is a multiple
+ *             of LEANK_CHANNEL_QUANTUM (LEANK_EUNSUPPORTED otherwise: the
+ *             cache plan takes kept counts in that quantum).  Each head's
+ *             passing count is floored to a multiple of align; that many
+ *             channels with the largest alpha of the head are kept, ties
+ *             towards the lower channel index.
  * mask_out        device, uint8 [L][H][d]: 1 = kept.
  * kept_count_out  device, int32 [L][H]: kept channels per head.
  * kept_idx_out    device, int16 [L][H][d]: kept channel ids in ascending
@@ -96,6 +98,19 @@ int leank_build_mask(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
                      int32_t head_dim, int32_t prune_pct, int32_t align,
                      uint8_t* mask_out, int32_t* kept_count_out,
                      int16_t* kept_idx_out, void* stream);
+
+/*
+ * leank_build_mask_host -- the same mask from host memory, computed on the
+ * host: the offline one-off conversion of the LeanK page, section 2.2
+ * stage 2, for a caller that holds alpha on the host.  Host, synchronous,
+ * pure; every pointer is host memory (alpha as above; mask_out uint8
+ * [L][H][d], kept_count_out int32 [L][H], kept_idx_out int16 [L][H][d]).
+ * Same rule, arguments and errors as leank_build_mask, and bit for bit the
+ * same outputs.  Uses no device.
+ */
+int leank_build_mask_host(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
+                          int32_t head_dim, int32_t prune_pct, int32_t align,
+                          uint8_t* mask_out, int32_t* kept_count_out, int16_t* kept_idx_out);
 
 /*
  * One layer's channel-pruned KV cache: shape, head grouping and buffer

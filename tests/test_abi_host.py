@@ -220,6 +220,60 @@ def test_workspace_covers_a_step_at_the_same_context():
             assert dac.leank_workspace_bytes(desc, ctx) >= batch * n_kv * stride * 4
 
 
+def test_host_mask_feeds_the_plan_for_every_align():
+    """leank_build_mask_host from host memory, for every align that divides
+    128: an align the plan's kept-count quantum does not divide is refused
+    (LEANK_EUNSUPPORTED); every other mask equals the oracle's bit for bit
+    and each of its layers plans."""
+    import torch
+
+    for cfg in CONFIGS:
+        alpha = alpha_for(cfg)
+        for align in (1, 2, 4, 8, 16, 32, 64, 128):
+            if align % _lib.CHANNEL_QUANTUM:
+                with pytest.raises(dac.LeankError) as err:
+                    dac.leank_build_mask(torch.from_numpy(alpha), cfg.prune_pct, align)
+                assert err.value.status == _lib.EUNSUPPORTED
+                continue
+            mask, kept_count, kept_idx = dac.leank_build_mask(torch.from_numpy(alpha),
+                                                              cfg.prune_pct, align)
+            om, okc, oki = oracle.build_mask(alpha, cfg.prune_pct, align)
+            assert np.array_equal(mask.numpy(), om), (cfg.name, align)
+            assert np.array_equal(kept_count.numpy(), okc), (cfg.name, align)
+            assert np.array_equal(kept_idx.numpy(), oki), (cfg.name, align)
+            for layer in range(cfg.n_layers):
+                dac.leank_plan_layer(kept_count[layer].tolist(), cfg.batch, cfg.n_q_heads,
+                                     cfg.n_kv_heads, cfg.head_dim, cfg.n_sink, cfg.window,
+                                     cfg.ctx + 1)
+
+
+def test_host_mask_matches_oracle_on_ties_and_signs():
+    import torch
+
+    rng = np.random.default_rng(102)
+    cases = [rng.integers(0, 5, size=(3, 5, 16)).astype(np.float32),
+             np.full((2, 2, 32), 0.5, dtype=np.float32),
+             rng.integers(0, 50, size=(2, 3, 1024)).astype(np.float32)]
+    signed = rng.standard_normal((4, 4, 64)).astype(np.float32)
+    signed[0, 0, :5] = [np.inf, -np.inf, 0.0, -0.0, 1e-45]
+    signed[1, 2, :3] = [-0.0, 0.0, -0.0]
+    cases.append(signed)
+    for alpha in cases:
+        for p in (0, 1, 33, 50, 70, 99, 100):
+            for align in (8, 16, 32):
+                if alpha.shape[2] % align:
+                    continue
+                mask, kc, ki = dac.leank_build_mask(torch.from_numpy(alpha), p, align)
+                om, okc, oki = oracle.build_mask(alpha, p, align)
+                assert np.array_equal(mask.numpy(), om) and np.array_equal(kc.numpy(), okc)
+                assert np.array_equal(ki.numpy(), oki), (alpha.shape, p, align)
+    nan = np.ones((1, 2, 128), dtype=np.float32)
+    nan[0, 1, 3] = np.nan
+    with pytest.raises(dac.LeankError) as err:
+        dac.leank_build_mask(torch.from_numpy(nan), 50, 32)
+    assert err.value.status == _lib.EINVAL
+
+
 def test_build_mask_rejected_before_launch():
     L = _lib.lib()
     p = ctypes.c_void_p(0x1000)
@@ -229,6 +283,9 @@ def test_build_mask_rejected_before_launch():
     assert L.leank_build_mask(p, 1, 2, 128, 50, 48, p, p, p, None) == _lib.EINVAL
     assert L.leank_build_mask(p, 1, 2, 128, 50, 0, p, p, p, None) == _lib.EINVAL
     assert L.leank_build_mask(p, 0, 2, 128, 50, 32, p, p, p, None) == _lib.EINVAL
+    for align in (1, 2, 4):   # divides head_dim, but not a multiple of the kept-count quantum
+        assert L.leank_build_mask(p, 1, 2, 128, 50, align, p, p, p, None) == _lib.EUNSUPPORTED
+        assert L.leank_build_mask_host(p, 1, 2, 128, 50, align, p, p, p) == _lib.EUNSUPPORTED
 
 
 def test_plan_layer_q_layout():
