@@ -21,9 +21,10 @@ namespace leank {
 //      complete yet are read from the bf16 staging rows as they are;
 //   V  codes of the 8-row blocks, turned into exact bf16 integers the same
 //      way for the B operand of the PV product.  The per-token scale
-//      multiplies the weight (p' = p * scale) and sum_t p_t * min'_t is
-//      added to every channel of the head at the end (min' = min, or
-//      min - 128 * scale for 4-bit codes).
+//      multiplies the weight (p' = p * scale) and sum_t p_t * min_t is
+//      added to every channel of the head at the end; for 4-bit codes so is
+//      -128 sum_t p'_t, with p'_t rounded as it entered the product, so the
+//      offset cancels exactly.
 
 // Pointers of one (batch row, live head) pair's low-bit middle: contiguous
 // streams, or one page per 64-row group through the block table.
@@ -325,7 +326,8 @@ __device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, int
 
 // Builds the group's query tables in this wavefront's LDS and returns the
 // offset term of quad qd's head i in bias[qd][i] (every lane): q' = q *
-// scale * qk_scale (hi + lo), min' = min (8-bit) or min - 128 scale.
+// scale * qk_scale (hi + lo); the offset is qk_scale sum_c q_c min_c, and
+// for 4-bit codes also -128 sum_c q'_c (q'_c as rounded in the table).
 template <int G, int NQ, int QB>
 __device__ __forceinline__ void build_group_tables(const f32x4_t& par16, int c,
                                                    const uint16_t* s_q, const int16_t* s_idx,
@@ -351,15 +353,26 @@ __device__ __forceinline__ void build_group_tables(const f32x4_t& par16, int c,
     tab[at] = __builtin_bit_cast(uint16_t, hi);
     tab[NQ * 4 * c + at] = __builtin_bit_cast(uint16_t, lo);
   }
-  // offset terms: lanes of a head sum its channels, then one lane each
+  // offset terms: lanes of a head sum its channels, then one lane each.
+  // sum_c q_c min_c (times the softmax scale), and for 4-bit codes, which
+  // enter the product as 128 + code, -128 sum_c q'_c with q'_c rounded as
+  // it entered the product (hi + lo), so that the 128 terms cancel
   constexpr int kLanes = 64 / (NQ * 4);  // lanes per head (16 or 8)
   const int h = lane / kLanes;
   const int part = lane - h * kLanes;
   float sum = 0.0f;
   if (h < G) {
     for (int j = part; j < c; j += kLanes) {
-      const float mn = QB == 4 ? fmaf(-128.0f, par[2 * j], par[2 * j + 1]) : par[2 * j + 1];
-      sum = fmaf(bf16_to_f32(s_q[h * LEANK_HEAD_DIM + (s_idx[j] & (LEANK_HEAD_DIM - 1))]), mn, sum);
+      const float qv = bf16_to_f32(s_q[h * LEANK_HEAD_DIM + (s_idx[j] & (LEANK_HEAD_DIM - 1))]);
+      if constexpr (QB == 4) {
+        const float x = qv * par[2 * j] * qk_scale;
+        const __bf16 hi = static_cast<__bf16>(x);
+        const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
+        sum = fmaf(qv * qk_scale, par[2 * j + 1], sum);
+        sum = fmaf(-128.0f, static_cast<float>(hi) + static_cast<float>(lo), sum);
+      } else {
+        sum = fmaf(qv, par[2 * j + 1], sum);
+      }
     }
   }
   sum += dpp_f32<kDppQuadXor1>(sum);
@@ -370,7 +383,8 @@ __device__ __forceinline__ void build_group_tables(const f32x4_t& par16, int c,
   for (int qd = 0; qd < NQ; ++qd) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      bias[qd][i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), (4 * qd + i) * kLanes)) * qk_scale;
+      bias[qd][i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sum), (4 * qd + i) * kLanes)) *
+                    (QB == 4 ? 1.0f : qk_scale);
   }
 }
 
@@ -459,8 +473,10 @@ __device__ __forceinline__ void attend_group(const GroupRegs<KB, QB>& gr, int c,
     }
   }
 
-  // weights, staged as bf16 hi / lo: w_lds[part][head][row]
-  const float vmin_row = QB == 4 ? fmaf(-128.0f, gr.vs, gr.vm) : gr.vm;
+  // weights, staged as bf16 hi / lo: w_lds[part][head][row].  4-bit codes
+  // enter the product as 128 + code; the offset is taken out with the weight
+  // as it enters the product (hi + lo), so that the two 128 terms cancel and
+  // only the weight's rounding times the code (at most 15) remains
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
 #pragma unroll
@@ -468,12 +484,14 @@ __device__ __forceinline__ void attend_group(const GroupRegs<KB, QB>& gr, int c,
       const float m_use = rs.m[qd][i] == -INFINITY ? 0.0f : rs.m[qd][i];
       const float pw = fast_exp2(s[qd][i] - m_use);
       rs.l[qd][i] += pw;
-      rs.vmin[qd][i] = fmaf(pw, vmin_row, rs.vmin[qd][i]);
+      const float pv = pw * gr.vs;
+      const __bf16 hi = static_cast<__bf16>(pv);
+      const __bf16 lo = static_cast<__bf16>(pv - static_cast<float>(hi));
+      const float in_product = static_cast<float>(hi) + static_cast<float>(lo);
+      rs.vmin[qd][i] = QB == 4 ? fmaf(-128.0f, in_product, fmaf(pw, gr.vm, rs.vmin[qd][i]))
+                               : fmaf(pw, gr.vm, rs.vmin[qd][i]);
       const int head = 4 * qd + i;
       if (head < G) {
-        const float pv = pw * gr.vs;
-        const __bf16 hi = static_cast<__bf16>(pv);
-        const __bf16 lo = static_cast<__bf16>(pv - static_cast<float>(hi));
         w_lds[head * 64 + lane] = __builtin_bit_cast(uint16_t, hi);
         w_lds[(16 + head) * 64 + lane] = __builtin_bit_cast(uint16_t, lo);
       }
@@ -537,9 +555,9 @@ __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&v
   }
 
   // per-token V scale folded into the weights; the minimum summed apart
-  float vmin_row[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) vmin_row[j] = QB == 4 ? fmaf(-128.0f, vs[j], vm[j]) : vm[j];
+  // (for 4-bit codes, which enter the product as 128 + code, with the
+  // offset taken out by the weight as it enters the product, hi + lo, so
+  // that the 128 terms cancel)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float m_use = st.m[i] == -INFINITY ? 0.0f : st.m[i];
@@ -550,7 +568,7 @@ __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&v
       const float pw = fast_exp2(s[j][i] - m_use);  // 0 for a dropped row
       st.l[i] += pw;
       const bool valid = !kTail || 2 * col + j < nvalid;
-      vmin[i] = valid ? fmaf(pw, vmin_row[j], vmin[i]) : vmin[i];
+      vmin[i] = valid ? fmaf(pw, vm[j], vmin[i]) : vmin[i];
       pv[j] = valid ? pw * vs[j] : 0.0f;
     }
     // rows 2 col, 2 col + 1 as one hi and one lo pair; every head's row is
@@ -558,6 +576,11 @@ __device__ __forceinline__ void softmax_pv_q(f32x4_t (&s)[2], const uint32_t (&v
     // recorded), so the stores need no branch
     uint32_t hi, lo;
     split_bf16x2(pv[0], pv[1], hi, lo);
+    if constexpr (QB == 4) {
+      const float in0 = __uint_as_float(hi << 16) + __uint_as_float(lo << 16);
+      const float in1 = __uint_as_float(hi & 0xffff0000u) + __uint_as_float(lo & 0xffff0000u);
+      vmin[i] = fmaf(-128.0f, in0 + in1, vmin[i]);
+    }
     reinterpret_cast<uint32_t*>(p_lds)[(head * kTileRows) / 2 + col] = hi;
     reinterpret_cast<uint32_t*>(p_lds)[((16 + head) * kTileRows) / 2 + col] = lo;
   }
