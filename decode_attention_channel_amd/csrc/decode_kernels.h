@@ -444,6 +444,17 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     // merge, and no other item of the call uses the rows written here.
     // Lane `lane` owns channels 2 lane, 2 lane + 1: their K words and the
     // 16-byte groups of the two V blocks, so no lane reads another's LDS.
+    //
+    // Invariant of the whole-block V stores below: each 8-row V block (and,
+    // 4-bit, each code byte shared by two rows) is written back with every
+    // row but the appended one unchanged -- exactly the bytes this item read
+    // in its prologue.  Other items of the call may read the same block at
+    // the same time (the last middle item reads the rows before the new
+    // middle row; a regular full-width item the ring rows around the
+    // slot); they read only rows whose bytes this store leaves as they
+    // were, and they mask the one row that changes.  So a block must
+    // belong to one (batch row, head) pair and one call must not append to
+    // it twice: distinct block-table pages and one step per call keep it so.
     const int e_ring = tok.slot % LEANK_V_BLOCK;
     const int e_mid = tok.mid_row % LEANK_V_BLOCK;
     if constexpr (QB != 0) {

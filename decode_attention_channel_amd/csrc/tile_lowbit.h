@@ -6,6 +6,10 @@
 
 namespace leank {
 
+// A paged low-bit middle holds one 64-row K group per page: the group
+// number indexes the block table.
+static_assert(LEANK_PAGE_ROWS == LEANK_QUANT_GROUP, "a page must hold exactly one K group");
+
 // ---------------------------------------------------------------- low-bit middle
 //
 // A middle item of a cache with low-bit streams reads, per 64-row group

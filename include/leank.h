@@ -185,7 +185,8 @@ int leank_build_mask_host(const float* alpha, int32_t n_layers, int32_t n_kv_hea
  * v_mid are unused (k_prun_bytes = v_mid_bytes = 0).  The caller maps a
  * page before rows are appended to it (for one token per step: whenever
  * r % 64 == 0); the kernels read the table on the device and do not check
- * it, so every entry that covers written rows must lie in [0, n_pages).
+ * it, so every entry that covers written rows must lie in [0, n_pages),
+ * and distinct entries (of any batch row) must name distinct pages.
  *
  * Paged low-bit middle (leank_plan_layer_paged_q): a page holds one 64-row
  * K group of every live head.  Within the page, at byte offsets: the K

@@ -192,3 +192,56 @@ def test_full_workload_steps_sampled(name):
     sel_k = np.stack([kh[b, h] for b, h in kv_pairs])[:, None]
     sel_v = np.stack([vh[b, h] for b, h in kv_pairs])[:, None]
     assert_cache_matches(cache, sel_k, sel_v, om[0], pairs=kv_pairs)
+
+
+@pytest.mark.parametrize("layout", ["bf16", "paged", "q4", "q8", "paged-q4"])
+def test_step_rewrites_shared_v_blocks_unchanged(layout):
+    """The step item writes back whole 8-row V blocks (4-bit: code bytes
+    that two rows share) while the last middle item reads the same block.
+    From a new middle row 3 into its block, across the next block edge, every
+    row of every pair stays bit-exact after every step, and the outputs
+    match the oracle."""
+    from tests.gpu_cases import assert_quant_cache_matches, shuffled_block_table
+
+    n_sink, window, batch, group = 8, 40, 4, 4
+    counts = [32, 0, 64, 128]
+    bits = 4 if "q4" in layout else 8 if "q8" in layout else 0
+    paged = layout.startswith("paged")
+    t0 = n_sink + window + 64 * 3 + 3   # the first step moves middle row 195 = 8 * 24 + 3
+    steps = 12
+    mask = mask_with_counts(np.random.default_rng(77), counts)
+    n_kv = len(counts)
+    max_ctx = t0 + steps + 1
+    kept_count = mask.sum(axis=1).astype(np.int32)
+    kept_idx = np.full((n_kv, 128), -1, dtype=np.int16)
+    for h in range(n_kv):
+        kept_idx[h, :kept_count[h]] = np.flatnonzero(mask[h])
+    extra = {}
+    if paged:
+        ppr = -(-(max_ctx - n_sink - window) // 64)
+        n_pages = batch * ppr + 2
+        extra = dict(n_pages=n_pages,
+                     block_table=shuffled_block_table(np.random.default_rng(5), batch, ppr, n_pages))
+    cache = dac.LayerCache(kept_count.tolist(), torch.from_numpy(kept_idx).to(DEV), batch,
+                           n_kv * group, n_kv, n_sink, window, max_ctx, device=DEV,
+                           quant_bits=bits, **extra)
+    gen = torch.Generator(device=DEV).manual_seed(78)
+    k = random_bf16((batch, n_kv, t0 + steps, 128), gen, scale=2.0)
+    v = random_bf16((batch, n_kv, t0 + steps, 128), gen)
+    q = random_bf16((steps, batch, n_kv * group, 128), gen)
+    kh, vh = bf16_bits(k), bf16_bits(v)
+    case("shared V blocks", layout)
+    dac.leank_pack_k(cache, k[:, :, :t0].contiguous(), v[:, :, :t0].contiguous())
+    for s in range(steps):
+        pos = t0 + s
+        out = dac.leank_decode_step(cache, q[s], k[:, :, pos].contiguous(), v[:, :, pos].contiguous())
+        torch.cuda.synchronize()
+        if bits:
+            assert_quant_cache_matches(cache, kh[:, :, :pos + 1], vh[:, :, :pos + 1], mask)
+            ref = oracle.decode_q(bf16_bits(q[s]), kh[:, :, :pos + 1], vh[:, :, :pos + 1], mask,
+                                  n_sink, window, bits)
+        else:
+            assert_cache_matches(cache, kh[:, :, :pos + 1], vh[:, :, :pos + 1], mask)
+            ref = oracle.decode(bf16_bits(q[s]), kh[:, :, :pos + 1], vh[:, :, :pos + 1], mask,
+                                n_sink, window)
+        assert_close(out.cpu().numpy(), ref, f"{layout} step {s}")
