@@ -34,6 +34,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# the most items per (batch row, KV head) pair the one-wavefront combine merges
+# (kWaveCombineItems in the decode kernels)
+WAVE_COMBINE_ITEMS = 32
 SHAPES = {
     "llama_b64_4k": "Llama-3.1-8B attention, one layer",
     "qwen_b16_32k": "Qwen2.5-7B attention, one layer",
@@ -56,8 +59,11 @@ def parse_args():
                          "0), is for profiling it alone with --skip-extras)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the main workload (no 0%% pruning, Qwen or CPU baseline)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target wall time for the oracle baseline sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the oracle's sample of the headline step (the "
+                         "other workloads' samples take fractions of it)")
+    ap.add_argument("--gen-steps", type=int, default=1024,
+                    help="decode steps of the 32-layer generation loop (the workload's 1024)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
     return ap.parse_args()
@@ -229,7 +235,7 @@ def workload(cfg, prune_override=None, copies=6, steps=200, warmup=20, fused=Tru
     return res
 
 
-def whole_model(cfg, steps=20, warmup=3):
+def whole_model(cfg, steps=20, warmup=3, prune_override=None):
     """All layers of a multi-layer workload per token: each layer has its own
     mask (one global threshold over every layer, as the mask is built),
     cache and query; a step is one leank_decode_step call per layer, in
@@ -242,7 +248,8 @@ def whole_model(cfg, steps=20, warmup=3):
 
     dev = torch.device("cuda:0")
     alpha = torch.from_numpy(alpha_for(cfg)).to(dev)
-    mask, kept_count, kept_idx = dac.leank_build_mask(alpha, cfg.prune_pct, cfg.align)
+    prune = cfg.prune_pct if prune_override is None else prune_override
+    mask, kept_count, kept_idx = dac.leank_build_mask(alpha, prune, cfg.align)
     counts_all = kept_count.cpu().tolist()
     max_ctx = cfg.ctx + steps + warmup + 2
     layers = []
@@ -296,52 +303,248 @@ def whole_model(cfg, steps=20, warmup=3):
     return res
 
 
-def cpu_baseline(cfg, target_seconds):
-    """The CPU oracle on the same workload's decode step, on host cores.
-
-    Samples whole batch rows (all query heads of a row, full context),
-    cycling through the batch until about `target_seconds` of wall time have
-    passed, and scales the mean wall time per row to the full batch.
-    """
+def generation_loop(cfg, n_steps, prune_override=None, fused=True):
+    """The 32-layer generation loop: every layer's cache prefilled with the
+    workload's context, then n_steps decode steps in order, each appending
+    one token per batch row to every layer and attending.  fused: one
+    leank_decode_step per layer, in layer order.  Unfused: every layer's
+    leank_pack_k, then every layer's leank_decode_attn, with HIP events
+    around the two halves of each step (three events per step, so the split
+    costs next to nothing).  Layers are independent of each other's output
+    here, as the inputs are synthetic.  Returns per-step times and the
+    attention's algorithmic bytes per step (every layer at its context)."""
     import numpy as np
     import torch
 
-    import oracle
-    from synthetic import alpha_for, bf16_bits, make_kv, make_q
+    import decode_attention_channel_amd as dac
+    from synthetic import alpha_for, make_kv, make_q, make_step_kv
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
     dev = torch.device("cuda:0")
-    alpha = alpha_for(cfg)
-    om, _, _ = oracle.build_mask(alpha, cfg.prune_pct, cfg.align)
-    k, v = make_kv(cfg, 0, device=dev)
-    q = make_q(cfg, 0, device=dev)
-    kh, vh, qh = bf16_bits(k), bf16_bits(v), bf16_bits(q)
-    del k, v
-    per_row = []
-    t_all = time.perf_counter()
-    n = 0
-    while time.perf_counter() - t_all < target_seconds:
-        b = n % cfg.batch
-        t0 = time.perf_counter()
-        oracle.decode(qh[b:b + 1], kh[b:b + 1], vh[b:b + 1], om[0], cfg.n_sink, cfg.window)
-        per_row.append(time.perf_counter() - t0)
-        n += 1
-    us_per_step = float(np.mean(per_row)) * cfg.batch * 1e6
-    return {
-        "value": us_per_step,
-        "unit": "us/step",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": (f"{n} batch-row decodes of the {cfg.name} step ({n / cfg.batch:.1f} passes over "
-                   f"the {cfg.batch} rows; each row = all {cfg.n_q_heads} query heads over the "
-                   f"{cfg.ctx}-token cache), float64 numpy, mean per row x {cfg.batch}; "
-                   f"{sum(per_row):.1f} s wall time on {int(threads)} threads"),
+    alpha = torch.from_numpy(alpha_for(cfg)).to(dev)
+    prune = cfg.prune_pct if prune_override is None else prune_override
+    _, kept_count, kept_idx = dac.leank_build_mask(alpha, prune, cfg.align)
+    counts_all = kept_count.cpu().tolist()
+    max_ctx = cfg.ctx + n_steps + 2
+    layers = []
+    for layer in range(cfg.n_layers):
+        cache = dac.LayerCache(counts_all[layer], kept_idx[layer].contiguous(), cfg.batch,
+                               cfg.n_q_heads, cfg.n_kv_heads, cfg.n_sink, cfg.window, max_ctx)
+        k, v = make_kv(cfg, layer, device=dev)
+        dac.leank_pack_k(cache, k, v)
+        del k, v
+        cache.workspace()
+        new = [make_step_kv(cfg, layer, s, device=dev) for s in range(4)]
+        out = torch.empty((cfg.batch, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32, device=dev)
+        layers.append((cache, make_q(cfg, layer, device=dev), new, out))
+    torch.cuda.synchronize()
+    ctx0 = layers[0][0].length
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    split = []
+    t0.record(stream)
+    for s in range(n_steps):
+        if fused:
+            for cache, q, new, out in layers:
+                dac.leank_decode_step(cache, q, new[s % 4][0], new[s % 4][1], out=out)
+        else:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record(stream)
+            for cache, q, new, out in layers:
+                dac.leank_pack_k(cache, new[s % 4][0], new[s % 4][1])
+            ev[1].record(stream)
+            for cache, q, new, out in layers:
+                dac.leank_decode_attn(cache, q, out=out)
+            ev[2].record(stream)
+            split.append(ev)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / n_steps
+    byt = float(np.mean([sum(dac.leank_decode_bytes(cache, ctx0 + s + 1) for cache, _, _, _ in layers)
+                         for s in range(n_steps)]))
+    res = {
+        "ms_per_step": ms,
+        "decode_bytes_per_step": byt,
+        "achieved_GBps": byt / (ms * 1e-3) / 1e9,
+        "frac_of_peak": byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "floor_ms_at_peak": byt / (HBM_PEAK_GBPS * 1e9) * 1e3,
+        "layers": cfg.n_layers,
+        "batch": cfg.batch,
+        "steps_timed": n_steps,
+        "ctx_range_timed": [ctx0 + 1, ctx0 + n_steps],
+        "live_kv_heads": sum(1 for row in counts_all for c in row if c > 0),
+        "kv_heads": cfg.n_layers * cfg.n_kv_heads,
+        "step": "leank_decode_step per layer (fused)" if fused else
+                "leank_pack_k per layer, then leank_decode_attn per layer",
     }
+    if split:
+        res["pack_ms_per_step"] = float(np.mean([e[0].elapsed_time(e[1]) for e in split]))
+        res["decode_ms_per_step"] = float(np.mean([e[1].elapsed_time(e[2]) for e in split]))
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_threads():
+    """Threads for the CPU oracle: the cores this process may run on (its
+    affinity), capped by OMP_NUM_THREADS when set; BLAS is pinned to that.
+    Returns (threads, os.cpu_count(), affinity size)."""
+    n_cpu = os.cpu_count() or 1
+    try:
+        n_aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n_aff = n_cpu
+    n = n_aff
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n, n_cpu, n_aff
+
+
+def oracle_units(q_bits, k_bits, v_bits, mask, n_sink, window, target_seconds, seed=0):
+    """The CPU oracle on one layer's decode, one (batch row, KV head) unit at
+    a time in a seeded random order, until about target_seconds have passed
+    (at least one unit).  Each unit's bf16 -> float64 widening and its
+    attention (oracle.decode_f64) are timed apart.  Returns (seconds of
+    attention per full layer, seconds of widening per full layer, units
+    timed, units in the layer): the means over the units timed times the
+    units in the layer (a uniform random sample, so unbiased)."""
+    import numpy as np
+
+    import oracle
+
+    batch, n_q, _ = q_bits.shape
+    n_kv = k_bits.shape[1]
+    group = n_q // n_kv
+    order = np.random.default_rng(seed).permutation(batch * n_kv)
+    widen, attend = [], []
+    t_all = time.perf_counter()
+    for n in order:
+        b, h = divmod(int(n), n_kv)
+        t0 = time.perf_counter()
+        qw = oracle.bf16_bits_to_f64(q_bits[b:b + 1, h * group:(h + 1) * group])
+        kw = oracle.bf16_bits_to_f64(k_bits[b:b + 1, h:h + 1])
+        vw = oracle.bf16_bits_to_f64(v_bits[b:b + 1, h:h + 1])
+        t1 = time.perf_counter()
+        oracle.decode_f64(qw, kw, vw, mask[h:h + 1], n_sink, window)
+        t2 = time.perf_counter()
+        widen.append(t1 - t0)
+        attend.append(t2 - t1)
+        if time.perf_counter() - t_all >= target_seconds:
+            break
+    units = batch * n_kv
+    return float(np.mean(attend)) * units, float(np.mean(widen)) * units, len(attend), units
+
+
+def _layer_bits(cfg, layer, n_tokens=None):
+    """Host bf16 bits of one layer's synthetic q, K, V (generated on the GPU
+    from the same seeds as the GPU workload) and its oracle mask row."""
+    import torch
+
+    from synthetic import bf16_bits, make_kv, make_q
+
+    dev = torch.device("cuda:0")
+    k, v = make_kv(cfg, layer, n_tokens=n_tokens, device=dev)
+    q = make_q(cfg, layer, device=dev)
+    out = bf16_bits(q), bf16_bits(k), bf16_bits(v)
+    del k, v
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baselines(target_seconds):
+    """The CPU oracle (plain float64 numpy, as it stands) on the host's cores,
+    on bounded samples of the benchmark workloads.  The first entry is the
+    headline's (the Llama-3.1-8B-shaped batch-64 4K step); the others are
+    the Qwen2.5-7B-shaped batch-16 32K step, the 128K-token batch-1 model
+    (per layer and per token) and the 32-layer generation loop (per step)."""
+    import oracle
+    from synthetic import alpha_for, get_config
+
+    import contextlib
+
+    threads, n_cpu, n_aff = cpu_threads()
+    try:
+        from threadpoolctl import threadpool_limits
+
+        limiter = threadpool_limits(limits=threads)
+    except ImportError:  # pragma: no cover
+        limiter = contextlib.nullcontext()
+    where = {"cores": threads, "host_cpus": n_cpu, "affinity_cpus": n_aff,
+             "blas_threads": threads}
+    res = {}
+    with limiter:
+        # headline: one layer step of the Llama workload
+        cfg = get_config("llama_b64_4k")
+        mask, _, _ = oracle.build_mask(alpha_for(cfg), cfg.prune_pct, cfg.align)
+        qb, kb, vb = _layer_bits(cfg, 0)
+        att, wid, n, units = oracle_units(qb, kb, vb, mask[0], cfg.n_sink, cfg.window,
+                                          target_seconds)
+        res["headline"] = dict(
+            value=att * 1e6, unit="us/step", kind="oracle", **where,
+            widening_us_per_step=wid * 1e6,
+            sample=(f"{n} of the {units} (batch row, KV head) units of the {cfg.name} decode "
+                    f"step (context {cfg.ctx}), in seeded random order, float64 attention "
+                    f"(oracle.decode_f64) timed apart from the bf16 -> float64 widening; the "
+                    f"mean per unit times {units}; {threads} BLAS threads"))
+        del qb, kb, vb
+        # Qwen2.5-7B-shaped step
+        cfg = get_config("qwen_b16_32k")
+        mask, _, _ = oracle.build_mask(alpha_for(cfg), cfg.prune_pct, cfg.align)
+        qb, kb, vb = _layer_bits(cfg, 0)
+        att, wid, n, units = oracle_units(qb, kb, vb, mask[0], cfg.n_sink, cfg.window,
+                                          0.6 * target_seconds, seed=1)
+        res["qwen_b16_32k"] = dict(value=att * 1e6, unit="us/step", widening_us_per_step=wid * 1e6,
+                                   units_timed=n, units=units, **where)
+        del qb, kb, vb
+        # 128K-token batch-1 model: layers 0 and 1 timed, the token from
+        # their per-head means (every live head of this model keeps the
+        # same number of channels, so a head costs the same in every layer)
+        cfg = get_config("llama32_b1_128k")
+        mask, kept_count, _ = oracle.build_mask(alpha_for(cfg), cfg.prune_pct, cfg.align)
+        live_t, dead_t, layers_us = [], [], []
+        for layer in (0, 1):
+            qb, kb, vb = _layer_bits(cfg, layer)
+            for h in range(cfg.n_kv_heads):
+                g = cfg.group
+                t0 = time.perf_counter()
+                qw = oracle.bf16_bits_to_f64(qb[:, h * g:(h + 1) * g])
+                kw = oracle.bf16_bits_to_f64(kb[:, h:h + 1])
+                vw = oracle.bf16_bits_to_f64(vb[:, h:h + 1])
+                t1 = time.perf_counter()
+                oracle.decode_f64(qw, kw, vw, mask[layer, h:h + 1], cfg.n_sink, cfg.window)
+                t2 = time.perf_counter()
+                (live_t if kept_count[layer, h] > 0 else dead_t).append(t2 - t1)
+            del qb, kb, vb
+        n_live = int((kept_count > 0).sum())
+        n_dead = kept_count.size - n_live
+        live_mean = sum(live_t) / len(live_t)
+        dead_mean = sum(dead_t) / len(dead_t)
+        layer0 = live_mean * int((kept_count[0] > 0).sum()) + dead_mean * int((kept_count[0] == 0).sum())
+        res["llama32_b1_128k"] = dict(
+            layer0_us=layer0 * 1e6, token_us=(live_mean * n_live + dead_mean * n_dead) * 1e6,
+            unit="us", live_head_us=live_mean * 1e6, dead_head_us=dead_mean * 1e6, **where,
+            sample=(f"every KV head of layers 0 and 1 at context {cfg.ctx} ({len(live_t)} live, "
+                    f"{len(dead_t)} fully pruned), float64 attention only; the token as "
+                    f"{n_live} live + {n_dead} fully pruned heads at those means"))
+        # generation loop: layers 0 and 31 at the first and the last step
+        cfg = get_config("llama32_b64_gen")
+        mask, kept_count, _ = oracle.build_mask(alpha_for(cfg), cfg.prune_pct, cfg.align)
+        per_layer = []
+        for ctx in (cfg.ctx + 1, cfg.ctx + cfg.decode_steps):
+            for layer in (0, cfg.n_layers - 1):
+                qb, kb, vb = _layer_bits(cfg, layer, n_tokens=ctx)
+                att, _, n, units = oracle_units(qb, kb, vb, mask[layer], cfg.n_sink, cfg.window,
+                                                0.15 * target_seconds, seed=2 + layer)
+                per_layer.append(att)
+                del qb, kb, vb
+        step = sum(per_layer) / len(per_layer) * cfg.n_layers
+        res["llama32_b64_gen"] = dict(
+            ms_per_step=step * 1e3, unit="ms/step", **where,
+            sample=(f"layers 0 and {cfg.n_layers - 1} at contexts {cfg.ctx + 1} and "
+                    f"{cfg.ctx + cfg.decode_steps}, sampled (batch row, KV head) units of each; the "
+                    f"step as {cfg.n_layers} layers at their mean"))
+    return res
 
 
 def copy_calibration():
@@ -444,6 +647,11 @@ def main():
         long_cfg = get_config("llama32_b1_128k")
         long_ctx = workload(long_cfg, copies=args.copies, steps=args.steps, warmup=args.warmup)
         long_model = whole_model(long_cfg)
+        long_model_dense = whole_model(long_cfg, prune_override=0)
+        gen_cfg = get_config("llama32_b64_gen")
+        gen = generation_loop(gen_cfg, args.gen_steps)
+        gen_unfused = generation_loop(gen_cfg, args.gen_steps, fused=False)
+        gen_dense = generation_loop(gen_cfg, args.gen_steps, prune_override=0)
         extras = {
             "unfused_pack_then_decode": unfused,
             "lowbit_middle_8bit": q8,
@@ -458,12 +666,21 @@ def main():
             "qwen_speedup_vs_0pct_step": qwen_dense["us_per_step"] / qwen["us_per_step"],
             "llama_b1_128k_layer0": long_ctx,
             "llama_b1_128k_all_32_layers": long_model,
+            "llama_b1_128k_all_32_layers_dense_0pct": long_model_dense,
+            "llama_b1_128k_speedup_vs_0pct_token": (long_model_dense["us_per_token"]
+                                                     / long_model["us_per_token"]),
+            "llama32_b64_generation_loop": gen,
+            "llama32_b64_generation_loop_unfused": gen_unfused,
+            "llama32_b64_generation_loop_dense_0pct": gen_dense,
+            "generation_speedup_vs_0pct_step": gen_dense["ms_per_step"] / gen["ms_per_step"],
         }
     if args.copy_calibration:
         extras["copy_calibration"] = copy_calibration()
     cpu = None
     if not args.skip_extras:
-        cpu = cpu_baseline(cfg, args.cpu_seconds)
+        cpu_all = cpu_baselines(args.cpu_seconds)
+        cpu = cpu_all.pop("headline")
+        extras["cpu_oracle_other_workloads"] = cpu_all
 
     line = {
         "metric": METRIC,
@@ -497,8 +714,8 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": (f"leank_decode_step = decode_split_kernel<{cfg.group}> + its combine "
-                       f"(decode_combine_wave_kernel<{cfg.group}> up to 16 items per pair, "
-                       f"else decode_combine_kernel<{cfg.group}>); "
+                       f"(decode_combine_wave_kernel<{cfg.group}> up to {WAVE_COMBINE_ITEMS} "
+                       f"items per pair, else decode_combine_kernel<{cfg.group}>); "
                        "one launch pair per step, averaged over the timed steps"),
             "achieved": main_res["achieved_GBps"],
             "peak": HBM_PEAK_GBPS,

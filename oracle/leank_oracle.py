@@ -79,6 +79,7 @@ __all__ = [
     "ring_slot",
     "pack_reference",
     "decode",
+    "decode_f64",
     "QUANT_GROUP",
     "quantize_asym",
     "dequantize",
@@ -298,6 +299,22 @@ def decode(q_bits, k_bits, v_bits, mask, n_sink, window, scale=None, pairs=None)
                    lambda b, h, rows: bf16_bits_to_f64(v_bits[b, h, rows]),
                    mask, n_sink, window, scale, pairs)
 
+
+
+def decode_f64(q, k, v, mask, n_sink, window, scale=None, pairs=None):
+    """decode() on values already widened to float64 (q [B, Hq, d], k, v
+    [B, H, T, d]), the same definition step for step; lets a caller time the
+    widening of the bf16 inputs apart from the attention itself."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    batch, n_q_heads, d = q.shape
+    _, n_heads, ctx_len, _ = k.shape
+    return _attend((batch, n_q_heads, n_heads, ctx_len, d),
+                   lambda b, j: q[b, j],
+                   lambda b, h, rows: k[b, h, rows],
+                   lambda b, h, rows: v[b, h, rows],
+                   mask, n_sink, window, scale, pairs)
 
 # ---------------------------------------------------------------------------
 # low-bit middle streams (LeanK page, section 4.2; white paper section 5.2.1)

@@ -345,6 +345,10 @@ def pin_decode_masked_matches_sdpa(O):
             got = O.decode(q, k, v, mask, n_sink, window)
             expect = _reference_masked(q, k, v, mask, n_sink, window)
             np.testing.assert_allclose(got, expect, rtol=1e-10, atol=1e-12)
+            # the entry point on values already widened to float64
+            wide = O.decode_f64(_bits_to_f64(q).numpy(), _bits_to_f64(k).numpy(),
+                                _bits_to_f64(v).numpy(), mask, n_sink, window)
+            np.testing.assert_allclose(wide, expect, rtol=1e-10, atol=1e-12)
             # sampled-pairs entry point returns the same rows
             pairs = [(batch - 1, n_q - 1), (0, 0)]
             sampled = O.decode(q, k, v, mask, n_sink, window, pairs=pairs)

@@ -28,3 +28,35 @@ def test_other_workload_needs_skip_extras():
 def test_unknown_workload_is_refused():
     r = _run("--workload", "no_such_workload")
     assert r.returncode == 2
+
+
+def test_wave_combine_label_matches_the_kernels():
+    import re
+
+    sys.path.insert(0, ROOT)
+    import bench
+
+    text = open(os.path.join(ROOT, "decode_attention_channel_amd", "csrc", "decode_base.h")).read()
+    assert int(re.search(r"#define LEANK_WAVE_COMBINE_ITEMS (\d+)", text).group(1)) == \
+        bench.WAVE_COMBINE_ITEMS
+
+
+def test_oracle_sampler_on_host_arrays():
+    """The CPU baseline's sampler: seeded random (batch row, KV head) units,
+    widening timed apart, scaled to the whole layer."""
+    import numpy as np
+
+    sys.path.insert(0, ROOT)
+    import bench
+
+    rng = np.random.default_rng(3)
+    q = rng.integers(0, 1 << 15, size=(2, 4, 128)).astype(np.uint16) & 0x3FFF
+    k = rng.integers(0, 1 << 15, size=(2, 2, 40, 128)).astype(np.uint16) & 0x3FFF
+    mask = np.ones((2, 128), dtype=np.uint8)
+    mask[1] = 0
+    attend, widen, n, units = bench.oracle_units(q, k, k, mask, 4, 8, target_seconds=0.0)
+    assert n == 1 and units == 4 and attend > 0 and widen > 0
+    attend, widen, n, units = bench.oracle_units(q, k, k, mask, 4, 8, target_seconds=60.0)
+    assert n == units == 4
+    threads, n_cpu, n_aff = bench.cpu_threads()
+    assert 1 <= threads <= n_aff <= n_cpu

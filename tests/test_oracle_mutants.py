@@ -107,6 +107,9 @@ MUTANTS = [
     ("low-bit pack pairs every head's K with the first live head's V",
      "mid_q.append([quantize_middle(kp[b], ref[\"v_mid\"][head][b], bits, group)",
      "mid_q.append([quantize_middle(kp[b], [m for m in ref[\"v_mid\"] if m is not None][0][b], bits, group)"),
+    ("widened entry point reads the first head's values",
+     "lambda b, h, rows: v[b, h, rows],",
+     "lambda b, h, rows: v[b, 0, rows],"),
     ("open K group left out of the byte count",
      "k = n_groups * group * c * bits // 8 + n_groups * c * 8 + n_stage * c * 2",
      "k = n_groups * group * c * bits // 8 + n_groups * c * 8"),
