@@ -47,6 +47,9 @@ namespace {
 #ifndef LEANK_ONE_ROUND
 #define LEANK_ONE_ROUND 1
 #endif
+#ifndef LEANK_BALANCE_ROUND
+#define LEANK_BALANCE_ROUND 1
+#endif
 
 constexpr int64_t kTargetCUs = 256;  // compute units of an MI355X
 constexpr int64_t kRoundPerCU = 3;   // split-kernel workgroups resident per compute unit
@@ -115,6 +118,80 @@ int64_t items_for_target(const leank_layer_cache* c, int32_t t_sl, int32_t t_mid
     per_b += n;
   }
   return per_b * c->batch;
+}
+
+// Balanced one round: `n_items` items (a multiple of the compute units)
+// over the segments of one batch row -- the full-width rows of each of the
+// n_kv heads (one shared item count) and the middle of each live head --
+// with nearly equal bytes per item.  Each segment takes its share of the
+// items by largest remainder, at most `cap` items and at least one; the
+// result is written to the plan fields.  Returns false (plan untouched)
+// when the row's items cannot be placed.
+bool balance_round(const leank_layer_cache* c, int32_t t_sl, int32_t t_mid, int step,
+                   int64_t per_b, const int32_t* cap_mid, int32_t cap_sl, WorkPlan* w) {
+  const int H = c->n_kv_heads;
+  const double fw_bytes = static_cast<double>(t_sl) * 4 * LEANK_HEAD_DIM;
+  double mid_bytes[LEANK_MAX_KV_HEADS] = {0};
+  double total = fw_bytes * H;
+  for (int h = 0; h < H; ++h)
+    if (c->kept_count[h] > 0) {
+      mid_bytes[h] = static_cast<double>(t_mid) * middle_row_cost(c, c->kept_count[h]);
+      total += mid_bytes[h];
+    }
+  if (total <= 0) return false;
+  const double per_item = total / static_cast<double>(per_b);
+  const int32_t sl_min = (t_sl > 0 || step) ? 1 : 0;
+  int32_t n_sl = t_sl > 0 ? static_cast<int32_t>(std::llround(fw_bytes / per_item)) : 0;
+  n_sl = std::min(std::max(n_sl, sl_min), std::max(cap_sl, sl_min));
+  int32_t n_mid[LEANK_MAX_KV_HEADS] = {0};
+  int64_t sum = static_cast<int64_t>(H) * n_sl;
+  for (int h = 0; h < H; ++h)
+    if (mid_bytes[h] > 0 && t_mid > 0) {
+      n_mid[h] = std::min(std::max<int32_t>(1, static_cast<int32_t>(std::llround(mid_bytes[h] / per_item))),
+                          std::max(cap_mid[h], 1));
+      sum += n_mid[h];
+    }
+  // largest remainder: take items from the segment with the smallest items,
+  // give them to the one with the largest, until the row holds per_b
+  for (int it = 0; it < 4 * LEANK_MAX_KV_HEADS * 64 && sum != per_b; ++it) {
+    int best = -2;  // -1: the full-width segments, h: head h's middle
+    double best_size = sum > per_b ? 1e300 : -1.0;
+    if (n_sl > 0) {
+      const double size = fw_bytes / n_sl;
+      const bool ok = sum > per_b ? (n_sl > sl_min && sum - H >= per_b - H) : (n_sl < cap_sl && sum + H <= per_b);
+      if (ok && (sum > per_b ? size < best_size : size > best_size)) best = -1, best_size = size;
+    }
+    for (int h = 0; h < H; ++h) {
+      if (n_mid[h] == 0) continue;
+      const double size = mid_bytes[h] / n_mid[h];
+      const bool ok = sum > per_b ? n_mid[h] > 1 : n_mid[h] < cap_mid[h];
+      if (ok && (sum > per_b ? size < best_size : size > best_size)) best = h, best_size = size;
+    }
+    if (best == -2) break;
+    const int d = sum > per_b ? -1 : 1;
+    if (best == -1) {
+      n_sl += d;
+      sum += d * H;
+    } else {
+      n_mid[best] += d;
+      sum += d;
+    }
+  }
+  if (sum > per_b) return false;
+  auto rows_for = [](int32_t rows, int32_t n, int32_t* n_out, int32_t* rows_out) {
+    if (rows <= 0 || n <= 0) {
+      *n_out = n > 0 ? n : 0;
+      *rows_out = 0;
+      return;
+    }
+    const int64_t per = ceil_div(ceil_div(rows, n), kRowQuantum) * kRowQuantum;
+    *rows_out = static_cast<int32_t>(per);
+    *n_out = static_cast<int32_t>(ceil_div(rows, per));
+  };
+  rows_for(t_sl, n_sl, &w->n_sl_items, &w->sl_rows);
+  if (step && w->n_sl_items == 0) w->n_sl_items = 1;
+  for (int h = 0; h < H; ++h) rows_for(t_mid, n_mid[h], &w->n_mid[h], &w->mid_rows[h]);
+  return true;
 }
 
 }  // namespace
@@ -259,19 +336,43 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPl
     w->n_sl_items = 1;
     bound_per_b += c->n_kv_heads;
   }
-  int32_t base = 0;
+  const int32_t cap_sl = static_cast<int32_t>(b);  // full-width items at the smallest size
+  int32_t cap_mid[LEANK_MAX_KV_HEADS] = {0};
+  int64_t items = static_cast<int64_t>(w->n_sl_items) * c->n_kv_heads;
   for (int h = 0; h < c->n_kv_heads; ++h) {
-    w->head_base[h] = base;
     const int kept = c->kept_count[h];
     if (kept > 0) {
       const int64_t row_bytes = middle_row_cost(c, kept);
       split_rows(w->t_mid, row_target(row_bytes, kItemBytesMin), &n32, &rows32, &b);
       bound_per_b += b;
+      cap_mid[h] = static_cast<int32_t>(b);
       int64_t rows = row_target(row_bytes, target);
       // a paged item reads its page list from LDS: at most 64 pages
       if (c->page_rows) rows = std::min<int64_t>(rows, 64 * LEANK_PAGE_ROWS);
       split_rows(w->t_mid, rows, &w->n_mid[h], &w->mid_rows[h], &unused_n);
+      items += w->n_mid[h];
     }
+  }
+  items *= c->batch;
+  // Balanced round: the compute units share HBM bandwidth per unit, so a
+  // unit running three workgroups of a round serves each more slowly than
+  // one running two, and a round ends when its most loaded unit does.  A
+  // bf16 call of one round with at least 2 * kItemBytesMin bytes per unit
+  // makes exactly 2 or 3 items per unit (as many as keep items at or above
+  // kItemBytesMin), of nearly equal bytes.  Measured (MI355X): the
+  // Qwen2.5-7B-shaped batch-16 32K step 93.0 -> 89.9 us (688 -> 768 items);
+  // one item per unit was slower (the 128K-token layer with one live head:
+  // 20.9 -> 23.1 us with 256 items instead of 475).  Paged middles keep the
+  // plan above (an item's pages are capped).
+  const int64_t units_items = stream_bytes / (kTargetCUs * kItemBytesMin);
+  if (LEANK_BALANCE_ROUND && c->quant_bits == 0 && !c->page_rows &&
+      items <= kTargetCUs * kRoundPerCU && units_items >= 2) {
+    const int64_t per_b = kTargetCUs * std::min<int64_t>(kRoundPerCU, units_items) / c->batch;
+    if (per_b >= 1) balance_round(c, w->t_sl, w->t_mid, step, per_b, cap_mid, cap_sl, w);
+  }
+  int32_t base = 0;
+  for (int h = 0; h < c->n_kv_heads; ++h) {
+    w->head_base[h] = base;
     base += w->n_sl_items + w->n_mid[h];
   }
   (void)unused_rows;
