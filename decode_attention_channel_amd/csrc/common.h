@@ -46,8 +46,12 @@ struct WorkPlan {
   int32_t t_mid;          // middle rows: max(0, ctx - n_sink - window)
   int32_t n_sl_items;
   int32_t sl_rows;        // rows per full-width item
-  int32_t n_mid[LEANK_MAX_KV_HEADS];
-  int32_t mid_rows[LEANK_MAX_KV_HEADS];
+  int32_t n_mid[LEANK_MAX_KV_HEADS];       // middle items of head h (bulk + tail)
+  int32_t mid_rows[LEANK_MAX_KV_HEADS];    // rows per bulk middle item
+  int32_t n_mid_b[LEANK_MAX_KV_HEADS];     // bulk middle items (the first ones)
+  int32_t mid_rows_t[LEANK_MAX_KV_HEADS];  // rows per tail middle item
+  int32_t bulk_per_b;     // items of a batch row dispatched first (full-width + bulk middle)
+  int32_t tail_per_b;     // items of a batch row dispatched after every bulk item
   int32_t step;           // 1 for a fused decode step
   int32_t head_base[LEANK_MAX_KV_HEADS + 1];  // first item of head h within a batch row
   int32_t items_per_b;

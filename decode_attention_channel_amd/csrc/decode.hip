@@ -208,6 +208,9 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   p.n_sl_items = w.n_sl_items;
   p.sl_rows = w.sl_rows;
   p.items_per_b = w.items_per_b;
+  p.bulk_per_b = w.bulk_per_b;
+  p.tail_per_b = w.tail_per_b;
+  p.n_bulk = static_cast<int64_t>(w.bulk_per_b) * c->batch;
   p.partial_stride = w.partial_stride;
   // pairs with many items get their channels split over several combine workgroups
   int32_t max_items = 0;
@@ -254,6 +257,8 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
     p.heads[h].n_mid = w.n_mid[h];
     p.heads[h].mid_rows = w.mid_rows[h];
     p.heads[h].base = w.head_base[h];
+    p.heads[h].n_mid_b = w.n_mid_b[h];
+    p.heads[h].mid_rows_t = w.mid_rows_t[h];
     if (quant && p.paged && c->kept_count[h] > 0) {
       p.heads[h].pq_k_codes = static_cast<int32_t>(c->k_q_off[h]);
       p.heads[h].pq_k_par = static_cast<int32_t>(4 * c->k_qp_off[h]);

@@ -38,9 +38,11 @@ struct DecodeHead {
   int64_t k_off;   // elements of K_prun, -1 for a dead head (low-bit: kept channels of the live heads before it)
   int64_t v_off;   // elements of V_mid, -1 for a dead head (low-bit: its rank among the live heads)
   int32_t kept;
-  int32_t n_mid;     // middle items of this head per batch row
-  int32_t mid_rows;  // rows per middle item
+  int32_t n_mid;     // middle items of this head per batch row (bulk + tail)
+  int32_t mid_rows;  // rows per bulk middle item
   int32_t base;      // first item of this head within a batch row
+  int32_t n_mid_b;     // bulk middle items (chunks [0, n_mid_b)); the rest are tail items
+  int32_t mid_rows_t;  // rows per tail middle item
   // paged low-bit middle: byte offsets of the head's K codes, K pairs, V
   // codes and V parameters within a page
   int32_t pq_k_codes, pq_k_par, pq_v_codes, pq_v_par;
@@ -97,8 +99,15 @@ struct DecodeParams {
   int64_t page_elems;
   int32_t pages_per_row;
   int32_t wave_items;  // one-wavefront combine: the most items of any pair
+  // dispatch order: every batch row's bulk items (its full-width and bulk
+  // middle items, head by head), then every batch row's tail items
+  int32_t bulk_per_b;
+  int32_t tail_per_b;
+  int64_t n_bulk;  // batch * bulk_per_b
   DecodeHead heads[LEANK_MAX_KV_HEADS];
 };
+// kernel arguments are limited to 4 KiB
+static_assert(sizeof(DecodeParams) <= 4096, "decode launch parameters exceed the kernel argument limit");
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

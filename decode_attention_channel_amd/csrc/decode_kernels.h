@@ -66,6 +66,21 @@
 
 namespace leank {
 
+// Rows [r0, r1) of middle chunk `chunk` of a head (t_mid middle rows in the
+// batch row): bulk chunks [0, n_mid_b) of mid_rows rows, then tail chunks of
+// mid_rows_t rows.
+__device__ __forceinline__ void mid_chunk_rows(const DecodeHead& hd, int chunk, int t_mid, int& r0,
+                                               int& r1) {
+  if (chunk < hd.n_mid_b) {
+    r0 = chunk * hd.mid_rows;
+    r1 = r0 + hd.mid_rows;
+  } else {
+    r0 = hd.n_mid_b * hd.mid_rows + (chunk - hd.n_mid_b) * hd.mid_rows_t;
+    r1 = r0 + hd.mid_rows_t;
+  }
+  r1 = min(t_mid, r1);
+}
+
 // Middle rows of item `chunk_id` of head hd in batch row b (t_mid middle
 // rows in this row) of a low-bit stream: the head's kept channels select
 // the tile width (bf16 middles: attend_middle_staged).
@@ -74,8 +89,8 @@ __device__ __forceinline__ void attend_middle(const DecodeParams& p, const Decod
                                               int chunk_id, int t_mid, const uint16_t* s_q,
                                               const int16_t* s_idx, const int32_t* s_pages,
                                               uint16_t* p_lds, WaveState& st, float (&vmin)[4]) {
-  const int r0 = chunk_id * hd.mid_rows;
-  const int r1 = min(t_mid, r0 + hd.mid_rows);
+  int r0, r1;
+  mid_chunk_rows(hd, chunk_id, t_mid, r0, r1);
   const int c = hd.kept;
   if constexpr (QB != 0) {
     const QSegment q = q_segment<QB>(p, hd, b, t_mid);
@@ -113,8 +128,8 @@ __device__ __forceinline__ void attend_middle_staged(const DecodeParams& p, cons
                                                      const uint16_t* s_q, const int16_t* s_idx,
                                                      const int32_t* s_pages, uint16_t* p_lds,
                                                      WaveState& st) {
-  const int r0 = chunk_id * hd.mid_rows;
-  const int r1 = min(t_mid, r0 + hd.mid_rows);
+  int r0, r1;
+  mid_chunk_rows(hd, chunk_id, t_mid, r0, r1);
   const int c = hd.kept;
   if (p.paged) {
     const int32_t* g_pages =
@@ -183,13 +198,32 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ float s_midv[QB ? LEANK_HEAD_DIM : 1];
   __shared__ float s_vpar[2];
 
-  const int item = blockIdx.x;
-  const int b = item / p.items_per_b;
-  const int r = item - b * p.items_per_b;
-  int h = 0;
-  while (h + 1 < p.n_kv && r >= p.heads[h + 1].base) ++h;
+  // dispatch order: every batch row's bulk items (full-width, then bulk
+  // middle, head by head), then every batch row's tail items; `local` is
+  // the item's place among its pair's records (full-width items, then
+  // middle chunks in row order), so the record order does not depend on it
+  const int64_t item = blockIdx.x;
+  int b, h = 0, local;
+  if (item < p.n_bulk) {
+    b = static_cast<int>(item / p.bulk_per_b);
+    int r = static_cast<int>(item - static_cast<int64_t>(b) * p.bulk_per_b);
+    while (h + 1 < p.n_kv && r >= p.n_sl_items + p.heads[h].n_mid_b) {
+      r -= p.n_sl_items + p.heads[h].n_mid_b;
+      ++h;
+    }
+    local = r;
+  } else {
+    const int64_t t_item = item - p.n_bulk;
+    b = static_cast<int>(t_item / p.tail_per_b);
+    int r = static_cast<int>(t_item - static_cast<int64_t>(b) * p.tail_per_b);
+    while (h + 1 < p.n_kv && r >= p.heads[h].n_mid - p.heads[h].n_mid_b) {
+      r -= p.heads[h].n_mid - p.heads[h].n_mid_b;
+      ++h;
+    }
+    local = p.n_sl_items + p.heads[h].n_mid_b + r;
+  }
   const DecodeHead hd = p.heads[h];
-  const int local = r - hd.base;
+  const int64_t rec_item = static_cast<int64_t>(b) * p.items_per_b + hd.base + local;
   const bool middle = local >= p.n_sl_items;
   const bool carries_step = p.step && local == 0;  // block-uniform
   const int t = threadIdx.x;
@@ -203,9 +237,11 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   if (QB == 0 && p.paged && middle && t >= 192) {
     // the item's pages (items span at most 64 pages: their rows are capped
     // by the plan's largest item size)
-    const int first = (local - p.n_sl_items) * hd.mid_rows / LEANK_PAGE_ROWS;
+    int pr0, pr1;
+    mid_chunk_rows(hd, local - p.n_sl_items, INT32_MAX, pr0, pr1);
+    const int first = pr0 / LEANK_PAGE_ROWS;
     const int i = t - 192;
-    if (i < hd.mid_rows / LEANK_PAGE_ROWS && first + i < p.pages_per_row)
+    if (i < (pr1 - pr0) / LEANK_PAGE_ROWS && first + i < p.pages_per_row)
       s_pages[i] = p.block_table[static_cast<int64_t>(b) * p.pages_per_row + first + i];
   }
   if ((middle || carries_step) && t >= 128 && t < 144)
@@ -395,7 +431,7 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
 
   // one record per item: (acc[G][128], m[G], l[G]) merged over the
   // wavefronts (and, in a step, the two step tokens)
-  float* rec = p.partials + static_cast<int64_t>(item) * p.partial_stride;
+  float* rec = p.partials + rec_item * p.partial_stride;
   for (int k = t; k < G * LEANK_HEAD_DIM; k += kThreads) {
     const int g = k / LEANK_HEAD_DIM;
     const int ch = k - g * LEANK_HEAD_DIM;
