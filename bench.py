@@ -53,10 +53,18 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=6, help="rotating cache copies")
     ap.add_argument("--workload", default="llama_b64_4k",
-                    choices=["llama_b64_4k", "qwen_b16_32k", "llama32_b1_128k"],
-                    help="workload of the main line (llama_b64_4k is the headline; another "
-                         "one-layer workload, e.g. qwen_b16_32k or llama32_b1_128k (its layer "
-                         "0), is for profiling it alone with --skip-extras)")
+                    choices=["llama_b64_4k", "qwen_b16_32k", "llama32_b1_128k",
+                             "llama32_b1_128k_model", "llama32_b64_gen"],
+                    help="workload of the main line (llama_b64_4k is the headline).  With "
+                         "--skip-extras another workload runs alone, for profiling: a one-layer "
+                         "step (qwen_b16_32k, or llama32_b1_128k: its layer 0), every layer of "
+                         "the 128K-token model per token (llama32_b1_128k_model, --steps "
+                         "tokens), or the 32-layer generation loop (llama32_b64_gen, --gen-steps "
+                         "steps)")
+    ap.add_argument("--quant-bits", type=int, default=0, choices=[0, 4, 8],
+                    help="one-layer workload alone: middle held in 4- or 8-bit streams")
+    ap.add_argument("--paged", action="store_true",
+                    help="one-layer workload alone: middle in 64-row pages (shuffled table)")
     ap.add_argument("--skip-extras", action="store_true",
                     help="only the main workload (no 0%% pruning, Qwen or CPU baseline)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -613,12 +621,14 @@ def main():
         sys.exit(2)
     from synthetic import get_config
 
-    cfg = get_config(args.workload)
-    headline = cfg.name == "llama_b64_4k"
-    if not headline and not args.skip_extras:
-        print("--workload other than llama_b64_4k profiles that workload alone: add --skip-extras",
-              file=sys.stderr)
+    alone = args.workload != "llama_b64_4k" or args.quant_bits or args.paged
+    if alone and not args.skip_extras:
+        print("--workload other than llama_b64_4k, --quant-bits and --paged profile one workload "
+              "alone: add --skip-extras", file=sys.stderr)
         sys.exit(2)
+    many_layers = args.workload in ("llama32_b1_128k_model", "llama32_b64_gen")
+    cfg = get_config({"llama32_b1_128k_model": "llama32_b1_128k"}.get(args.workload, args.workload))
+    headline = cfg.name == "llama_b64_4k" and not alone
     import torch
 
     if not torch.cuda.is_available():
@@ -628,7 +638,17 @@ def main():
 
     dac.lib()  # fail loudly if the HIP library is missing
     torch.cuda.synchronize()
-    main_res = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup)
+    if many_layers:
+        if args.workload == "llama32_b64_gen":
+            res = generation_loop(cfg, args.gen_steps)
+        else:
+            res = whole_model(cfg, steps=args.steps, warmup=args.warmup)
+        if args.copy_calibration:
+            res["copy_calibration"] = copy_calibration()
+        print(json.dumps({"workload": args.workload, **res}), flush=True)
+        return
+    main_res = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup,
+                        quant_bits=args.quant_bits, paged=args.paged)
     extras = {}
     if not args.skip_extras:
         unfused = workload(cfg, copies=args.copies, steps=args.steps, warmup=args.warmup,
@@ -696,7 +716,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": cfg.name,
+            "workload": cfg.name + (f"_{args.quant_bits}bit" if args.quant_bits else "")
+                        + ("_paged" if args.paged else ""),
             "shape": SHAPES.get(cfg.name, cfg.name),
             "batch": cfg.batch,
             "n_q_heads": cfg.n_q_heads,
