@@ -29,6 +29,13 @@ static_assert(kWaveCombineItems == 16 || kWaveCombineItems == 32,
               "the one-wavefront combine merges up to 16 or 32 items");
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Raw buffer resources (CDNA): word 3 of the descriptor for plain byte
+// addressing, the cache-policy operand of a non-temporal load, and an
+// offset past any resource's end (its load returns zeros).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kBufNT = LEANK_NT_LOADS ? 2 : 0;
+constexpr uint32_t kBufOutside = 0x80000000u;
+
 // The reference max only moves when a tile's max exceeds it by more than
 // this (base-2 units), so weights stay <= 2^kRescaleSlack and most tiles
 // skip the rescale; the softmax is unchanged because the reference cancels.
