@@ -127,6 +127,17 @@ typedef float f32x4_alias_t __attribute__((ext_vector_type(4), may_alias));
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// This lane's wavefront within the workgroup, in a scalar register.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// A 64-bit value that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint64_t u = static_cast<uint64_t>(x);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // 16-byte load of streamed cache data (read once per call).
 __device__ __forceinline__ u32x4_t load_stream16(const uint16_t* p) {
 #if LEANK_NT_LOADS

@@ -119,55 +119,64 @@ __device__ __forceinline__ void attend_middle(const DecodeParams& p, const Decod
   }
 }
 
-// bf16 middle rows of item `chunk_id`, contiguous or paged (the staged
-// form: holds the workgroup barrier that publishes q, the kept ids and the
-// item's pages).
+// bf16 middle rows of item `chunk_id` of a paged stream (holds the
+// workgroup barrier that publishes q, the kept ids and the item's pages,
+// which the caller has staged).
 template <int G>
-__device__ __forceinline__ void attend_middle_staged(const DecodeParams& p, const DecodeHead& hd,
-                                                     int b, int chunk_id, int t_mid,
-                                                     const uint16_t* s_q, const int16_t* s_idx,
-                                                     const int32_t* s_pages, uint16_t* p_lds,
-                                                     WaveState& st) {
+__device__ __forceinline__ void attend_middle_paged(const DecodeParams& p, const DecodeHead& hd,
+                                                    int b, int chunk_id, int t_mid,
+                                                    const uint16_t* s_q, const int16_t* s_idx,
+                                                    const int32_t* s_pages, uint16_t* p_lds,
+                                                    WaveState& st) {
   int r0, r1;
   mid_chunk_rows(hd, chunk_id, t_mid, r0, r1);
   const int c = hd.kept;
-  if (p.paged) {
-    const int32_t* g_pages =
-        p.block_table + static_cast<int64_t>(b) * p.pages_per_row + r0 / LEANK_PAGE_ROWS;
-    switch ((c + 31) / 32) {
-      case 1:
-        attend_range_paged_staged<G, 1>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
-                                        r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
-        break;
-      case 2:
-        attend_range_paged_staged<G, 2>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
-                                        r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
-        break;
-      case 3:
-        attend_range_paged_staged<G, 3>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
-                                        r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
-        break;
-      default:
-        attend_range_paged_staged<G, 4>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
-                                        r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
-        break;
-    }
-    return;
+  const int32_t* g_pages =
+      p.block_table + static_cast<int64_t>(b) * p.pages_per_row + r0 / LEANK_PAGE_ROWS;
+  switch ((c + 31) / 32) {
+    case 1:
+      attend_range_paged_staged<G, 1>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
+                                      r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
+      break;
+    case 2:
+      attend_range_paged_staged<G, 2>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
+                                      r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
+      break;
+    case 3:
+      attend_range_paged_staged<G, 3>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
+                                      r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
+      break;
+    default:
+      attend_range_paged_staged<G, 4>(p.pool, p.page_elems, g_pages, s_pages, hd.k_off, hd.v_off,
+                                      r0, r1, c, s_q, s_idx, p.qk_scale, p_lds, st);
+      break;
   }
+}
+
+// bf16 middle rows of item `chunk_id` of a contiguous stream; `stage` is
+// the workgroup's staging (see attend_range_staged).
+template <int G, class Stage>
+__device__ __forceinline__ void attend_middle_contig(const DecodeParams& p, const DecodeHead& hd,
+                                                     int b, int chunk_id, int t_mid,
+                                                     const uint16_t* s_q, const int16_t* s_idx,
+                                                     uint16_t* p_lds, WaveState& st, Stage&& stage) {
+  int r0, r1;
+  mid_chunk_rows(hd, chunk_id, t_mid, r0, r1);
+  const int c = hd.kept;
   const uint16_t* kb = p.k_prun + hd.k_off + static_cast<int64_t>(b) * p.mid_cap * c;
   const uint16_t* vb = p.v_mid + hd.v_off + static_cast<int64_t>(b) * p.v_mid_rows * LEANK_HEAD_DIM;
   switch ((c + 31) / 32) {
     case 1:
-      attend_range_staged<G, 1>(kb, c, vb, r0, r1, -1, c, s_q, s_idx, false, p.qk_scale, p_lds, st);
+      attend_range_staged<G, 1>(kb, c, vb, r0, r1, -1, c, s_q, s_idx, false, p.qk_scale, p_lds, st, stage);
       break;
     case 2:
-      attend_range_staged<G, 2>(kb, c, vb, r0, r1, -1, c, s_q, s_idx, false, p.qk_scale, p_lds, st);
+      attend_range_staged<G, 2>(kb, c, vb, r0, r1, -1, c, s_q, s_idx, false, p.qk_scale, p_lds, st, stage);
       break;
     case 3:
-      attend_range_staged<G, 3>(kb, c, vb, r0, r1, -1, c, s_q, s_idx, false, p.qk_scale, p_lds, st);
+      attend_range_staged<G, 3>(kb, c, vb, r0, r1, -1, c, s_q, s_idx, false, p.qk_scale, p_lds, st, stage);
       break;
     default:
-      attend_range_staged<G, 4>(kb, c, vb, r0, r1, -1, c, s_q, s_idx, false, p.qk_scale, p_lds, st);
+      attend_range_staged<G, 4>(kb, c, vb, r0, r1, -1, c, s_q, s_idx, false, p.qk_scale, p_lds, st, stage);
       break;
   }
 }
@@ -228,29 +237,65 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   const bool carries_step = p.step && local == 0;  // block-uniform
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = wave_id();
 
-  // stage the group's q rows and the head's kept ids; clear the P staging
-  const uint16_t* qh = p.q + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM;
-  if (t < G * 16)
-    *reinterpret_cast<u32x4_t*>(s_q + t * 8) = *reinterpret_cast<const u32x4_t*>(qh + t * 8);
-  if (QB == 0 && p.paged && middle && t >= 192) {
-    // the item's pages (items span at most 64 pages: their rows are capped
-    // by the plan's largest item size)
-    int pr0, pr1;
-    mid_chunk_rows(hd, local - p.n_sl_items, INT32_MAX, pr0, pr1);
-    const int first = pr0 / LEANK_PAGE_ROWS;
-    const int i = t - 192;
-    if (i < (pr1 - pr0) / LEANK_PAGE_ROWS && first + i < p.pages_per_row)
-      s_pages[i] = p.block_table[static_cast<int64_t>(b) * p.pages_per_row + first + i];
-  }
-  if ((middle || carries_step) && t >= 128 && t < 144)
-    *reinterpret_cast<u32x4_t*>(s_idx + (t - 128) * 8) =
-        *reinterpret_cast<const u32x4_t*>(p.kept_idx + h * LEANK_HEAD_DIM + (t - 128) * 8);
-  for (int k = lane; k < (QB ? group_lds_halves<KBMAX, G>() : 2 * 16 * kTileRows) / 8; k += 64)
-    reinterpret_cast<u32x4_t*>(s_p[wave])[k] = u32x4_t{0u, 0u, 0u, 0u};
   const int64_t pair = static_cast<int64_t>(b) * p.n_kv + h;
+  // (values read per batch row go through readfirstlane: they are the same
+  // in every lane, and scalar registers keep them out of the vector budget)
+  int t_sl = p.t_sl, t_mid = p.t_mid;
+  int excl = -1;  // ring row replaced by a fused step's append
+  if (p.step) {
+    // rows cached before the append; the row of the token leaving the
+    // window is scored by the step item
+    const int64_t pos = p.row_pos ? uniform64(p.row_pos[b]) : p.step_pos;
+    const bool ok = pos >= 0 && pos <= p.max_len;
+    const int len = ok ? static_cast<int>(pos) : 0;
+    if (ok && p.window > 0 && len - p.window >= p.n_sink)
+      excl = p.n_sink + (len - p.n_sink) % p.window;
+    t_sl = min(len, p.slots);
+    t_mid = max(0, len - p.slots);
+  } else if (p.ctx_lens) {  // ragged batch: this row may hold fewer tokens than the plan
+    const int len = min(max(__builtin_amdgcn_readfirstlane(p.ctx_lens[b]), 0), p.max_len);
+    t_sl = min(len, p.slots);
+    t_mid = max(0, len - p.slots);
+  } else if (p.lens_from_pos) {  // ragged step whose appends ran first
+    const int64_t pos = uniform64(p.row_pos[b]);
+    const int len = pos >= 0 && pos < p.max_len ? static_cast<int>(pos) + 1 : 0;
+    t_sl = min(len, p.slots);
+    t_mid = max(0, len - p.slots);
+  }
   StepTokens tok{};
+  // The workgroup's staging: the group's q rows and the head's kept ids,
+  // the item's pages (paged middle) and cleared P staging.  Each attend
+  // path runs it first; the workgroup barrier that publishes it sits in the
+  // attend call (bf16 streams: after each wavefront has issued its first
+  // tile's loads) or just below (low-bit middles).  Where it is written
+  // changes the register allocation of the whole kernel: this form
+  // measured fastest (written out once before the paths, the Llama
+  // batch-64 4K step took 115.4 us instead of 110.9).
+  auto stage = [&]() {
+    // stage the group's q rows and the head's kept ids; clear the P staging
+    const uint16_t* qh = p.q + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM;
+    if (t < G * 16)
+      *reinterpret_cast<u32x4_t*>(s_q + t * 8) = *reinterpret_cast<const u32x4_t*>(qh + t * 8);
+    if (QB == 0 && p.paged && middle && t >= 192) {
+      // the item's pages (items span at most 64 pages: their rows are capped
+      // by the plan's largest item size)
+      int pr0, pr1;
+      mid_chunk_rows(hd, local - p.n_sl_items, INT32_MAX, pr0, pr1);
+      const int first = pr0 / LEANK_PAGE_ROWS;
+      const int i = t - 192;
+      if (i < (pr1 - pr0) / LEANK_PAGE_ROWS && first + i < p.pages_per_row)
+        s_pages[i] = p.block_table[static_cast<int64_t>(b) * p.pages_per_row + first + i];
+    }
+    if ((middle || carries_step) && t >= 128 && t < 144)
+      *reinterpret_cast<u32x4_t*>(s_idx + (t - 128) * 8) =
+          *reinterpret_cast<const u32x4_t*>(p.kept_idx + h * LEANK_HEAD_DIM + (t - 128) * 8);
+    for (int k = lane; k < (QB ? group_lds_halves<KBMAX, G>() : 2 * 16 * kTileRows) / 8; k += 64)
+      reinterpret_cast<u32x4_t*>(s_p[wave])[k] = u32x4_t{0u, 0u, 0u, 0u};
+  };
+  // the item that carries a fused step stages its tokens and V blocks
+  // before anything else (one item per pair)
   if (carries_step) {
     // the new token from k_new / v_new; the leaving one and the V blocks
     // the append rewrites from the cache
@@ -310,41 +355,20 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   for (int n = 0; n < 8; ++n) st.o[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   uint16_t* p_lds = s_p[wave];
 
-  int t_sl = p.t_sl, t_mid = p.t_mid;
-  int excl = -1;  // ring row replaced by a fused step's append
-  if (p.step) {
-    // rows cached before the append; the row of the token leaving the
-    // window is scored by the step item
-    const int64_t pos = p.row_pos ? p.row_pos[b] : p.step_pos;
-    const bool ok = pos >= 0 && pos <= p.max_len;
-    const int len = ok ? static_cast<int>(pos) : 0;
-    if (ok && p.window > 0 && len - p.window >= p.n_sink)
-      excl = p.n_sink + (len - p.n_sink) % p.window;
-    t_sl = min(len, p.slots);
-    t_mid = max(0, len - p.slots);
-  } else if (p.ctx_lens) {  // ragged batch: this row may hold fewer tokens than the plan
-    const int len = min(max(p.ctx_lens[b], 0), p.max_len);
-    t_sl = min(len, p.slots);
-    t_mid = max(0, len - p.slots);
-  } else if (p.lens_from_pos) {  // ragged step whose appends ran first
-    const int64_t pos = p.row_pos[b];
-    const int len = pos >= 0 && pos < p.max_len ? static_cast<int>(pos) + 1 : 0;
-    t_sl = min(len, p.slots);
-    t_mid = max(0, len - p.slots);
-  }
-  // the staging above is published by the workgroup barrier inside the
-  // attend call (bf16 streams: after each wavefront has issued its first
-  // tile's loads) or just below (low-bit middles)
   if (!middle) {
     const int r0 = local * p.sl_rows;
     const int r1 = min(t_sl, r0 + p.sl_rows);
     const uint16_t* kb = p.k_sl + pair * p.slots * LEANK_HEAD_DIM;
     const uint16_t* vb = p.v_sl + pair * p.v_sl_rows * LEANK_HEAD_DIM;
     attend_range_staged<G, 4>(kb, LEANK_HEAD_DIM, vb, r0, r1, excl, LEANK_HEAD_DIM, s_q, s_idx,
-                              true, p.qk_scale, p_lds, st);
+                              true, p.qk_scale, p_lds, st, stage);
+  } else if (QB == 0 && !p.paged) {
+    attend_middle_contig<G>(p, hd, b, local - p.n_sl_items, t_mid, s_q, s_idx, p_lds, st, stage);
   } else if (QB == 0) {
-    attend_middle_staged<G>(p, hd, b, local - p.n_sl_items, t_mid, s_q, s_idx, s_pages, p_lds, st);
+    stage();
+    attend_middle_paged<G>(p, hd, b, local - p.n_sl_items, t_mid, s_q, s_idx, s_pages, p_lds, st);
   } else {
+    stage();
     __syncthreads();
     attend_middle<G, QB, KBMAX>(p, hd, b, local - p.n_sl_items, t_mid, s_q, s_idx, s_pages, p_lds,
                                 st, vmin);
@@ -475,6 +499,11 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     }
   }
 
+  // The append below rewrites the staged blocks in LDS (wavefront 0 sets
+  // the appended row of each channel), and every wavefront's part of the
+  // record above reads the leaving token's V from the same staged ring
+  // block: all of them finish before wavefront 0 starts.
+  if (carries_step) __syncthreads();  // block-uniform
   if (carries_step && tok.ok && wave == 0) {
     // the append; this workgroup's reads of the ring row ended before the
     // merge, and no other item of the call uses the rows written here.

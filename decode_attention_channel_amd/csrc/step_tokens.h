@@ -31,7 +31,7 @@ struct StepTokens {
 
 __device__ __forceinline__ StepTokens step_tokens(const DecodeParams& p, int b, bool live) {
   StepTokens st;
-  const int64_t pos = p.row_pos ? p.row_pos[b] : p.step_pos;
+  const int64_t pos = p.row_pos ? uniform64(p.row_pos[b]) : p.step_pos;
   st.ok = pos >= 0 && pos <= p.max_len;
   st.pos = st.ok ? static_cast<int>(pos) : 0;
   const int S = p.n_sink, W = p.window;

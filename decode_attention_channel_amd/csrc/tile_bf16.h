@@ -16,34 +16,6 @@ struct TileRegs {
   u32x4_t vf[8];      // V block t0 / 8 + grp, channel 16 n + col
 };
 
-// Issues the loads of the tile starting at row t0 (rows >= nvalid are
-// outside the item).  kb: K row 0 (row length kstride = c elements); vb: V
-// block 0 of the stream.
-template <int KB>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ kb, int kstride,
-                                          const uint16_t* __restrict__ vb, int t0, int nvalid,
-                                          int c, TileRegs<KB>& tr) {
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  const uint16_t* kt = kb + static_cast<int64_t>(t0) * kstride;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-      const int row = 16 * j + col;
-      const int ch = 32 * kk + 8 * grp;
-      const bool ok = ch < c && row < nvalid;
-      tr.kf[j][kk] = ok ? load_stream16(kt + row * kstride + ch) : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-  const uint16_t* vt = vb + (static_cast<int64_t>(t0 / 8 + grp) * LEANK_HEAD_DIM + col) * 8;
-  const bool v_ok = 8 * grp < nvalid;
-#pragma unroll
-  for (int n = 0; n < 8; ++n)
-    tr.vf[n] = v_ok ? load_stream16(vt + n * 16 * 8) : u32x4_t{0u, 0u, 0u, 0u};
-}
-
 // Scores, softmax bookkeeping and weighted V of one loaded tile.  The
 // masked variant (kTail) drops rows >= nvalid and row excl_rel (a ring row
 // that a fused step replaces; any value outside [0, 32) drops nothing).
@@ -181,25 +153,28 @@ __device__ __forceinline__ void load_tile_buf(__amdgpu_buffer_rsrc_t rk, __amdgp
   for (int n = 0; n < 8; ++n) tr.vf[n] = load_buf16(rv, v0 + n * 256);
 }
 
-// Rows [r0, r1) of one stream, except row excl (-1: none), for a workgroup
-// whose q rows and kept ids are still on their way to LDS: each wavefront
-// issues its first tile's loads, then joins the workgroup barrier that
-// publishes the staging, then gathers its query operand, so the two memory
-// latencies at the start of an item overlap.  The loads go through buffer
-// resources bounded by the item's rows, so the last tile needs no lane
-// branches (measured against per-lane predicated global loads: the
+// Rows [r0, r1) of one stream, except row excl (-1: none).  `stage` runs
+// the workgroup's staging (q rows and kept ids into LDS; the caller defines
+// it), then each wavefront issues its first tile's loads, joins the
+// workgroup barrier that publishes the staging and gathers its query
+// operand, so the two memory latencies at the start of an item overlap.
+// (Running the staging after the tile's loads, so that it waits behind
+// them, measured slower: the Llama batch-64 4K step 110.9 -> 112.7 us, the
+// 32-layer 128K-token batch-1 token 960 -> 970 us.)  The loads go through
+// buffer resources bounded by the item's rows, so the last tile needs no
+// lane branches (measured against per-lane predicated global loads: the
 // 32-layer 128K-token batch-1 token 991 -> 978 us, the Qwen2.5-7B-shaped
 // batch-16 32K step 90.1 -> 89.4 us).  Keeping a second tile in flight per
 // wavefront (two tiles of registers, so two workgroups per compute unit
 // instead of three) measured slower: 1051 us and 98 us.  Every thread of
 // the workgroup must call this (it holds the barrier).
-template <int G, int KB>
+template <int G, int KB, class Stage>
 __device__ __forceinline__ void attend_range_staged(const uint16_t* kb, int kstride,
                                                     const uint16_t* vb, int r0, int r1, int excl,
                                                     int c, const uint16_t* s_q,
                                                     const int16_t* s_idx, bool dense,
                                                     float qk_scale, uint16_t* p_lds,
-                                                    WaveState& st) {
+                                                    WaveState& st, Stage&& stage) {
   constexpr int kStep = kWaves * kTileRows;
   const int wave = threadIdx.x >> 6;
   const int n = r1 - r0;  // rows of the item (r0 is a multiple of 8)
@@ -211,6 +186,7 @@ __device__ __forceinline__ void attend_range_staged(const uint16_t* kb, int kstr
   const int ex = excl < 0 ? -1 : excl - r0;
   int t = wave * kTileRows;
   TileRegs<KB> tr;
+  stage();
   load_tile_buf<KB>(rk, rv, kstride, t, c, tr);
   __syncthreads();
   u32x4_t qa[KB];
@@ -227,45 +203,42 @@ __device__ __forceinline__ void attend_range_staged(const uint16_t* kb, int kstr
 
 // Middle rows [r0, r1) of a paged stream: r0 is a multiple of the page
 // size and s_pages holds the physical pages of rows r0, r0 + 64, ...
-// (tiles never straddle a page: both are 32-row aligned).  Staged as
-// attend_range_staged: the first tile's page comes from g_pages, the block
-// table entries of the same rows in global memory, while s_pages and the q
-// rows are still on their way to LDS.  Every thread of the workgroup must
-// call this (it holds the barrier).
+// (tiles never straddle a page: both are 32-row aligned).  Each tile loads
+// through resources over its page's rows that belong to the item.  Staged
+// as attend_range_staged: the first tile's page comes from g_pages, the
+// block table entries of the same rows in global memory, while s_pages and
+// the q rows are still on their way to LDS.  Every thread of the workgroup
+// must call this (it holds the barrier).
 template <int G, int KB>
 __device__ __forceinline__ void attend_range_paged_staged(
     const uint16_t* pool, int64_t page_elems, const int32_t* g_pages, const int32_t* s_pages,
     int64_t k_off, int64_t v_off, int r0, int r1, int c, const uint16_t* s_q,
     const int16_t* s_idx, float qk_scale, uint16_t* p_lds, WaveState& st) {
+  constexpr int kStep = kWaves * kTileRows;
   const int wave = threadIdx.x >> 6;
-  int t0 = r0 + wave * kTileRows;
-  TileRegs<KB> first;
-  if (t0 < r1) {
-    const uint16_t* page = pool + static_cast<int64_t>(g_pages[(t0 - r0) / LEANK_PAGE_ROWS]) * page_elems;
-    load_tile<KB>(page + k_off, c, page + v_off, t0 % LEANK_PAGE_ROWS, r1 - t0, c, first);
-  }
+  const int n = r1 - r0;
+  // loads of the tile at item row t from physical page `page`
+  auto load = [&](int t, int32_t page, TileRegs<KB>& tr) {
+    const int in = t % LEANK_PAGE_ROWS;         // row within the page
+    const int rows = min(LEANK_PAGE_ROWS, n - (t - in));  // the item's rows in the page
+    const uint16_t* base = pool + static_cast<int64_t>(page) * page_elems;
+    load_tile_buf<KB>(stream_rsrc(base + k_off, static_cast<int64_t>(rows) * c * 2),
+                      stream_rsrc(base + v_off, static_cast<int64_t>((rows + 7) / 8) * (LEANK_HEAD_DIM * 8 * 2)),
+                      c, in, c, tr);
+  };
+  int t = wave * kTileRows;
+  TileRegs<KB> tr;
+  if (t < n) load(t, __builtin_amdgcn_readfirstlane(g_pages[t / LEANK_PAGE_ROWS]), tr);
   __syncthreads();
   u32x4_t qa[KB];
   gather_q<G, KB>(s_q, s_idx, false, c, qa);
-  if (t0 < r1) {
-    const int nvalid = r1 - t0;
-    if (nvalid >= kTileRows) {
-      compute_tile<G, KB, false>(first, kTileRows, -1, qa, qk_scale, p_lds, st);
-    } else {
-      compute_tile<G, KB, true>(first, nvalid, -1, qa, qk_scale, p_lds, st);
-    }
-    t0 += kWaves * kTileRows;
-  }
-  for (; t0 < r1; t0 += kWaves * kTileRows) {
-    const int nvalid = r1 - t0;
-    const uint16_t* page = pool + static_cast<int64_t>(s_pages[(t0 - r0) / LEANK_PAGE_ROWS]) * page_elems;
-    TileRegs<KB> cur;
-    load_tile<KB>(page + k_off, c, page + v_off, t0 % LEANK_PAGE_ROWS, nvalid, c, cur);
-    if (nvalid >= kTileRows) {
-      compute_tile<G, KB, false>(cur, kTileRows, -1, qa, qk_scale, p_lds, st);
-    } else {
-      compute_tile<G, KB, true>(cur, nvalid, -1, qa, qk_scale, p_lds, st);
-    }
+  while (t < n) {
+    if (n - t >= kTileRows)
+      compute_tile<G, KB, false>(tr, kTileRows, -1, qa, qk_scale, p_lds, st);
+    else
+      compute_tile<G, KB, true>(tr, n - t, -1, qa, qk_scale, p_lds, st);
+    t += kStep;
+    if (t < n) load(t, __builtin_amdgcn_readfirstlane(s_pages[t / LEANK_PAGE_ROWS]), tr);
   }
 }
 
