@@ -52,6 +52,7 @@ struct WorkPlan {
   int32_t mid_rows_t[LEANK_MAX_KV_HEADS];  // rows per tail middle item
   int32_t bulk_per_b;     // items of a batch row dispatched first (full-width + bulk middle)
   int32_t tail_per_b;     // items of a batch row dispatched after every bulk item
+  int32_t sl_first;       // 1: every row's full-width items are dispatched before any middle item
   int32_t step;           // 1 for a fused decode step
   int32_t head_base[LEANK_MAX_KV_HEADS + 1];  // first item of head h within a batch row
   int32_t items_per_b;

@@ -211,6 +211,7 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   p.bulk_per_b = w.bulk_per_b;
   p.tail_per_b = w.tail_per_b;
   p.n_bulk = static_cast<int64_t>(w.bulk_per_b) * c->batch;
+  p.n_sl_all = w.sl_first ? static_cast<int64_t>(c->batch) * c->n_kv_heads * w.n_sl_items : 0;
   p.partial_stride = w.partial_stride;
   // pairs with many items get their channels split over several combine workgroups
   int32_t max_items = 0;

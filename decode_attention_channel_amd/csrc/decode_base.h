@@ -111,6 +111,7 @@ struct DecodeParams {
   int32_t bulk_per_b;
   int32_t tail_per_b;
   int64_t n_bulk;  // batch * bulk_per_b
+  int64_t n_sl_all;  // full-width items dispatched first (batch * n_kv * n_sl_items), or 0
   DecodeHead heads[LEANK_MAX_KV_HEADS];
 };
 // kernel arguments are limited to 4 KiB

@@ -208,29 +208,48 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ float s_vpar[2];
 
   // dispatch order: every batch row's bulk items (full-width, then bulk
-  // middle, head by head), then every batch row's tail items; `local` is
-  // the item's place among its pair's records (full-width items, then
-  // middle chunks in row order), so the record order does not depend on it
-  const int64_t item = blockIdx.x;
+  // middle, head by head; or, when the plan puts the full-width items
+  // first, every row's full-width items, then every row's bulk middle
+  // items), then every batch row's tail items; `local` is the item's place
+  // among its pair's records (full-width items, then middle chunks in row
+  // order), so the record order does not depend on it
+  // (32-bit arithmetic: a launch holds fewer than 2^31 items; the results
+  // go through readfirstlane so that they stay in scalar registers)
+  const uint32_t item = blockIdx.x;
   int b, h = 0, local;
-  if (item < p.n_bulk) {
-    b = static_cast<int>(item / p.bulk_per_b);
-    int r = static_cast<int>(item - static_cast<int64_t>(b) * p.bulk_per_b);
-    while (h + 1 < p.n_kv && r >= p.n_sl_items + p.heads[h].n_mid_b) {
-      r -= p.n_sl_items + p.heads[h].n_mid_b;
+  if (item < static_cast<uint32_t>(p.n_sl_all)) {
+    const uint32_t per_b = static_cast<uint32_t>(p.n_kv * p.n_sl_items);
+    b = static_cast<int>(item / per_b);
+    const int r = static_cast<int>(item - static_cast<uint32_t>(b) * per_b);
+    h = r / p.n_sl_items;
+    local = r - h * p.n_sl_items;
+  } else if (item < static_cast<uint32_t>(p.n_bulk)) {
+    // every row's bulk middle items after the full-width ones (n_sl_all > 0),
+    // or each row's full-width and bulk middle items together
+    const uint32_t n_sl = p.n_sl_all > 0 ? 0u : static_cast<uint32_t>(p.n_sl_items);
+    const uint32_t per_b = static_cast<uint32_t>(p.bulk_per_b) -
+                           (p.n_sl_all > 0 ? static_cast<uint32_t>(p.n_kv * p.n_sl_items) : 0u);
+    const uint32_t j = item - static_cast<uint32_t>(p.n_sl_all);
+    b = static_cast<int>(j / per_b);
+    int r = static_cast<int>(j - static_cast<uint32_t>(b) * per_b);
+    while (h + 1 < p.n_kv && r >= static_cast<int>(n_sl) + p.heads[h].n_mid_b) {
+      r -= static_cast<int>(n_sl) + p.heads[h].n_mid_b;
       ++h;
     }
-    local = r;
+    local = r + (p.n_sl_all > 0 ? p.n_sl_items : 0);
   } else {
-    const int64_t t_item = item - p.n_bulk;
-    b = static_cast<int>(t_item / p.tail_per_b);
-    int r = static_cast<int>(t_item - static_cast<int64_t>(b) * p.tail_per_b);
+    const uint32_t t_item = item - static_cast<uint32_t>(p.n_bulk);
+    b = static_cast<int>(t_item / static_cast<uint32_t>(p.tail_per_b));
+    int r = static_cast<int>(t_item - static_cast<uint32_t>(b) * static_cast<uint32_t>(p.tail_per_b));
     while (h + 1 < p.n_kv && r >= p.heads[h].n_mid - p.heads[h].n_mid_b) {
       r -= p.heads[h].n_mid - p.heads[h].n_mid_b;
       ++h;
     }
     local = p.n_sl_items + p.heads[h].n_mid_b + r;
   }
+  b = __builtin_amdgcn_readfirstlane(b);
+  h = __builtin_amdgcn_readfirstlane(h);
+  local = __builtin_amdgcn_readfirstlane(local);
   const DecodeHead hd = p.heads[h];
   const int64_t rec_item = static_cast<int64_t>(b) * p.items_per_b + hd.base + local;
   const bool middle = local >= p.n_sl_items;

@@ -59,6 +59,9 @@ namespace {
 #ifndef LEANK_TAIL_MAX_KEPT
 #define LEANK_TAIL_MAX_KEPT 64
 #endif
+#ifndef LEANK_SL_FIRST
+#define LEANK_SL_FIRST 1
+#endif
 
 constexpr int64_t kTargetCUs = 256;  // compute units of an MI355X
 constexpr int64_t kRoundPerCU = 3;   // split-kernel workgroups resident per compute unit
@@ -414,6 +417,23 @@ int make_work_plan(const leank_layer_cache* c, int64_t ctx_len, int step, WorkPl
       w->mid_rows_t[h] = static_cast<int32_t>(r_t);
       w->n_mid[h] = static_cast<int32_t>(n_b + n_t);
     }
+  }
+  // Longest items first: a launch of more than one round dispatches its
+  // full-width items (every batch row's) ahead of the middle ones when a
+  // full-width item costs more than any bulk middle item, so that the long
+  // items do not start late and end the launch after the short ones.
+  // Measured (MI355X): the Llama batch-64 4K step with a 4-bit middle
+  // (full-width items 288 KB of bf16 rows, bulk middle items 1536 rows of
+  // 4-bit codes) 72.7 -> 70.5 us, with an 8-bit middle 88.4 -> 87.0 us;
+  // bf16 middles keep the interleaved order (their bulk items are larger).
+  w->sl_first = 0;
+  if (LEANK_SL_FIRST && w->n_sl_items > 0 && items > kTargetCUs * kRoundPerCU) {
+    const int64_t sl_cost = static_cast<int64_t>(w->sl_rows) * 4 * LEANK_HEAD_DIM;
+    int64_t mid_cost = 0;
+    for (int h = 0; h < c->n_kv_heads; ++h)
+      if (c->kept_count[h] > 0 && w->n_mid_b[h] > 0)
+        mid_cost = std::max(mid_cost, static_cast<int64_t>(w->mid_rows[h]) * middle_row_cost(c, c->kept_count[h]));
+    w->sl_first = sl_cost > mid_cost ? 1 : 0;
   }
   int32_t base = 0;
   w->bulk_per_b = 0;
