@@ -328,54 +328,96 @@ __device__ __forceinline__ void load_group(const QSegment& q, int c, int g0, int
   }
 }
 
+// The table entries and offset terms of the complete groups are split over
+// the lanes the same way in every group: lane l takes query head
+// h = l / kLanes and kept channels j = l % kLanes + kLanes k.  QueryCols
+// holds, per lane, q_h at those channels (0 for heads >= G or channels
+// past c), gathered once per item: a group then only scales them.
+// (Wide heads, more than 4 values per lane, keep the LDS pointers instead
+// and gather in every group: holding the values spilled registers.)
+template <int NQ>
+constexpr int query_lanes() { return 64 / (NQ * 4); }  // lanes per head: 16 or 8
+template <int KB, int NQ>
+constexpr int query_cols() { return 32 * KB / query_lanes<NQ>(); }
+template <int KB, int NQ>
+constexpr bool kHoldQueryCols = query_cols<KB, NQ>() <= 4;
+template <int KB, int NQ>
+struct QueryCols {
+  float qv[kHoldQueryCols<KB, NQ> ? query_cols<KB, NQ>() : 1];
+  const uint16_t* s_q;
+  const int16_t* s_idx;
+  int h_limit;  // G
+};
+
+// q of this lane's head at kept channel j (0 past c or for heads >= G)
+__device__ __forceinline__ float query_col(const uint16_t* s_q, const int16_t* s_idx, int h, int j,
+                                           int c, int g) {
+  return h < g && j < c ? bf16_to_f32(s_q[h * LEANK_HEAD_DIM + (s_idx[j] & (LEANK_HEAD_DIM - 1))]) : 0.0f;
+}
+
+template <int G, int KB, int NQ>
+__device__ __forceinline__ void gather_query_cols(const uint16_t* s_q, const int16_t* s_idx, int c,
+                                                  QueryCols<KB, NQ>& qc) {
+  constexpr int kLanes = query_lanes<NQ>();
+  const int lane = threadIdx.x & 63;
+  const int h = lane / kLanes;
+  const int part = lane - h * kLanes;
+  qc.s_q = s_q;
+  qc.s_idx = s_idx;
+  qc.h_limit = G;
+  if constexpr (kHoldQueryCols<KB, NQ>) {
+#pragma unroll
+    for (int k = 0; k < query_cols<KB, NQ>(); ++k) qc.qv[k] = query_col(s_q, s_idx, h, part + kLanes * k, c, G);
+  }
+}
+
 // Builds the group's query tables in this wavefront's LDS and returns the
 // offset term of quad qd's head i in bias[qd][i] (every lane): q' = q *
 // scale * qk_scale (hi + lo); the offset is qk_scale sum_c q_c min_c, and
 // for 4-bit codes also -128 sum_c q'_c (q'_c as rounded in the table).
-template <int G, int NQ, int QB>
+template <int G, int NQ, int QB, int KB>
 __device__ __forceinline__ void build_group_tables(const f32x4_t& par16, int c,
-                                                   const uint16_t* s_q, const int16_t* s_idx,
-                                                   float qk_scale, uint16_t* w_lds,
-                                                   float (&bias)[NQ][4]) {
+                                                   const QueryCols<KB, NQ>& qc, float qk_scale,
+                                                   uint16_t* w_lds, float (&bias)[NQ][4]) {
+  constexpr int kLanes = query_lanes<NQ>();
   const int lane = threadIdx.x & 63;
   float* par = reinterpret_cast<float*>(w_lds + kGroupStage);  // [c][2]
   uint16_t* tab = w_lds + kGroupStage + 4 * c;                // hi [NQ][c/4][4][4], then lo
   // the (scale, min) pairs, 16 bytes per lane, to LDS
   if (4 * lane < 2 * c) reinterpret_cast<f32x4_alias_t*>(par)[lane] = par16;
-  // entries (head h, kept channel j); head h of quad h / 4
-  for (int e = lane; e < NQ * 4 * c; e += 64) {
-    const int h = e / c;
-    const int j = e - h * c;
-    const float qv = h < G ? bf16_to_f32(s_q[h * LEANK_HEAD_DIM + (s_idx[j] & (LEANK_HEAD_DIM - 1))]) : 0.0f;
-    const float x = qv * par[2 * j] * qk_scale;
-    const __bf16 hi = static_cast<__bf16>(x);
-    const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
-    // 4-channel step and place of channel j in the code operand order
-    const int step = QB == 4 ? 2 * (j >> 3) + (j & 1) : j >> 2;
-    const int pos = QB == 4 ? (j & 7) >> 1 : j & 3;
-    const int at = (((h >> 2) * (c / 4) + step) * 4 + (h & 3)) * 4 + pos;
-    tab[at] = __builtin_bit_cast(uint16_t, hi);
-    tab[NQ * 4 * c + at] = __builtin_bit_cast(uint16_t, lo);
-  }
-  // offset terms: lanes of a head sum its channels, then one lane each.
-  // sum_c q_c min_c (times the softmax scale), and for 4-bit codes, which
-  // enter the product as 128 + code, -128 sum_c q'_c with q'_c rounded as
-  // it entered the product (hi + lo), so that the 128 terms cancel
-  constexpr int kLanes = 64 / (NQ * 4);  // lanes per head (16 or 8)
+  // this lane's entries (head h, kept channel j), and its part of head h's
+  // offset sum: sum_c q_c min_c (times the softmax scale), and for 4-bit
+  // codes, which enter the product as 128 + code, -128 sum_c q'_c with
+  // q'_c rounded as it entered the product (hi + lo), so that the 128
+  // terms cancel.  Every head slot's entries are written (zeros for heads
+  // >= G).
   const int h = lane / kLanes;
   const int part = lane - h * kLanes;
   float sum = 0.0f;
-  if (h < G) {
-    for (int j = part; j < c; j += kLanes) {
-      const float qv = bf16_to_f32(s_q[h * LEANK_HEAD_DIM + (s_idx[j] & (LEANK_HEAD_DIM - 1))]);
+#pragma unroll
+  for (int k = 0; k < query_cols<KB, NQ>(); ++k) {
+    const int j = part + kLanes * k;
+    if (j < c) {
+      const float2 pm = *reinterpret_cast<const float2*>(par + 2 * j);
+      float qv;
+      if constexpr (kHoldQueryCols<KB, NQ>)
+        qv = qc.qv[k];
+      else
+        qv = query_col(qc.s_q, qc.s_idx, h, j, c, qc.h_limit);
+      const float x = qv * pm.x * qk_scale;
+      const __bf16 hi = static_cast<__bf16>(x);
+      const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
+      // 4-channel step and place of channel j in the code operand order
+      const int step = QB == 4 ? 2 * (j >> 3) + (j & 1) : j >> 2;
+      const int pos = QB == 4 ? (j & 7) >> 1 : j & 3;
+      const int at = (((h >> 2) * (c / 4) + step) * 4 + (h & 3)) * 4 + pos;
+      tab[at] = __builtin_bit_cast(uint16_t, hi);
+      tab[NQ * 4 * c + at] = __builtin_bit_cast(uint16_t, lo);
       if constexpr (QB == 4) {
-        const float x = qv * par[2 * j] * qk_scale;
-        const __bf16 hi = static_cast<__bf16>(x);
-        const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
-        sum = fmaf(qv * qk_scale, par[2 * j + 1], sum);
+        sum = fmaf(qv * qk_scale, pm.y, sum);
         sum = fmaf(-128.0f, static_cast<float>(hi) + static_cast<float>(lo), sum);
       } else {
-        sum = fmaf(qv, par[2 * j + 1], sum);
+        sum = fmaf(qv, pm.y, sum);
       }
     }
   }
@@ -394,8 +436,8 @@ __device__ __forceinline__ void build_group_tables(const f32x4_t& par16, int c,
 
 // One complete group of 64 rows starting at g0 (group g0 / 64).
 template <int G, int KB, int QB>
-__device__ __forceinline__ void attend_group(const GroupRegs<KB, QB>& gr, int c, const uint16_t* s_q,
-                                             const int16_t* s_idx, float qk_scale,
+__device__ __forceinline__ void attend_group(const GroupRegs<KB, QB>& gr, int c,
+                                             const QueryCols<KB, (G + 3) / 4>& qc, float qk_scale,
                                              uint16_t* w_lds, RowState<(G + 3) / 4>& rs,
                                              WaveState& st) {
   constexpr int NQ = (G + 3) / 4;
@@ -404,7 +446,7 @@ __device__ __forceinline__ void attend_group(const GroupRegs<KB, QB>& gr, int c,
   const int grp = lane >> 4;
 
   float bias[NQ][4];
-  build_group_tables<G, NQ, QB>(gr.par, c, s_q, s_idx, qk_scale, w_lds, bias);
+  build_group_tables<G, NQ, QB, KB>(gr.par, c, qc, qk_scale, w_lds, bias);
 
   // scores (already times the softmax scale)
   f32x4_t s[NQ];
@@ -611,7 +653,7 @@ constexpr bool kPrefetchGroups = QB == 4 && G <= 4;
 // group is scored.  The loop body holds no branch around a load.
 template <int G, int KB, int QB, bool kPaged>
 __device__ __forceinline__ void attend_groups_pipelined(const QSegment& q, int& g0, int full_end, int c,
-                                                        const uint16_t* s_q, const int16_t* s_idx,
+                                                        const QueryCols<KB, (G + 3) / 4>& qc,
                                                         float qk_scale, uint16_t* p_lds,
                                                         RowState<(G + 3) / 4>& rs, WaveState& st) {
   constexpr int kStep = kWaves * LEANK_QUANT_GROUP;
@@ -623,13 +665,13 @@ __device__ __forceinline__ void attend_groups_pipelined(const QSegment& q, int& 
   for (; g0 + kStep < full_end; g0 += kStep) {
     load_group<KB, QB, true>(q, c, g0 + kStep, page, nxt);
     if (kPaged) page = q.pages[min(g0 + 2 * kStep, last) / LEANK_QUANT_GROUP];
-    attend_group<G, KB, QB>(cur, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+    attend_group<G, KB, QB>(cur, c, qc, qk_scale, p_lds, rs, st);
     // the copy waits for the next group's loads: keep it after the group's
     // work, where those loads have had the whole group to land
     __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
   }
-  attend_group<G, KB, QB>(cur, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+  attend_group<G, KB, QB>(cur, c, qc, qk_scale, p_lds, rs, st);
   g0 += kStep;  // the wavefront's first group at or past full_end
 }
 
@@ -645,7 +687,7 @@ constexpr bool kPrefetchGroupK = QB == 8 && G <= 4;
 // the group is done and land behind the next group's tables and scores.
 template <int G, int KB, int QB, bool kPaged>
 __device__ __forceinline__ void attend_groups_kpart_pipelined(const QSegment& q, int& g0, int full_end, int c,
-                                                    const uint16_t* s_q, const int16_t* s_idx,
+                                                    const QueryCols<KB, (G + 3) / 4>& qc,
                                                     float qk_scale, uint16_t* p_lds,
                                                     RowState<(G + 3) / 4>& rs, WaveState& st) {
   constexpr int kStep = kWaves * LEANK_QUANT_GROUP;
@@ -654,7 +696,7 @@ __device__ __forceinline__ void attend_groups_kpart_pipelined(const QSegment& q,
   for (; g0 + kStep < full_end; g0 += kStep) {
     const int pn = kPaged ? q.pages[(g0 + kStep) / LEANK_QUANT_GROUP] : 0;
     load_group<KB, QB, true, 1>(q, c, g0 + kStep, pn, nxt);
-    attend_group<G, KB, QB>(cur, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+    attend_group<G, KB, QB>(cur, c, qc, qk_scale, p_lds, rs, st);
     __builtin_amdgcn_sched_barrier(0);
     cur.par = nxt.par;
 #pragma unroll
@@ -663,7 +705,7 @@ __device__ __forceinline__ void attend_groups_kpart_pipelined(const QSegment& q,
     cur.vm = nxt.vm;
     load_group<KB, QB, true, 2>(q, c, g0 + kStep, pn, cur);
   }
-  attend_group<G, KB, QB>(cur, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+  attend_group<G, KB, QB>(cur, c, qc, qk_scale, p_lds, rs, st);
   g0 += kStep;
 }
 
@@ -682,6 +724,8 @@ __device__ __forceinline__ void attend_range_q(const QSegment& q, int r0, int r1
   int g0 = r0 + wave * LEANK_QUANT_GROUP;
   const int full_end = min(r1, q.full_rows);
   if (g0 < full_end) {
+    QueryCols<KB, NQ> qc;
+    gather_query_cols<G, KB, NQ>(s_q, s_idx, c, qc);
     RowState<NQ> rs;
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
@@ -694,21 +738,21 @@ __device__ __forceinline__ void attend_range_q(const QSegment& q, int r0, int r1
     }
     if constexpr (kPrefetchGroups<G, QB>) {
       if (q.pool)
-        attend_groups_pipelined<G, KB, QB, true>(q, g0, full_end, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+        attend_groups_pipelined<G, KB, QB, true>(q, g0, full_end, c, qc, qk_scale, p_lds, rs, st);
       else
-        attend_groups_pipelined<G, KB, QB, false>(q, g0, full_end, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+        attend_groups_pipelined<G, KB, QB, false>(q, g0, full_end, c, qc, qk_scale, p_lds, rs, st);
     } else if constexpr (kPrefetchGroupK<G, QB>) {
       if (q.pool)
-        attend_groups_kpart_pipelined<G, KB, QB, true>(q, g0, full_end, c, s_q, s_idx, qk_scale,
+        attend_groups_kpart_pipelined<G, KB, QB, true>(q, g0, full_end, c, qc, qk_scale,
                                                        p_lds, rs, st);
       else
-        attend_groups_kpart_pipelined<G, KB, QB, false>(q, g0, full_end, c, s_q, s_idx, qk_scale,
+        attend_groups_kpart_pipelined<G, KB, QB, false>(q, g0, full_end, c, qc, qk_scale,
                                                         p_lds, rs, st);
     } else {
       for (; g0 < full_end; g0 += kWaves * LEANK_QUANT_GROUP) {
         GroupRegs<KB, QB> gr;
         load_group<KB, QB, false>(q, c, g0, q.pool ? q.pages[g0 / LEANK_QUANT_GROUP] : 0, gr);
-        attend_group<G, KB, QB>(gr, c, s_q, s_idx, qk_scale, p_lds, rs, st);
+        attend_group<G, KB, QB>(gr, c, qc, qk_scale, p_lds, rs, st);
       }
     }
     // fold into the tile layout: head 4 grp + i of lane (col, grp), whose
