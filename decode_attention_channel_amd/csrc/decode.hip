@@ -212,6 +212,20 @@ int decode_impl(const leank_layer_cache* c, const void* q, const CallExtras& x, 
   p.tail_per_b = w.tail_per_b;
   p.n_bulk = static_cast<int64_t>(w.bulk_per_b) * c->batch;
   p.n_sl_all = w.sl_first ? static_cast<int64_t>(c->batch) * c->n_kv_heads * w.n_sl_items : 0;
+  {
+    int32_t be = 0, te = 0;
+    for (int h = 0; h < 8; ++h) {
+      if (h < c->n_kv_heads - 1) {
+        be += (w.sl_first ? 0 : w.n_sl_items) + w.n_mid_b[h];
+        te += w.n_mid[h] - w.n_mid_b[h];
+        p.bulk_end8[h] = be;
+        p.tail_end8[h] = te;
+      } else {
+        p.bulk_end8[h] = INT32_MAX;
+        p.tail_end8[h] = INT32_MAX;
+      }
+    }
+  }
   p.partial_stride = w.partial_stride;
   // pairs with many items get their channels split over several combine workgroups
   int32_t max_items = 0;

@@ -112,6 +112,13 @@ struct DecodeParams {
   int32_t tail_per_b;
   int64_t n_bulk;  // batch * bulk_per_b
   int64_t n_sl_all;  // full-width items dispatched first (batch * n_kv * n_sl_items), or 0
+  // calls of at most 8 KV heads: each head's last item + 1 within a batch
+  // row's bulk items (full-width and bulk middle together, or bulk middle
+  // only when n_sl_all > 0) and within its tail items, cumulative over the
+  // heads (entries past n_kv - 1 hold INT32_MAX), so an item finds its head
+  // from values loaded with the other parameters
+  int32_t bulk_end8[8];
+  int32_t tail_end8[8];
   DecodeHead heads[LEANK_MAX_KV_HEADS];
 };
 // kernel arguments are limited to 4 KiB

@@ -181,6 +181,23 @@ __device__ __forceinline__ void attend_middle_contig(const DecodeParams& p, cons
   }
 }
 
+// The head of item r of a batch row's phase, from the heads' cumulative
+// ends (nondecreasing, INT32_MAX past the last head): h = the number of
+// ends at or below r, r becomes the item's place within its head.  All
+// compares and selects, no dependent load: the ends come with the launch
+// parameters.
+__device__ __forceinline__ void head_from_ends(const int32_t (&end)[8], int& r, int& h) {
+  int start = 0, hh = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    const bool past = r >= end[i];
+    hh += past ? 1 : 0;
+    start = past ? end[i] : start;
+  }
+  h = hh;
+  r -= start;
+}
+
 // KBMAX: 32-channel blocks of the widest live head (low-bit streams only;
 // 4 for bf16 caches).
 template <int G, int QB, int KBMAX>
@@ -232,18 +249,26 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
     const uint32_t j = item - static_cast<uint32_t>(p.n_sl_all);
     b = static_cast<int>(j / per_b);
     int r = static_cast<int>(j - static_cast<uint32_t>(b) * per_b);
-    while (h + 1 < p.n_kv && r >= static_cast<int>(n_sl) + p.heads[h].n_mid_b) {
-      r -= static_cast<int>(n_sl) + p.heads[h].n_mid_b;
-      ++h;
+    if (p.n_kv <= 8) {
+      head_from_ends(p.bulk_end8, r, h);
+    } else {
+      while (h + 1 < p.n_kv && r >= static_cast<int>(n_sl) + p.heads[h].n_mid_b) {
+        r -= static_cast<int>(n_sl) + p.heads[h].n_mid_b;
+        ++h;
+      }
     }
     local = r + (p.n_sl_all > 0 ? p.n_sl_items : 0);
   } else {
     const uint32_t t_item = item - static_cast<uint32_t>(p.n_bulk);
     b = static_cast<int>(t_item / static_cast<uint32_t>(p.tail_per_b));
     int r = static_cast<int>(t_item - static_cast<uint32_t>(b) * static_cast<uint32_t>(p.tail_per_b));
-    while (h + 1 < p.n_kv && r >= p.heads[h].n_mid - p.heads[h].n_mid_b) {
-      r -= p.heads[h].n_mid - p.heads[h].n_mid_b;
-      ++h;
+    if (p.n_kv <= 8) {
+      head_from_ends(p.tail_end8, r, h);
+    } else {
+      while (h + 1 < p.n_kv && r >= p.heads[h].n_mid - p.heads[h].n_mid_b) {
+        r -= p.heads[h].n_mid - p.heads[h].n_mid_b;
+        ++h;
+      }
     }
     local = p.n_sl_items + p.heads[h].n_mid_b + r;
   }
