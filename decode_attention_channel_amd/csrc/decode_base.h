@@ -138,6 +138,49 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // This lane's wavefront within the workgroup, in a scalar register.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+#ifndef LEANK_TOUCH_ARGS
+#define LEANK_TOUCH_ARGS 1
+#endif
+// Reads one dword of every 64-byte line of the first `kLines` lines of the
+// kernel argument block and waits for them, so that the lines sit in the
+// scalar cache before the kernel's own argument loads.  Those loads form a
+// chain (the item's head depends on the per-head counts, its record on the
+// head, its stream addresses on both), and each first touch of a line
+// missed the cache at every step: per-item timestamps (a one-round
+// 128K-token layer) put the item's head record 1.1 us after its start and
+// its staging loads 2.5 us after it, 0.4 and 1.3 us with the lines
+// touched first (Llama batch-64 4K step 110.9 ->
+// 110.1 us, Qwen2.5-7B-shaped batch-16 32K 89.5 -> 88.8 us, 32-layer
+// 128K-token batch-1 token 958 -> 940 us).  Loads only; the values are
+// discarded.
+template <int kLines>
+__device__ __forceinline__ void touch_kernarg_lines() {
+  static_assert(kLines >= 1 && kLines <= 16, "touch at most 16 lines");
+  const auto* args = __builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t sink;
+  asm volatile(
+      "s_load_dword %0, %1, 0x0\n\t"
+      ".if %2 > 1\n\ts_load_dword %0, %1, 0x40\n\t.endif\n\t"
+      ".if %2 > 2\n\ts_load_dword %0, %1, 0x80\n\t.endif\n\t"
+      ".if %2 > 3\n\ts_load_dword %0, %1, 0xc0\n\t.endif\n\t"
+      ".if %2 > 4\n\ts_load_dword %0, %1, 0x100\n\t.endif\n\t"
+      ".if %2 > 5\n\ts_load_dword %0, %1, 0x140\n\t.endif\n\t"
+      ".if %2 > 6\n\ts_load_dword %0, %1, 0x180\n\t.endif\n\t"
+      ".if %2 > 7\n\ts_load_dword %0, %1, 0x1c0\n\t.endif\n\t"
+      ".if %2 > 8\n\ts_load_dword %0, %1, 0x200\n\t.endif\n\t"
+      ".if %2 > 9\n\ts_load_dword %0, %1, 0x240\n\t.endif\n\t"
+      ".if %2 > 10\n\ts_load_dword %0, %1, 0x280\n\t.endif\n\t"
+      ".if %2 > 11\n\ts_load_dword %0, %1, 0x2c0\n\t.endif\n\t"
+      ".if %2 > 12\n\ts_load_dword %0, %1, 0x300\n\t.endif\n\t"
+      ".if %2 > 13\n\ts_load_dword %0, %1, 0x340\n\t.endif\n\t"
+      ".if %2 > 14\n\ts_load_dword %0, %1, 0x380\n\t.endif\n\t"
+      ".if %2 > 15\n\ts_load_dword %0, %1, 0x3c0\n\t.endif\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(sink)
+      : "s"(args), "i"(kLines)
+      : "memory");
+}
+
 // A 64-bit value that is the same in every lane, moved to scalar registers.
 __device__ __forceinline__ int64_t uniform64(int64_t x) {
   const uint64_t u = static_cast<uint64_t>(x);

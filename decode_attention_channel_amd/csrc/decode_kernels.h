@@ -232,6 +232,11 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   // order), so the record order does not depend on it
   // (32-bit arithmetic: a launch holds fewer than 2^31 items; the results
   // go through readfirstlane so that they stay in scalar registers)
+  // the scalar launch parameters and the first 8 heads' records (the
+  // parameters' first 14 lines: sizeof checked below)
+  static_assert(offsetof(DecodeParams, heads) + 8 * sizeof(DecodeHead) <= 14 * 64,
+                "touched lines do not cover the first 8 heads");
+  if (LEANK_TOUCH_ARGS) touch_kernarg_lines<14>();
   const uint32_t item = blockIdx.x;
   int b, h = 0, local;
   if (item < static_cast<uint32_t>(p.n_sl_all)) {
@@ -310,18 +315,28 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   }
   StepTokens tok{};
   // The workgroup's staging: the group's q rows and the head's kept ids,
-  // the item's pages (paged middle) and cleared P staging.  Each attend
-  // path runs it first; the workgroup barrier that publishes it sits in the
-  // attend call (bf16 streams: after each wavefront has issued its first
-  // tile's loads) or just below (low-bit middles).  Where it is written
+  // the item's pages (paged middle) and cleared P staging, in two parts:
+  // `stage` issues the global loads into registers and returns the part
+  // that writes them to LDS.  The bf16 attend paths issue their first
+  // tile's loads between the two, so that a wavefront's staging loads and
+  // tile loads are in flight together (written out in one part, a
+  // wavefront's tile loads waited for its staging loads' round trip); the
+  // workgroup barrier that publishes the staging sits in the attend call
+  // (bf16 streams) or just below (low-bit middles).  Where it is written
   // changes the register allocation of the whole kernel: this form
   // measured fastest (written out once before the paths, the Llama
   // batch-64 4K step took 115.4 us instead of 110.9).
   auto stage = [&]() {
-    // stage the group's q rows and the head's kept ids; clear the P staging
-    const uint16_t* qh = p.q + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM;
-    if (t < G * 16)
-      *reinterpret_cast<u32x4_t*>(s_q + t * 8) = *reinterpret_cast<const u32x4_t*>(qh + t * 8);
+    const u32x4_t zero4{0u, 0u, 0u, 0u};
+    const bool has_q = t < G * 16;
+    const bool has_idx = (middle || carries_step) && t >= 128 && t < 144;
+    bool has_page = false;
+    u32x4_t qv = zero4, iv = zero4;
+    int32_t page = 0;
+    if (has_q) {
+      const uint16_t* qh = p.q + (static_cast<int64_t>(b) * p.n_q + h * G) * LEANK_HEAD_DIM;
+      qv = *reinterpret_cast<const u32x4_t*>(qh + t * 8);
+    }
     if (QB == 0 && p.paged && middle && t >= 192) {
       // the item's pages (items span at most 64 pages: their rows are capped
       // by the plan's largest item size)
@@ -329,14 +344,18 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
       mid_chunk_rows(hd, local - p.n_sl_items, INT32_MAX, pr0, pr1);
       const int first = pr0 / LEANK_PAGE_ROWS;
       const int i = t - 192;
-      if (i < (pr1 - pr0) / LEANK_PAGE_ROWS && first + i < p.pages_per_row)
-        s_pages[i] = p.block_table[static_cast<int64_t>(b) * p.pages_per_row + first + i];
+      has_page = i < (pr1 - pr0) / LEANK_PAGE_ROWS && first + i < p.pages_per_row;
+      if (has_page) page = p.block_table[static_cast<int64_t>(b) * p.pages_per_row + first + i];
     }
-    if ((middle || carries_step) && t >= 128 && t < 144)
-      *reinterpret_cast<u32x4_t*>(s_idx + (t - 128) * 8) =
-          *reinterpret_cast<const u32x4_t*>(p.kept_idx + h * LEANK_HEAD_DIM + (t - 128) * 8);
-    for (int k = lane; k < (QB ? group_lds_halves<KBMAX, G>() : 2 * 16 * kTileRows) / 8; k += 64)
-      reinterpret_cast<u32x4_t*>(s_p[wave])[k] = u32x4_t{0u, 0u, 0u, 0u};
+    if (has_idx)
+      iv = *reinterpret_cast<const u32x4_t*>(p.kept_idx + h * LEANK_HEAD_DIM + (t - 128) * 8);
+    return [=]() {
+      if (has_q) *reinterpret_cast<u32x4_t*>(s_q + t * 8) = qv;
+      if (has_page) s_pages[t - 192] = page;
+      if (has_idx) *reinterpret_cast<u32x4_t*>(s_idx + (t - 128) * 8) = iv;
+      for (int k = lane; k < (QB ? group_lds_halves<KBMAX, G>() : 2 * 16 * kTileRows) / 8; k += 64)
+        reinterpret_cast<u32x4_t*>(s_p[wave])[k] = zero4;
+    };
   };
   // the item that carries a fused step stages its tokens and V blocks
   // before anything else (one item per pair)
@@ -409,10 +428,10 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   } else if (QB == 0 && !p.paged) {
     attend_middle_contig<G>(p, hd, b, local - p.n_sl_items, t_mid, s_q, s_idx, p_lds, st, stage);
   } else if (QB == 0) {
-    stage();
+    stage()();
     attend_middle_paged<G>(p, hd, b, local - p.n_sl_items, t_mid, s_q, s_idx, s_pages, p_lds, st);
   } else {
-    stage();
+    stage()();
     __syncthreads();
     attend_middle<G, QB, KBMAX>(p, hd, b, local - p.n_sl_items, t_mid, s_q, s_idx, s_pages, p_lds,
                                 st, vmin);

@@ -153,12 +153,13 @@ __device__ __forceinline__ void load_tile_buf(__amdgpu_buffer_rsrc_t rk, __amdgp
   for (int n = 0; n < 8; ++n) tr.vf[n] = load_buf16(rv, v0 + n * 256);
 }
 
-// Rows [r0, r1) of one stream, except row excl (-1: none).  `stage` runs
-// the workgroup's staging (q rows and kept ids into LDS; the caller defines
-// it), then each wavefront issues its first tile's loads, joins the
-// workgroup barrier that publishes the staging and gathers its query
+// Rows [r0, r1) of one stream, except row excl (-1: none).  `stage` issues
+// the workgroup's staging loads (q rows and kept ids; the caller defines
+// it) and returns the part that writes them to LDS; each wavefront issues
+// its first tile's loads in between, then writes its part of the staging,
+// joins the workgroup barrier that publishes it and gathers its query
 // operand, so the two memory latencies at the start of an item overlap.
-// (Running the staging after the tile's loads, so that it waits behind
+// (Issuing the staging loads after the tile's, so that they return behind
 // them, measured slower: the Llama batch-64 4K step 110.9 -> 112.7 us, the
 // 32-layer 128K-token batch-1 token 960 -> 970 us.)  The loads go through
 // buffer resources bounded by the item's rows, so the last tile needs no
@@ -186,8 +187,9 @@ __device__ __forceinline__ void attend_range_staged(const uint16_t* kb, int kstr
   const int ex = excl < 0 ? -1 : excl - r0;
   int t = wave * kTileRows;
   TileRegs<KB> tr;
-  stage();
+  const auto commit = stage();
   load_tile_buf<KB>(rk, rv, kstride, t, c, tr);
+  commit();
   __syncthreads();
   u32x4_t qa[KB];
   gather_q<G, KB>(s_q, s_idx, dense, c, qa);
