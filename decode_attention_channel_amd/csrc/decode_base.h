@@ -148,11 +148,10 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // head, its stream addresses on both), and each first touch of a line
 // missed the cache at every step: per-item timestamps (a one-round
 // 128K-token layer) put the item's head record 1.1 us after its start and
-// its staging loads 2.5 us after it, 0.4 and 1.3 us with the lines
-// touched first (Llama batch-64 4K step 110.9 ->
-// 110.1 us, Qwen2.5-7B-shaped batch-16 32K 89.5 -> 88.8 us, 32-layer
-// 128K-token batch-1 token 958 -> 940 us).  Loads only; the values are
-// discarded.
+// its staging loads 2.5 us after it, 0.4 and 1.3 us with the lines touched
+// first (Llama batch-64 4K step 110.9 -> 110.1 us, Qwen2.5-7B-shaped
+// batch-16 32K 89.5 -> 88.8 us, 32-layer 128K-token batch-1 token 958 ->
+// 940 us).  Loads only; the values are discarded.
 template <int kLines>
 __device__ __forceinline__ void touch_kernarg_lines() {
   static_assert(kLines >= 1 && kLines <= 16, "touch at most 16 lines");

@@ -224,6 +224,12 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   __shared__ float s_midv[QB ? LEANK_HEAD_DIM : 1];
   __shared__ float s_vpar[2];
 
+  // bring the launch parameters' scalar fields and the first 8 heads'
+  // records (their first 14 lines) into the scalar cache
+  static_assert(offsetof(DecodeParams, heads) + 8 * sizeof(DecodeHead) <= 14 * 64,
+                "touched lines do not cover the first 8 heads");
+  if (LEANK_TOUCH_ARGS) touch_kernarg_lines<14>();
+
   // dispatch order: every batch row's bulk items (full-width, then bulk
   // middle, head by head; or, when the plan puts the full-width items
   // first, every row's full-width items, then every row's bulk middle
@@ -232,11 +238,6 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   // order), so the record order does not depend on it
   // (32-bit arithmetic: a launch holds fewer than 2^31 items; the results
   // go through readfirstlane so that they stay in scalar registers)
-  // the scalar launch parameters and the first 8 heads' records (the
-  // parameters' first 14 lines: sizeof checked below)
-  static_assert(offsetof(DecodeParams, heads) + 8 * sizeof(DecodeHead) <= 14 * 64,
-                "touched lines do not cover the first 8 heads");
-  if (LEANK_TOUCH_ARGS) touch_kernarg_lines<14>();
   const uint32_t item = blockIdx.x;
   int b, h = 0, local;
   if (item < static_cast<uint32_t>(p.n_sl_all)) {
