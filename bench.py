@@ -635,7 +635,7 @@ def measured_traffic():
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
               "multi-GPU path; every figure is one GPU's.", file=sys.stderr)
         sys.exit(2)
     from synthetic import get_config

@@ -152,9 +152,10 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // first (Llama batch-64 4K step 110.9 -> 110.1 us, Qwen2.5-7B-shaped
 // batch-16 32K 89.5 -> 88.8 us, 32-layer 128K-token batch-1 token 958 ->
 // 940 us).  Loads only; the values are discarded.
-template <int kLines>
+template <int kLines, class Args>
 __device__ __forceinline__ void touch_kernarg_lines() {
   static_assert(kLines >= 1 && kLines <= 16, "touch at most 16 lines");
+  static_assert(sizeof(Args) >= kLines * 64, "the touched lines must lie inside the argument block");
   const auto* args = __builtin_amdgcn_kernarg_segment_ptr();
   uint32_t sink;
   asm volatile(

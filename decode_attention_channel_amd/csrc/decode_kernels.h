@@ -228,7 +228,7 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
   // records (their first 14 lines) into the scalar cache
   static_assert(offsetof(DecodeParams, heads) + 8 * sizeof(DecodeHead) <= 14 * 64,
                 "touched lines do not cover the first 8 heads");
-  if (LEANK_TOUCH_ARGS) touch_kernarg_lines<14>();
+  if (LEANK_TOUCH_ARGS) touch_kernarg_lines<14, DecodeParams>();
 
   // dispatch order: every batch row's bulk items (full-width, then bulk
   // middle, head by head; or, when the plan puts the full-width items
@@ -658,7 +658,7 @@ __global__ LEANK_SPLIT_ATTRS void decode_split_kernel(const DecodeParams p) {
 template <int G, int NI>
 __global__ __launch_bounds__(64 * G) void decode_combine_wave_kernel(const DecodeParams p) {
   // as in the split kernel (the 32-layer 128K-token token: 938.7 -> 935.0 us)
-  if (LEANK_TOUCH_ARGS) touch_kernarg_lines<14>();
+  if (LEANK_TOUCH_ARGS) touch_kernarg_lines<14, DecodeParams>();
   const int lane = threadIdx.x & 63;
   const int g = threadIdx.x >> 6;
   const int b = static_cast<int>(blockIdx.x / p.n_kv);
@@ -731,7 +731,7 @@ constexpr int kCombineUnroll = LEANK_COMBINE_UNROLL;
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(const DecodeParams p) {
-  if (LEANK_TOUCH_ARGS) touch_kernarg_lines<14>();  // as in the split kernel
+  if (LEANK_TOUCH_ARGS) touch_kernarg_lines<14, DecodeParams>();  // as in the split kernel
   __shared__ float s_max[kWaves * 32];
   __shared__ float4 s_acc[kWaves * 32];
   __shared__ float s_sum[kWaves * 32];
