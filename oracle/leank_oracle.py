@@ -245,12 +245,16 @@ def _attend(shape, get_q, get_k, get_v, mask, n_sink, window, scale, pairs):
         out = np.zeros((batch, n_q_heads, d), dtype=np.float64)
         put = lambda b, j, val: out.__setitem__((b, j), val)
     else:
+        # row n of the result answers pairs[n]; a pair listed twice is
+        # computed once and written to every row that asks for it
         out = np.zeros((len(pairs), d), dtype=np.float64)
-        index = {pair: n for n, pair in enumerate(pairs)}
+        index = {}
+        for n, pair in enumerate(pairs):
+            index.setdefault(tuple(pair), []).append(n)
         put = lambda b, j, val: out.__setitem__(index[(b, j)], val)
 
     by_kv = {}
-    for b, j in pairs:
+    for b, j in dict.fromkeys(tuple(p) for p in pairs):
         by_kv.setdefault((b, j // group), []).append(j)
     for (b, h), heads in sorted(by_kv.items()):
         beta = np.asarray(mask[h], dtype=np.float64)

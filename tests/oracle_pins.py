@@ -349,8 +349,9 @@ def pin_decode_masked_matches_sdpa(O):
             wide = O.decode_f64(_bits_to_f64(q).numpy(), _bits_to_f64(k).numpy(),
                                 _bits_to_f64(v).numpy(), mask, n_sink, window)
             np.testing.assert_allclose(wide, expect, rtol=1e-10, atol=1e-12)
-            # sampled-pairs entry point returns the same rows
-            pairs = [(batch - 1, n_q - 1), (0, 0)]
+            # sampled-pairs entry point returns the same rows, in the order
+            # asked, a pair asked twice in both rows
+            pairs = [(batch - 1, n_q - 1), (0, 0), (batch - 1, n_q - 1), (0, 0)]
             sampled = O.decode(q, k, v, mask, n_sink, window, pairs=pairs)
             for n, (b, j) in enumerate(pairs):
                 np.testing.assert_allclose(sampled[n], expect[b, j], rtol=1e-10, atol=1e-12)

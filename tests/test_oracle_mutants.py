@@ -14,6 +14,9 @@ import oracle.leank_oracle as real
 from tests import oracle_pins
 
 MUTANTS = [
+    ("a pair asked twice answered in its last row only",
+     "index.setdefault(tuple(pair), []).append(n)",
+     "index[tuple(pair)] = n"),
     ("softmax scale from kept channels",
      "s = (keys @ qv) * scale",
      "s = (keys @ qv) / np.sqrt(max(1.0, beta.sum()))"),
