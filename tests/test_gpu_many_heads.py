@@ -10,7 +10,8 @@ step's appended and leaving tokens), so a lost or doubled row, or an item
 attributed to the wrong head, shows: 16 and 12 KV heads with dead heads and
 kept widths from 8 to 128, in plans of more than one round of workgroups
 (bulk and tail items, and for a low-bit middle the full-width items
-dispatched first) and of one round.
+dispatched first) and of one round, and at the most KV heads a plan holds
+(64: their records fill the launch parameters).
 """
 
 import pytest
@@ -45,3 +46,20 @@ def test_needles_12_kv_heads_paged_step():
 
 def test_needles_16_kv_heads_one_round():
     run_case(1, 16, COUNTS16, 64, 1024, 32768, True, 0, False, seed=57, oracle_pairs=1)
+
+
+# the most KV heads a plan holds (LEANK_MAX_KV_HEADS): every fifth head dead,
+# the others keeping 8 to 128 channels
+COUNTS64 = [8 * ((7 * h) % 17) if h % 5 else 0 for h in range(64)]
+
+
+def test_needles_64_kv_heads_step():
+    run_case(2, 128, COUNTS64, 16, 128, 2000, True, 0, False, seed=61, per_pair=16)
+
+
+def test_needles_64_kv_heads_8_query_heads_each():
+    run_case(1, 512, COUNTS64, 16, 128, 2000, False, 0, False, seed=63, per_pair=16)
+
+
+def test_needles_64_kv_heads_4bit_step():
+    run_case(2, 64, COUNTS64, 16, 128, 2000, True, 4, False, seed=65, per_pair=16)
