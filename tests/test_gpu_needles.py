@@ -217,3 +217,10 @@ def test_needles_step_at_group_edge_q4():
     # the leaving token becomes middle row ctx - window - n_sink; 63 mod 64 completes the group
     ctx = 64 + 512 + 64 * 55 + 63
     run_case(64, 32, LLAMA_COUNTS, 64, 512, ctx, True, 4, False, seed=31, per_pair=48)
+
+
+def test_needles_512_batch_rows():
+    """Thousands of (batch row, KV head) pairs in one call: the combine's grid
+    and the record offsets of the last batch rows."""
+    run_case(512, 16, [32, 0, 64, 32, 0, 96, 32, 128], 4, 32, 300, True, 0, False, seed=71,
+             per_pair=8)

@@ -2,8 +2,8 @@
 
 Each case draws a layer shape (query heads per KV head 1..8, 1..12 KV heads
 with kept widths from 0 to 128 in steps of 8, sink and window sizes, batch,
-context length) and a cache kind (bf16, paged bf16, 4- and 8-bit middles,
-paged 4-bit), prefills it, and checks a decode call or a fused step over
+context length; a second set takes 9 to 64 KV heads) and a cache kind
+(bf16, paged bf16, 4- and 8-bit middles, paged 4-bit), prefills it, and checks a decode call or a fused step over
 sampled (batch row, query head) pairs against the oracle's attention
 (`oracle.decode`, or `oracle.decode_q` over the low-bit streams) within the
 parity bound.  The draws reach plans the fixed cases may not: one round or
@@ -65,10 +65,39 @@ def build(kind, mask, batch, n_q, n_sink, window, max_ctx, seed):
     return cache, bits
 
 
+def draw_wide(i):
+    """Layers of 9 to 64 KV heads (the items walk the heads' records) with 1
+    to 8 query heads each, at small batches and contexts."""
+    rng = np.random.default_rng(20261204 + i)
+    group = int(rng.integers(1, 9))
+    n_kv = int(rng.integers(9, 65))
+    counts = [int(c) for c in rng.choice([0, 8, 16, 24, 32, 48, 64, 96, 128], size=n_kv)]
+    if not any(counts):
+        counts[int(rng.integers(n_kv))] = 32
+    n_sink = int(rng.choice([0, 4, 64]))
+    window = int(rng.choice([1, 16, 256]))
+    batch = int(rng.choice([1, 2, 3]))
+    lo = n_sink + window + 130
+    ctx = int(rng.integers(lo, lo + 2500))
+    return dict(group=group, counts=counts, n_sink=n_sink, window=window, batch=batch, ctx=ctx,
+                kind=KINDS[i % len(KINDS)], step=bool(i % 2), seed=20261204 + i)
+
+
+N_WIDE = 20
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_layer(i):
-    c = draw(i)
-    print("CASE random", i, c, flush=True)
+    check(draw(i), f"random case {i}")
+
+
+@pytest.mark.parametrize("i", range(N_WIDE))
+def test_random_wide_layer(i):
+    check(draw_wide(i), f"random wide case {i}")
+
+
+def check(c, what):
+    print("CASE", what, c, flush=True)
     rng = np.random.default_rng(c["seed"])
     mask = mask_with_counts(rng, c["counts"])
     n_kv = mask.shape[0]
@@ -95,4 +124,4 @@ def test_random_layer(i):
     else:
         ref = oracle.decode(qb, kb, vb, mask, c["n_sink"], c["window"], pairs=pairs)
     got = out.cpu().numpy()
-    assert_close(np.stack([got[b, j] for b, j in pairs]), ref, f"random case {i}")
+    assert_close(np.stack([got[b, j] for b, j in pairs]), ref, what)
