@@ -272,3 +272,27 @@ def shuffled_block_table(rng, batch, pages_per_row, n_pages, device="cuda"):
     random order."""
     pick = rng.permutation(n_pages)[:batch * pages_per_row]
     return torch.from_numpy(pick.astype(np.int32).reshape(batch, pages_per_row)).to(device)
+
+
+# cache kinds of the seeded random layers
+KINDS = ["bf16", "paged", "q4", "q8", "paged_q4"]
+
+
+def build_kind(kind, mask, batch, n_q, n_sink, window, max_ctx, seed):
+    """A cache of one of KINDS for `mask`: bf16, paged bf16 (64-row pages
+    through a shuffled block table), 4- or 8-bit middles, paged 4-bit.
+    Returns (cache, bits)."""
+    kept_count, kept_idx = kept_from_mask(mask)
+    kw = {}
+    if kind.startswith("paged"):
+        mid_cap = max(0, max_ctx - n_sink - window)
+        ppr = -(-mid_cap // 64)
+        n_pages = batch * ppr + 3
+        kw = dict(n_pages=n_pages,
+                  block_table=shuffled_block_table(np.random.default_rng(seed), batch, ppr, n_pages))
+    bits = {"q4": 4, "q8": 8, "paged_q4": 4}.get(kind, 0)
+    if bits:
+        kw["quant_bits"] = bits
+    cache = dac.LayerCache(kept_count.tolist(), torch.from_numpy(kept_idx).to("cuda"), batch, n_q,
+                           mask.shape[0], n_sink, window, max_ctx, device="cuda", **kw)
+    return cache, bits

@@ -18,11 +18,10 @@ import torch
 import decode_attention_channel_amd as dac
 import oracle
 from synthetic import bf16_bits
-from tests.gpu_cases import assert_close, kept_from_mask, mask_with_counts, random_bf16, shuffled_block_table
+from tests.gpu_cases import KINDS, assert_close, build_kind, mask_with_counts, random_bf16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-KINDS = ["bf16", "paged", "q4", "q8", "paged_q4"]
 N_CASES = 40
 
 
@@ -46,23 +45,6 @@ def draw(i):
     ctx = int(rng.integers(lo, hi))
     return dict(group=group, counts=counts, n_sink=n_sink, window=window, batch=batch, ctx=ctx,
                 kind=kind, step=step, seed=20261203 + i)
-
-
-def build(kind, mask, batch, n_q, n_sink, window, max_ctx, seed):
-    kept_count, kept_idx = kept_from_mask(mask)
-    kw = {}
-    if kind.startswith("paged"):
-        mid_cap = max(0, max_ctx - n_sink - window)
-        ppr = -(-mid_cap // 64)
-        n_pages = batch * ppr + 3
-        kw = dict(n_pages=n_pages,
-                  block_table=shuffled_block_table(np.random.default_rng(seed), batch, ppr, n_pages))
-    bits = {"q4": 4, "q8": 8, "paged_q4": 4}.get(kind, 0)
-    if bits:
-        kw["quant_bits"] = bits
-    cache = dac.LayerCache(kept_count.tolist(), torch.from_numpy(kept_idx).to(DEV), batch, n_q,
-                           mask.shape[0], n_sink, window, max_ctx, device=DEV, **kw)
-    return cache, bits
 
 
 def draw_wide(i):
@@ -103,7 +85,7 @@ def check(c, what):
     n_kv = mask.shape[0]
     n_q = n_kv * c["group"]
     batch, ctx = c["batch"], c["ctx"]
-    cache, bits = build(c["kind"], mask, batch, n_q, c["n_sink"], c["window"], ctx + 4, c["seed"])
+    cache, bits = build_kind(c["kind"], mask, batch, n_q, c["n_sink"], c["window"], ctx + 4, c["seed"])
     gen = torch.Generator(device=DEV).manual_seed(c["seed"])
     k = random_bf16((batch, n_kv, ctx, 128), gen, scale=1.5)
     v = random_bf16((batch, n_kv, ctx, 128), gen)

@@ -17,8 +17,7 @@ import torch
 import decode_attention_channel_amd as dac
 import oracle
 from synthetic import bf16_bits
-from tests.gpu_cases import assert_close, mask_with_counts, random_bf16
-from tests.test_gpu_random import KINDS, build
+from tests.gpu_cases import KINDS, assert_close, build_kind, mask_with_counts, random_bf16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -55,7 +54,7 @@ def test_random_ragged_layer(i):
     n_q = n_kv * c["group"]
     lengths = c["lengths"]
     batch, l_max = len(lengths), max(lengths)
-    cache, bits = build(c["kind"], mask, batch, n_q, c["n_sink"], c["window"], l_max + 2, c["seed"])
+    cache, bits = build_kind(c["kind"], mask, batch, n_q, c["n_sink"], c["window"], l_max + 2, c["seed"])
     gen = torch.Generator(device=DEV).manual_seed(c["seed"])
     k = random_bf16((batch, n_kv, l_max + 1, 128), gen, scale=1.5)
     v = random_bf16((batch, n_kv, l_max + 1, 128), gen)
