@@ -3,12 +3,13 @@
 Each case draws a layer shape (query heads per KV head 1..8, 1..12 KV heads
 with kept widths from 0 to 128 in steps of 8, sink and window sizes, batch,
 context length; a second set takes 9 to 64 KV heads) and a cache kind
-(bf16, paged bf16, 4- and 8-bit middles, paged 4-bit), prefills it, and checks a decode call or a fused step over
-sampled (batch row, query head) pairs against the oracle's attention
-(`oracle.decode`, or `oracle.decode_q` over the low-bit streams) within the
-parity bound.  The draws reach plans the fixed cases may not: one round or
-several, balanced rounds, tail items, full-width items first, wide and
-narrow heads side by side.
+(bf16, paged bf16, 4- and 8-bit middles, paged 4-bit), prefills it, and
+checks a decode call or a fused step over sampled (batch row, query head)
+pairs against the oracle's attention (`oracle.decode`, or `oracle.decode_q`
+over the low-bit streams) within the parity bound; a decode call repeated
+gives the same bits.  The draws reach plans the fixed cases may not: one
+round or several, balanced rounds, tail items, full-width items first, wide
+and narrow heads side by side.
 """
 
 import numpy as np
@@ -96,6 +97,10 @@ def check(c, what):
     else:
         dac.leank_pack_k(cache, k, v)
         out = dac.leank_decode_attn(cache, q)
+        # the merge order is fixed: a second call gives the same bits
+        again = dac.leank_decode_attn(cache, q)
+        torch.cuda.synchronize()
+        assert torch.equal(out, again), f"{what}: a repeated decode call differs"
     torch.cuda.synchronize()
     assert cache.length == ctx
     pairs = sorted({(int(rng.integers(batch)), int(rng.integers(n_q))) for _ in range(20)}
